@@ -1,0 +1,11 @@
+"""MI355X-native single-precision GEMM (C = A x B, row-major) behind a C ABI.
+
+The compute path is the HIP library libsgemm.so (built from csrc/ for gfx950);
+this package holds its thin ctypes binding (binding.py), the seeded input
+generators (inputs.py) and host-side counting (metrics.py).  The library is
+loaded on first use; if it is missing, every entry point raises.
+"""
+from .binding import (  # noqa: F401
+    SgemmError, load, sgemm, sgemm_f32, sgemm_f32_ex, sgemm_f32_plan,
+    sgemm_f32_query, sgemm_f32_version, LIB_PATH,
+)
