@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark: single-precision GEMM TFLOP/s on one MI355X, and its fraction of
+the FP32 matrix peak.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one C = A x B call through the library's C ABI at the headline
+workload, M = N = K = 8192, row-major, A and B i.i.d. U[-1, 1] drawn with seed
+4 (synthetic data; inputs are resident in HBM before timing starts).  W
+untimed warm-up steps are followed by exactly K timed steps, bracketed by
+device synchronisation, with HIP events recorded on the launch stream around
+each step.  TFLOP/s = 2*M*N*K / t ("4.1 CUDA GEMM operator performance
+optimization", section 1.3).  A second workload, 3072^3 with N(0, 1) inputs
+(seed 2), is timed the same way and reported under "secondary".
+
+One JSON line is printed.  Besides the driver's fields it holds:
+  roofline      the dominant (only) kernel against the FP32 matrix peak
+                (157.3 TFLOP/s): achieved = 2*M*N*K / mean launch time;
+                traffic = HBM bytes per launch from rocprofv3 counters stored
+                under profiles/, or null if the kernel sources changed since.
+  cpu_baseline  the CPU reference (oracle/) timed on this host on a bounded
+                sample of the same product (whole rows of C, about
+                --cpu-seconds of work), in TFLOP/s, with the threads used; the
+                sampled rows are also compared with the GPU result.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SGEMM TFLOP/s and % of FP32 matrix peak at 3072³ and 8192³, 1×MI355X"
+HEADLINE = "sgemm_8192x8192x8192_uniform_seed4"
+SECONDARY = "sgemm_3072x3072x3072_normal_seed2"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sgemm_8192x8192x8192_traffic.txt")
+KERNEL_SOURCES = ["sgemm_mfma.hpp", "sgemm_valu.hpp", "select.hpp", "sgemm.hip"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "fp32_gemm_sgemm_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE,
+    if they were taken on the current kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def time_workload(torch, sg, w, steps, warmup, cfg=None):
+    from fp32_gemm_sgemm_amd import inputs
+    A_np, B_np = inputs.workload_operands(w)
+    A = torch.from_numpy(A_np).to("cuda")
+    B = torch.from_numpy(B_np).to("cuda")
+    C = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        sg.sgemm(A, B, out=C, stream=stream, cfg=cfg)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        sg.sgemm(A, B, out=C, stream=stream, cfg=cfg)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    per_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    region_ms = starts[0].elapsed_time(ends[-1])
+    return {
+        "A": A_np, "B": B_np, "C": C,
+        "region_ms": region_ms, "wall_s": wall_s,
+        "mean_ms": sum(per_ms) / len(per_ms), "min_ms": per_ms[0],
+        "median_ms": per_ms[len(per_ms) // 2], "p90_ms": per_ms[min(len(per_ms) - 1, int(0.9 * len(per_ms)))],
+    }
+
+
+def cpu_baseline(w, A_np, B_np, C_gpu, seconds):
+    """The CPU reference on whole rows of the same product, about `seconds` of
+    work; its rows are also checked against the GPU result."""
+    import numpy as np
+    import oracle
+    nt = oracle.default_threads()
+    rows = 0
+    spent = 0.0
+    n_bad = 0
+    max_err = 0.0
+    while rows < w.M and (spent < seconds or rows == 0):
+        r1 = min(w.M, rows + nt)
+        t0 = time.perf_counter()
+        ref, absb = oracle.sgemm_ref(A_np[rows:r1], B_np, nthreads=nt)
+        spent += time.perf_counter() - t0
+        rep = oracle.compare(C_gpu[rows:r1], ref, absb)
+        n_bad += rep["n_bad"]
+        max_err = max(max_err, rep["max_norm_err"])
+        rows = r1
+    flops = 2.0 * rows * w.N * w.K
+    return {
+        "value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": nt, "kind": "oracle",
+        "sample": f"rows 0..{rows - 1} of C ({rows} x {w.N} outputs, K = {w.K}, "
+                  f"{flops / 1e9:.1f} GFLOP) in {spent:.1f} s",
+        "check": {"n": rows * w.N, "n_bad": n_bad, "max_norm_err": max_err,
+                  "tol": oracle.TOL},
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--secondary", default=SECONDARY, help="'' to skip")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--variant", type=int, default=-1, help="force a compiled variant id")
+    ap.add_argument("--group-m", type=int, default=8)
+    ap.add_argument("--xcd-remap", type=int, default=1)
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "this library has no multi-GPU path.", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    import fp32_gemm_sgemm_amd as sg
+    from fp32_gemm_sgemm_amd import inputs, metrics
+    if not os.path.exists(sg.LIB_PATH):
+        from fp32_gemm_sgemm_amd import build
+        build.build()
+    sg.load()
+
+    cfg = None
+    if args.variant >= 0:
+        cfg = sg.SgemmCfg()
+        cfg.id, cfg.group_m, cfg.xcd_remap = args.variant, args.group_m, args.xcd_remap
+
+    w = inputs.WORKLOADS[args.workload]
+    r = time_workload(torch, sg, w, args.steps, args.warmup, cfg)
+    flops = w.flops
+    ms_per_step = r["region_ms"] / args.steps
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (r["mean_ms"] * 1e-3) / 1e12
+    peak = metrics.MI355X_FP32_MATRIX_PEAK_TFLOPS
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    # torch's allocations are 256-byte aligned, so the operands are 16-byte aligned
+    plan = sg.sgemm_f32_plan(w.M, w.N, w.K, w.K, w.N, w.N, 1, cus) \
+        if cfg is None else sg.sgemm_f32_variant(cfg.id)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "M": w.M, "N": w.N, "K": w.K, "layout": "row-major",
+            "inputs": f"{w.dist} seed {w.seed}",
+            "variant": plan.id, "tile": f"{plan.bm}x{plan.bn}x{plan.bk}",
+            "waves": f"{plan.waves_m}x{plan.waves_n}",
+            "kernel": "mfma_f32_32x32x2" if plan.kernel == 0 else "valu_fma",
+            "parallelism": "single GPU",
+        },
+        "frac_of_fp32_matrix_peak": round(value / peak, 4),
+        "timing_ms": {k: round(r[k], 4) for k in ("mean_ms", "median_ms", "min_ms", "p90_ms")},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": read_traffic(),
+            "compulsory_bytes": metrics.compulsory_bytes(w.M, w.N, w.K),
+            "kernel_source_sha256_16": kernel_source_hash(),
+        },
+    }
+
+    if args.secondary:
+        w2 = inputs.WORKLOADS[args.secondary]
+        r2 = time_workload(torch, sg, w2, args.steps, args.warmup, cfg)
+        v2 = w2.flops / (r2["region_ms"] / args.steps * 1e-3) / 1e12
+        result["secondary"] = {
+            "workload": w2.name, "value": round(v2, 3), "unit": "TFLOP/s",
+            "ms_per_step": round(r2["region_ms"] / args.steps, 4),
+            "frac_of_fp32_matrix_peak": round(v2 / peak, 4),
+            "mean_kernel_ms": round(r2["mean_ms"], 4),
+        }
+        del r2
+
+    if not args.no_cpu_baseline:
+        C_host = r["C"].cpu().numpy()
+        result["cpu_baseline"] = cpu_baseline(w, r["A"], r["B"], C_host, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

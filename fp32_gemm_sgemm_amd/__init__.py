@@ -6,6 +6,7 @@ generators (inputs.py) and host-side counting (metrics.py).  The library is
 loaded on first use; if it is missing, every entry point raises.
 """
 from .binding import (  # noqa: F401
-    SgemmError, load, sgemm, sgemm_f32, sgemm_f32_ex, sgemm_f32_plan,
-    sgemm_f32_query, sgemm_f32_version, LIB_PATH,
+    SgemmCfg, SgemmError, load, sgemm, sgemm_f32, sgemm_f32_ex,
+    sgemm_f32_num_variants, sgemm_f32_plan, sgemm_f32_query, sgemm_f32_variant,
+    sgemm_f32_version, LIB_PATH, SGEMM_KERNEL_MFMA, SGEMM_KERNEL_VALU,
 )

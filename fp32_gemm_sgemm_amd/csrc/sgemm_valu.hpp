@@ -1,0 +1,136 @@
+// Vector-FMA single-precision GEMM, kept only as a measured comparison for the
+// matrix-core kernel.  It is the classic register-blocked design of
+// "4.1 CUDA GEMM operator performance optimization" carried to 64-wide
+// wavefronts: a 128x128 workgroup tile (section 4), an 8x8 register tile per
+// thread split into four 4x4 quadrants so that each LDS read is a 16-byte
+// vector and a 16-lane row of threads reads 256 contiguous bytes (sections
+// 5-8), A stored transposed in LDS (section 7.3) and register + LDS double
+// buffering with one barrier per K slice (section 9).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sgemm {
+
+struct ValuTraits {
+    static constexpr int BM = 128, BN = 128, BK = 8;
+    static constexpr int NT = 256;             // 16 x 16 threads, 4 waves
+    static constexpr int LDA_S = BM + 4;       // transposed A tile: [BK][BM + 4]
+    static constexpr int LDB_S = BN;           // B tile: [BK][BN]
+    static constexpr int LDS_FLOATS = 2 * (BK * LDA_S + BK * LDB_S);
+};
+
+template <bool VEC>
+__global__ void __launch_bounds__(256)
+sgemm_valu_kernel(int M, int N, int K,
+                  const float *__restrict__ A, int lda,
+                  const float *__restrict__ B, int ldb,
+                  float *__restrict__ C, int ldc,
+                  int tiles_m, int tiles_n, int group_m, int xcd_remap)
+{
+    typedef ValuTraits T;
+    constexpr int BM = T::BM, BN = T::BN, BK = T::BK;
+    constexpr int LDA_S = T::LDA_S, LDB_S = T::LDB_S;
+    typedef float f4 __attribute__((ext_vector_type(4)));
+
+    __shared__ __attribute__((aligned(16))) float As[2][BK * LDA_S];
+    __shared__ __attribute__((aligned(16))) float Bs[2][BK * LDB_S];
+
+    int tm, tn;
+    map_tile(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, xcd_remap, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int tid = threadIdx.x;
+    const int tx = tid & 15, ty = tid >> 4;
+    const bool tile_inside = (m0 + BM <= M) && (n0 + BN <= N);
+
+    // cooperative load mapping: one float4 of A and one of B per thread
+    const int a_row = tid >> 1, a_col = 4 * (tid & 1);     // A tile 128 x 8
+    const int b_row = tid >> 5, b_col = 4 * (tid & 31);    // B tile 8 x 128
+
+    float acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
+
+    f4 ra, rb;
+    auto gload = [&](int kt) {
+        const int k0 = kt * BK;
+        const bool inside = tile_inside && (k0 + BK <= K);
+        const float *pa = A + (int64_t)(m0 + a_row) * lda + (k0 + a_col);
+        const float *pb = B + (int64_t)(k0 + b_row) * ldb + (n0 + b_col);
+        if (inside) {
+            if (VEC) {
+                ra = *reinterpret_cast<const f4 *>(pa);
+                rb = *reinterpret_cast<const f4 *>(pb);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { ra[e] = pa[e]; rb[e] = pb[e]; }
+            }
+        } else {
+            const bool av = m0 + a_row < M, bv = k0 + b_row < K;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ra[e] = (av && k0 + a_col + e < K) ? pa[e] : 0.0f;
+                rb[e] = (bv && n0 + b_col + e < N) ? pb[e] : 0.0f;
+            }
+        }
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) As[buf][(a_col + e) * LDA_S + a_row] = ra[e];
+        *reinterpret_cast<f4 *>(&Bs[buf][b_row * LDB_S + b_col]) = rb;
+    };
+    auto compute = [&](int buf) {
+#pragma unroll
+        for (int k = 0; k < BK; ++k) {
+            const f4 a0 = *reinterpret_cast<const f4 *>(&As[buf][k * LDA_S + 4 * ty]);
+            const f4 a1 = *reinterpret_cast<const f4 *>(&As[buf][k * LDA_S + 64 + 4 * ty]);
+            const f4 b0 = *reinterpret_cast<const f4 *>(&Bs[buf][k * LDB_S + 4 * tx]);
+            const f4 b1 = *reinterpret_cast<const f4 *>(&Bs[buf][k * LDB_S + 64 + 4 * tx]);
+            const float a[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+            const float b[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+        }
+    };
+
+    const int nk = (K + BK - 1) / BK;
+    if (nk > 0) {
+        gload(0);
+        sstore(0);
+        __syncthreads();
+        for (int kt = 0; kt < nk; ++kt) {
+            const int cur = kt & 1;
+            if (kt + 1 < nk) gload(kt + 1);
+            compute(cur);
+            if (kt + 1 < nk) sstore(cur ^ 1);
+            __syncthreads();
+        }
+    }
+
+    // rows 4*ty + {0..3} and 64 + 4*ty + {0..3}; columns likewise with tx
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = m0 + (i < 4 ? 4 * ty + i : 64 + 4 * ty + (i - 4));
+        if (row >= M) continue;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int col = n0 + 64 * h + 4 * tx;
+            float *p = C + (int64_t)row * ldc + col;
+            if (VEC && col + 3 < N) {
+                f4 v = {acc[i][4 * h], acc[i][4 * h + 1], acc[i][4 * h + 2], acc[i][4 * h + 3]};
+                *reinterpret_cast<f4 *>(p) = v;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (col + e < N) p[e] = acc[i][4 * h + e];
+            }
+        }
+    }
+}
+
+}  // namespace sgemm
