@@ -138,6 +138,11 @@ def main(argv=None):
     ap.add_argument("--variant", type=int, default=-1, help="force a compiled variant id")
     ap.add_argument("--group-m", type=int, default=8)
     ap.add_argument("--xcd-remap", type=int, default=1)
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the MFMA-peak probe (the measured matrix-core ceiling)")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="before timing, run one plain device copy of this many MiB, a "
+                         "known-size kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -165,6 +170,15 @@ def main(argv=None):
         cfg = sg.SgemmCfg()
         cfg.id, cfg.group_m, cfg.xcd_remap = args.variant, args.group_m, args.xcd_remap
 
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     w = inputs.WORKLOADS[args.workload]
     r = time_workload(torch, sg, w, args.steps, args.warmup, cfg)
     flops = w.flops
@@ -173,8 +187,7 @@ def main(argv=None):
     achieved = flops / (r["mean_ms"] * 1e-3) / 1e12
     peak = metrics.MI355X_FP32_MATRIX_PEAK_TFLOPS
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    # torch's allocations are 256-byte aligned, so the operands are 16-byte aligned
-    plan = sg.sgemm_f32_plan(w.M, w.N, w.K, w.K, w.N, w.N, 1, cus) \
+    plan = sg.sgemm_f32_plan(w.M, w.N, w.K, w.K, w.N, w.N, cus) \
         if cfg is None else sg.sgemm_f32_variant(cfg.id)
 
     result = {
@@ -223,6 +236,16 @@ def main(argv=None):
             "mean_kernel_ms": round(r2["mean_ms"], 4),
         }
         del r2
+
+    if not args.no_probe:
+        from fp32_gemm_sgemm_amd import probes
+        ceil = probes.mfma_peak_tflops()
+        result["mfma_probe"] = {
+            "tflops": round(ceil, 3),
+            "frac_of_published_peak": round(ceil / peak, 4),
+            "gemm_frac_of_probe": round(value / ceil, 4),
+            "what": "sustained v_mfma_f32_32x32x2_f32 rate, register operands only",
+        }
 
     if not args.no_cpu_baseline:
         C_host = r["C"].cpu().numpy()

@@ -26,7 +26,7 @@ class SgemmError(RuntimeError):
 
 class SgemmCfg(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
-        "id", "kernel", "bm", "bn", "bk", "waves_m", "waves_n", "vec",
+        "id", "kernel", "bm", "bn", "bk", "waves_m", "waves_n",
         "group_m", "xcd_remap", "grid", "threads", "lds_bytes",
         "tiles_m", "tiles_n")]
 
@@ -57,7 +57,7 @@ def load():
     lib.sgemm_f32.restype = i
     lib.sgemm_f32_ex.argtypes = [i, i, i, p, i, p, i, p, i, p, cfgp]
     lib.sgemm_f32_ex.restype = i
-    lib.sgemm_f32_plan.argtypes = [i, i, i, i, i, i, i, i, cfgp]
+    lib.sgemm_f32_plan.argtypes = [i, i, i, i, i, i, i, cfgp]
     lib.sgemm_f32_plan.restype = i
     lib.sgemm_f32_query.argtypes = [i, i, i, p, i, p, i, p, i, cfgp]
     lib.sgemm_f32_query.restype = i
@@ -86,9 +86,9 @@ def sgemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, stream=0, cfg=None):
     return load().sgemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, stream, ref)
 
 
-def sgemm_f32_plan(M, N, K, lda, ldb, ldc, aligned16=1, num_cus=0):
+def sgemm_f32_plan(M, N, K, lda, ldb, ldc, num_cus=0):
     out = SgemmCfg()
-    _check(load().sgemm_f32_plan(M, N, K, lda, ldb, ldc, aligned16, num_cus,
+    _check(load().sgemm_f32_plan(M, N, K, lda, ldb, ldc, num_cus,
                                  ctypes.byref(out)), "sgemm_f32_plan")
     return out
 

@@ -16,10 +16,12 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsgemm.so")
+PROBES_LIB = os.path.join(HERE, "libsgemm_probes.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = [os.path.join(CSRC, "sgemm.hip")]
+PROBE_SOURCES = [os.path.join(CSRC, "probes.hip")]
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -28,16 +30,24 @@ FLAGS = [
 ]
 
 
-def build(save_temps: str = None, verbose: bool = False, extra=()) -> str:
+def _hipcc(out, sources, save_temps=None, verbose=False, extra=()):
     cmd = [HIPCC, *FLAGS, *extra]
     if save_temps:
         os.makedirs(save_temps, exist_ok=True)
-        cmd += [f"-save-temps={'obj'}", "-Rpass-analysis=kernel-resource-usage"]
-    cmd += ["-o", LIB + ".tmp", *SOURCES]
+        cmd += ["-save-temps=obj", "-Rpass-analysis=kernel-resource-usage"]
+    cmd += ["-o", out + ".tmp", *sources]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True, cwd=save_temps or HERE)
-    os.replace(LIB + ".tmp", LIB)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def build(save_temps: str = None, verbose: bool = False, extra=()) -> str:
+    """Compile libsgemm.so (the product) and libsgemm_probes.so (measurement
+    probes); returns the product library's path."""
+    _hipcc(LIB, SOURCES, save_temps, verbose, extra)
+    _hipcc(PROBES_LIB, PROBE_SOURCES, save_temps, verbose, extra)
     return LIB
 
 

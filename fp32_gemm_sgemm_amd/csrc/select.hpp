@@ -4,10 +4,10 @@
 // Geometry uses round-up-and-guard sizing (DD2360 workbook "Applied GPU
 // Programming", Module 6, section 6.3): tiles_m = ceil(M/BM),
 // tiles_n = ceil(N/BN), one workgroup per tile.  The selector weighs per-tile
-// efficiency against wave quantisation: a grid of n workgroups on S resident
-// slots takes ceil(n/S) rounds ("4.1 CUDA GEMM operator performance
-// optimization", section 12.5 on launching at least as many blocks as SMs;
-// the workbook's Module 17 on the tail effect).
+// efficiency against wave quantisation: on S compute units a grid of n equal
+// tiles takes ceil(n/S) rounds ("4.1 CUDA GEMM operator performance
+// optimization", section 12.5 on launching at least as many blocks as SMs and
+// tuning per shape; the workbook's Module 17 on the tail effect).
 #pragma once
 
 #include <limits.h>
@@ -20,20 +20,26 @@ struct Variant {
     int kernel;
     int bm, bn, bk;
     int waves_m, waves_n;
-    int vec;
+    int stage_at;
     int threads;
     int lds_bytes;
     const void *fn;
+    int eff_permille;  // measured steady-state fraction of the FP32 matrix peak
+                       // (x1000) at 8192^3; 0 = never chosen by the selector
 };
 
-// Largest size accepted, so that k0 + BK and similar sums stay in int.
+// Largest sizes accepted: k0 + BK and similar sums stay in int, and the byte
+// offsets of a thread inside one slice ((BM-1)*lda + BK floats of A,
+// (BK-1)*ldb + BN floats of B) stay below 2^32.
 constexpr int kMaxDim = INT_MAX - 1024;
+constexpr int kMaxLda = (1 << 22) - 64;
+constexpr int kMaxLdb = (1 << 25) - 512;
 
 inline bool leading_dims_ok(int M, int N, int K, int lda, int ldb, int ldc)
 {
     if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return false;
     const int mk = K > 1 ? K : 1, mn = N > 1 ? N : 1;
-    return lda >= mk && ldb >= mn && ldc >= mn;
+    return lda >= mk && ldb >= mn && ldc >= mn && lda <= kMaxLda && ldb <= kMaxLdb;
 }
 
 inline long long ceil_div_ll(long long a, long long b) { return (a + b - 1) / b; }
@@ -47,7 +53,6 @@ inline void describe(const Variant &v, int id, sgemm_cfg *out)
     out->bk = v.bk;
     out->waves_m = v.waves_m;
     out->waves_n = v.waves_n;
-    out->vec = v.vec;
     out->group_m = 0;
     out->xcd_remap = 0;
     out->grid = 0;
@@ -74,26 +79,37 @@ inline bool finish_cfg(const Variant &v, int id, int M, int N, sgemm_cfg *out)
     return true;
 }
 
-// Index of the MFMA variant with the given tile and path, or -1.
-inline int find_variant(const Variant *vs, int n, int bm, int bn, int bk, int waves, int vec)
+// Per-tile overhead (prologue fetch, epilogue stores, pipeline fill), in
+// 16-deep slices of the same tile.
+constexpr long long kTileOverhead = 24;
+
+// Estimated cost of running variant v on M x N x K (arbitrary units):
+// rounds * tile area * (K slices + overhead) / efficiency.
+inline long long estimate(const Variant &v, int M, int N, int K, int cus)
 {
-    for (int i = 0; i < n; ++i)
-        if (vs[i].kernel == SGEMM_KERNEL_MFMA && vs[i].bm == bm && vs[i].bn == bn &&
-            vs[i].bk == bk && vs[i].waves_m * vs[i].waves_n == waves && vs[i].vec == vec)
-            return i;
-    return -1;
+    const long long tiles = ceil_div_ll(M, v.bm) * ceil_div_ll(N, v.bn);
+    const long long rounds = ceil_div_ll(tiles, cus);
+    long long slices = ceil_div_ll(K, v.bk);
+    if (v.stage_at >= 0) slices += slices & 1;  // pipelined kernels take slices in pairs
+    const long long kpad = slices * v.bk;
+    const long long area = (long long)v.bm * v.bn;
+    const long long work = area * (kpad / 16 + kTileOverhead);
+    return rounds * work * 1000 / v.eff_permille;
 }
 
-inline int select_variant(const Variant *vs, int n, int M, int N, int K, bool vec, int cus)
+inline int select_variant(const Variant *vs, int n, int M, int N, int K, int cus)
 {
-    (void)K;
-    const int v = vec ? 1 : 0;
-    const long long big = ceil_div_ll(M, 256) * ceil_div_ll(N, 256);
-    int id = -1;
-    if (big >= cus) id = find_variant(vs, n, 256, 256, 16, 8, v);
-    if (id < 0) id = find_variant(vs, n, 128, 128, 16, 4, v);
-    if (id < 0) id = 0;
-    return id;
+    int best = -1;
+    long long best_cost = 0;
+    for (int i = 0; i < n; ++i) {
+        if (vs[i].kernel != SGEMM_KERNEL_MFMA || vs[i].eff_permille <= 0) continue;
+        const long long c = estimate(vs[i], M, N, K, cus);
+        if (best < 0 || c < best_cost) {
+            best = i;
+            best_cost = c;
+        }
+    }
+    return best < 0 ? 0 : best;
 }
 
 }  // namespace sgemm

@@ -21,37 +21,38 @@ namespace {
 
 using sgemm::Variant;
 
-template <int BM, int BN, int BK, int WM, int WN, bool VEC>
-constexpr Variant mfma_variant()
+template <int BM, int BN, int BK, int WM, int WN, int STAGE_AT>
+Variant mfma_variant(int eff_permille)
 {
-    typedef sgemm::MfmaTraits<BM, BN, BK, WM, WN, VEC> T;
-    return Variant{SGEMM_KERNEL_MFMA, BM, BN, BK, WM, WN, VEC ? 1 : 0,
+    typedef sgemm::MfmaTraits<BM, BN, BK, WM, WN, STAGE_AT> T;
+    return Variant{SGEMM_KERNEL_MFMA, BM, BN, BK, WM, WN, STAGE_AT,
                    T::NT, (int)(T::LDS_FLOATS * sizeof(float)),
-                   reinterpret_cast<const void *>(&sgemm::sgemm_mfma_kernel<BM, BN, BK, WM, WN, VEC>)};
+                   reinterpret_cast<const void *>(
+                       &sgemm::sgemm_mfma_kernel<BM, BN, BK, WM, WN, STAGE_AT>),
+                   eff_permille};
 }
 
-template <bool VEC>
-constexpr Variant valu_variant()
+Variant valu_variant()
 {
     typedef sgemm::ValuTraits T;
-    return Variant{SGEMM_KERNEL_VALU, T::BM, T::BN, T::BK, 1, 1, VEC ? 1 : 0,
+    return Variant{SGEMM_KERNEL_VALU, T::BM, T::BN, T::BK, 1, 1, -1,
                    T::NT, (int)(T::LDS_FLOATS * sizeof(float)),
-                   reinterpret_cast<const void *>(&sgemm::sgemm_valu_kernel<VEC>)};
+                   reinterpret_cast<const void *>(&sgemm::sgemm_valu_kernel), 0};
 }
 
-// The compiled variants.  Indices are part of the ABI of sgemm_f32_ex.
+// The compiled variants.  Indices are part of the ABI of sgemm_f32_ex.  The
+// last argument is the fraction of the FP32 matrix peak (x1000) the variant
+// sustains at 8192^3 on MI355X, which the selector's cost model uses; 0 keeps
+// a variant out of automatic selection (comparison kernels).
 const Variant kVariants[] = {
-    mfma_variant<256, 256, 16, 4, 2, true>(),   // 0: 8 waves of 64x128
-    mfma_variant<256, 256, 16, 4, 2, false>(),  // 1
-    mfma_variant<128, 128, 16, 2, 2, true>(),   // 2: 4 waves of 64x64
-    mfma_variant<128, 128, 16, 2, 2, false>(),  // 3
-    mfma_variant<256, 128, 16, 4, 1, true>(),   // 4: 4 waves of 64x128
-    mfma_variant<128, 256, 16, 2, 2, true>(),   // 5: 4 waves of 64x128
-    mfma_variant<256, 256, 16, 2, 2, true>(),   // 6: 4 waves of 128x128
-    mfma_variant<128, 128, 32, 2, 2, true>(),   // 7
-    mfma_variant<256, 256, 32, 4, 2, true>(),   // 8
-    valu_variant<true>(),                       // 9: vector-FMA comparison
-    valu_variant<false>(),                      // 10
+    mfma_variant<256, 256, 16, 4, 2, 0>(894),   // 0: 8 waves of 64x128
+    mfma_variant<128, 128, 16, 2, 2, 0>(879),   // 1: 4 waves of 64x64
+    mfma_variant<128, 128, 32, 2, 2, 1>(839),   // 2: 4 waves of 64x64, BK 32
+    mfma_variant<128, 256, 16, 2, 2, 0>(0),     // 3: 4 waves of 64x128
+    mfma_variant<256, 128, 16, 4, 1, 0>(0),     // 4: 4 waves of 64x128
+    mfma_variant<256, 256, 16, 4, 2, -1>(0),    // 5: plain order (comparison)
+    mfma_variant<128, 128, 16, 2, 2, -1>(0),    // 6: plain order (comparison)
+    valu_variant(),                             // 7: vector-FMA comparison
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -79,7 +80,6 @@ hipError_t device_cus(int *cus)
 
 // ---- validation ---------------------------------------------------------------
 bool misaligned4(const void *p) { return ((uintptr_t)p & 3u) != 0; }
-bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Address range [lo, hi) spanned by a rows x cols row-major matrix with stride ld.
 void span(const void *p, int rows, int cols, int ld, uintptr_t &lo, uintptr_t &hi)
@@ -110,14 +110,6 @@ hipError_t validate(int M, int N, int K, const float *A, int lda, const float *B
     return hipSuccess;
 }
 
-bool operands_aligned16(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
-                        const float *C, int ldc)
-{
-    (void)M; (void)N;
-    const bool ab = K == 0 || (aligned16(A) && aligned16(B) && lda % 4 == 0 && ldb % 4 == 0);
-    return ab && aligned16(C) && ldc % 4 == 0;
-}
-
 hipError_t launch(const Variant &v, const sgemm_cfg &cfg, int M, int N, int K,
                   const float *A, int lda, const float *B, int ldb, float *C, int ldc,
                   hipStream_t stream)
@@ -142,16 +134,13 @@ int sgemm_f32_variant(int id, sgemm_cfg *out)
     return hipSuccess;
 }
 
-const char *sgemm_f32_version(void) { return "libsgemm 0.1.0 gfx950 fp32 (mfma_f32_32x32x2 + valu comparison)"; }
+const char *sgemm_f32_version(void) { return "libsgemm 0.2.0 gfx950 fp32 (mfma_f32_32x32x2 + valu comparison)"; }
 
-int sgemm_f32_plan(int M, int N, int K, int lda, int ldb, int ldc, int aligned, int num_cus,
-                   sgemm_cfg *out)
+int sgemm_f32_plan(int M, int N, int K, int lda, int ldb, int ldc, int num_cus, sgemm_cfg *out)
 {
     if (!out || M < 0 || N < 0 || K < 0) return hipErrorInvalidValue;
     if (!sgemm::leading_dims_ok(M, N, K, lda, ldb, ldc)) return hipErrorInvalidValue;
-    const bool vec = aligned && lda % 4 == 0 && ldb % 4 == 0 && ldc % 4 == 0;
-    const int id = sgemm::select_variant(kVariants, kNumVariants, M, N, K, vec,
-                                         num_cus > 0 ? num_cus : 256);
+    const int id = sgemm::select_variant(kVariants, kNumVariants, M, N, K, num_cus > 0 ? num_cus : 256);
     return sgemm::finish_cfg(kVariants[id], id, M, N, out) ? hipSuccess : hipErrorInvalidValue;
 }
 
@@ -164,8 +153,7 @@ int sgemm_f32_query(int M, int N, int K, const float *A, int lda, const float *B
     int cus = 0;
     e = device_cus(&cus);
     if (e != hipSuccess) return e;
-    const bool al = operands_aligned16(M, N, K, A, lda, B, ldb, C, ldc);
-    return sgemm_f32_plan(M, N, K, lda, ldb, ldc, al ? 1 : 0, cus, out);
+    return sgemm_f32_plan(M, N, K, lda, ldb, ldc, cus, out);
 }
 
 int sgemm_f32_ex(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
@@ -174,22 +162,19 @@ int sgemm_f32_ex(int M, int N, int K, const float *A, int lda, const float *B, i
     hipError_t e = validate(M, N, K, A, lda, B, ldb, C, ldc);
     if (e != hipSuccess) return e;
     if (M == 0 || N == 0) return hipSuccess;
-    const bool al = operands_aligned16(M, N, K, A, lda, B, ldb, C, ldc);
     sgemm_cfg cfg;
     int id;
     if (force) {
         id = force->id;
-        if (id < 0 || id >= kNumVariants) return hipErrorInvalidValue;
-        if (kVariants[id].vec && !al) return hipErrorInvalidValue;
+        if (id < 0 || id >= kNumVariants || force->group_m < 0) return hipErrorInvalidValue;
         if (!sgemm::finish_cfg(kVariants[id], id, M, N, &cfg)) return hipErrorInvalidValue;
-        if (force->group_m < 0) return hipErrorInvalidValue;
         cfg.group_m = force->group_m;
         cfg.xcd_remap = force->xcd_remap ? 1 : 0;
     } else {
         int cus = 0;
         e = device_cus(&cus);
         if (e != hipSuccess) return e;
-        id = sgemm::select_variant(kVariants, kNumVariants, M, N, K, al, cus);
+        id = sgemm::select_variant(kVariants, kNumVariants, M, N, K, cus);
         if (!sgemm::finish_cfg(kVariants[id], id, M, N, &cfg)) return hipErrorInvalidValue;
     }
     return launch(kVariants[id], cfg, M, N, K, A, lda, B, ldb, C, ldc, stream);

@@ -8,8 +8,7 @@
 // buffering with one barrier per K slice (section 9).
 #pragma once
 
-#include <hip/hip_runtime.h>
-#include <stdint.h>
+#include "common.hpp"
 
 namespace sgemm {
 
@@ -21,7 +20,6 @@ struct ValuTraits {
     static constexpr int LDS_FLOATS = 2 * (BK * LDA_S + BK * LDB_S);
 };
 
-template <bool VEC>
 __global__ void __launch_bounds__(256)
 sgemm_valu_kernel(int M, int N, int K,
                   const float *__restrict__ A, int lda,
@@ -32,7 +30,7 @@ sgemm_valu_kernel(int M, int N, int K,
     typedef ValuTraits T;
     constexpr int BM = T::BM, BN = T::BN, BK = T::BK;
     constexpr int LDA_S = T::LDA_S, LDB_S = T::LDB_S;
-    typedef float f4 __attribute__((ext_vector_type(4)));
+    typedef f32x4 f4;
 
     __shared__ __attribute__((aligned(16))) float As[2][BK * LDA_S];
     __shared__ __attribute__((aligned(16))) float Bs[2][BK * LDB_S];
@@ -55,25 +53,30 @@ sgemm_valu_kernel(int M, int N, int K,
         for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
 
     f4 ra, rb;
+    // Interior slices: 16-byte loads (dword-aligned suffices).  Edge slices:
+    // dword loads through buffer resources ending at the matrices' last
+    // elements (rows past M or K read as zero) plus a select for columns at
+    // or past K (A) or N (B).
     auto gload = [&](int kt) {
         const int k0 = kt * BK;
-        const bool inside = tile_inside && (k0 + BK <= K);
         const float *pa = A + (int64_t)(m0 + a_row) * lda + (k0 + a_col);
         const float *pb = B + (int64_t)(k0 + b_row) * ldb + (n0 + b_col);
-        if (inside) {
-            if (VEC) {
-                ra = *reinterpret_cast<const f4 *>(pa);
-                rb = *reinterpret_cast<const f4 *>(pb);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) { ra[e] = pa[e]; rb[e] = pb[e]; }
-            }
+        if (tile_inside && k0 + BK <= K) {
+            ra = *reinterpret_cast<const f32x4u *>(pa);
+            rb = *reinterpret_cast<const f32x4u *>(pb);
         } else {
-            const bool av = m0 + a_row < M, bv = k0 + b_row < K;
+            const float *abase = A + (int64_t)m0 * lda + k0;
+            const float *bbase = B + (int64_t)k0 * ldb + n0;
+            const auto ar = make_rsrc(abase, 4 * ((int64_t)(M - 1 - m0) * lda + (K - k0)));
+            const auto br = make_rsrc(bbase, 4 * ((int64_t)(K - 1 - k0) * ldb + (N - n0)));
+            const uint32_t ao = 4u * ((uint32_t)a_row * (uint32_t)lda + (uint32_t)a_col);
+            const uint32_t bo = 4u * ((uint32_t)b_row * (uint32_t)ldb + (uint32_t)b_col);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                ra[e] = (av && k0 + a_col + e < K) ? pa[e] : 0.0f;
-                rb[e] = (bv && n0 + b_col + e < N) ? pb[e] : 0.0f;
+                const float xa = buffer_load_f32(ar, ao + 4u * e);
+                const float xb = buffer_load_f32(br, bo + 4u * e);
+                ra[e] = (k0 + a_col + e < K) ? xa : 0.0f;
+                rb[e] = (n0 + b_col + e < N) ? xb : 0.0f;
             }
         }
     };
@@ -121,9 +124,9 @@ sgemm_valu_kernel(int M, int N, int K,
         for (int h = 0; h < 2; ++h) {
             const int col = n0 + 64 * h + 4 * tx;
             float *p = C + (int64_t)row * ldc + col;
-            if (VEC && col + 3 < N) {
+            if (col + 3 < N) {
                 f4 v = {acc[i][4 * h], acc[i][4 * h + 1], acc[i][4 * h + 2], acc[i][4 * h + 3]};
-                *reinterpret_cast<f4 *>(p) = v;
+                *reinterpret_cast<f32x4u *>(p) = v;
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)

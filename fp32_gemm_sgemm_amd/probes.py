@@ -1,0 +1,51 @@
+"""ctypes binding of libsgemm_probes.so: measurement probes that put the
+GEMM's numbers in context (not part of the product path)."""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+PROBES_PATH = os.path.join(HERE, "libsgemm_probes.so")
+_lib = None
+
+
+def load():
+    global _lib
+    if _lib is None:
+        import torch  # noqa: F401  (same HIP runtime as torch)
+        if not os.path.exists(PROBES_PATH):
+            raise RuntimeError(f"{PROBES_PATH} is not built")
+        lib = ctypes.CDLL(PROBES_PATH)
+        lib.sgemm_probe_mfma_peak.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                              ctypes.c_void_p]
+        lib.sgemm_probe_mfma_peak.restype = ctypes.c_int
+        lib.sgemm_probe_mfma_peak_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+        lib.sgemm_probe_mfma_peak_flops.restype = ctypes.c_double
+        _lib = lib
+    return _lib
+
+
+def mfma_peak_tflops(workgroups_per_cu=2, iters=20000, reps=3):
+    """Sustained v_mfma_f32_32x32x2_f32 throughput of the whole chip, TFLOP/s
+    (best of `reps` launches after one warm-up)."""
+    import torch
+    lib = load()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wgs = cus * workgroups_per_cu
+    out = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    best = 0.0
+    for rep in range(reps + 1):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        rc = lib.sgemm_probe_mfma_peak(wgs, iters, out.data_ptr(), stream.cuda_stream)
+        e1.record(stream)
+        if rc != 0:
+            raise RuntimeError(f"sgemm_probe_mfma_peak failed with hipError_t {rc}")
+        torch.cuda.synchronize()
+        if rep:
+            t = e0.elapsed_time(e1) * 1e-3
+            best = max(best, lib.sgemm_probe_mfma_peak_flops(wgs, iters) / t / 1e12)
+    if not torch.isfinite(out).all():
+        raise RuntimeError("probe produced non-finite values")
+    return best

@@ -37,8 +37,6 @@ typedef struct sgemm_cfg {
     int kernel;    /* SGEMM_KERNEL_MFMA or SGEMM_KERNEL_VALU */
     int bm, bn, bk;       /* workgroup tile: BM x BN outputs, BK-deep K slices */
     int waves_m, waves_n; /* wavefront grid inside a workgroup */
-    int vec;       /* 1: 16-byte global loads/stores (needs 16-byte aligned
-                      A, B, C and lda, ldb, ldc multiples of 4); 0: dword path */
     int group_m;   /* raster: tile rows per group, walked column by column
                       (0 = plain row-major order over tiles) */
     int xcd_remap; /* 1: give each XCD a contiguous run of logical tiles */
@@ -60,9 +58,10 @@ typedef struct sgemm_cfg {
  *             C is overwritten and never read; elements j >= N of each row
  *             (the padding up to ldc) are left untouched.
  *   stream    a HIP stream of the current device.
- * Pointers must be 4-byte aligned.  A 16-byte vector path is taken when A, B
- * and C are 16-byte aligned and lda, ldb, ldc are multiples of 4; otherwise a
- * dword path gives the same results.
+ * Pointers must be 4-byte aligned; any dword-aligned start and stride runs on
+ * the same kernels (16-byte loads and stores need only dword alignment on
+ * gfx950).  Limits: M, N, K <= INT_MAX - 1024, lda <= 2^22 - 64,
+ * ldb <= 2^25 - 512 (byte offsets inside one K slice are 32-bit).
  *
  * Semantics of degenerate sizes: M == 0 or N == 0 does nothing; K == 0 sets
  * the M x N block of C to zero (an empty sum).
@@ -87,11 +86,11 @@ int sgemm_f32(int M, int N, int K,
 
 /*
  * sgemm_f32_ex: sgemm_f32 with a forced configuration, for sweeps and for the
- * measured comparison kernel.  cfg == NULL behaves as sgemm_f32.  Otherwise
- * cfg->id selects the variant (see sgemm_f32_variant) and cfg->group_m and
- * cfg->xcd_remap set the tile order; the other fields are ignored.  A vector
- * variant on operands that do not meet its alignment returns
- * hipErrorInvalidValue.  Same arguments, ownership and errors as sgemm_f32.
+ * measured comparison kernels.  cfg == NULL behaves as sgemm_f32.  Otherwise
+ * cfg->id selects the variant (see sgemm_f32_variant; an id out of range, or
+ * cfg->group_m < 0, returns hipErrorInvalidValue) and cfg->group_m and
+ * cfg->xcd_remap set the tile order; the other fields are ignored.  Same
+ * arguments, ownership and errors as sgemm_f32.
  */
 int sgemm_f32_ex(int M, int N, int K,
                  const float *A, int lda,
@@ -100,15 +99,15 @@ int sgemm_f32_ex(int M, int N, int K,
                  hipStream_t stream, const sgemm_cfg *cfg);
 
 /*
- * sgemm_f32_plan: the configuration sgemm_f32 chooses for these sizes, with
- * `aligned16` = 1 when A, B and C are 16-byte aligned, on a device with
- * `num_cus` compute units (<= 0 means 256).  Pure host logic, no HIP call.
- * Writes *out; returns hipErrorInvalidValue for invalid sizes or out == NULL.
- * The geometry fields follow the round-up-and-guard rule: tiles_m =
- * ceil(M/BM), tiles_n = ceil(N/BN), grid = tiles_m * tiles_n.
+ * sgemm_f32_plan: the configuration sgemm_f32 chooses for these sizes on a
+ * device with `num_cus` compute units (<= 0 means 256).  Pure host logic, no
+ * HIP call.  Writes *out; returns hipErrorInvalidValue for invalid sizes or
+ * leading dimensions, or out == NULL.  The geometry fields follow the
+ * round-up-and-guard rule (DD2360 workbook, Module 6, section 6.3):
+ * tiles_m = ceil(M/BM), tiles_n = ceil(N/BN), grid = tiles_m * tiles_n.
  */
 int sgemm_f32_plan(int M, int N, int K, int lda, int ldb, int ldc,
-                   int aligned16, int num_cus, sgemm_cfg *out);
+                   int num_cus, sgemm_cfg *out);
 
 /*
  * sgemm_f32_query: the configuration sgemm_f32 would launch for these

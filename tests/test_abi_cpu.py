@@ -108,17 +108,14 @@ def test_ex_rejects_bad_forced_variant(lib):
     cfg.id = sg.sgemm_f32_num_variants()
     assert sg.sgemm_f32_ex(4, 4, 4, P, 4, 2 * P, 4, 3 * P, 4, 0, cfg) == HIP_ERROR_INVALID_VALUE
     cfg.id = 0
-    cfg.group_m = -1
+    cfg.group_m = -1  # negative group height
     assert sg.sgemm_f32_ex(4, 4, 4, P, 4, 2 * P, 4, 3 * P, 4, 0, cfg) == HIP_ERROR_INVALID_VALUE
 
 
-def test_ex_rejects_vector_variant_on_misaligned_operands(lib):
-    vec_ids = [i for i in range(sg.sgemm_f32_num_variants()) if sg.sgemm_f32_variant(i).vec]
-    assert vec_ids
-    cfg = sg.binding.SgemmCfg()
-    cfg.id = vec_ids[0]
-    # lda = 4099 is not a multiple of 4: the 16-byte path cannot be used
-    assert sg.sgemm_f32_ex(8, 8, 4099, P, 4099, 2 * P, 8, 4 * P, 8, 0, cfg) == HIP_ERROR_INVALID_VALUE
+def test_ex_rejects_limits(lib):
+    # lda beyond the 32-bit in-slice offset limit
+    assert sg.sgemm_f32(4, 4, 4, P, 1 << 22, 2 * P, 4, 3 * P, 4, 0) == HIP_ERROR_INVALID_VALUE
+    assert sg.sgemm_f32(4, 4, 4, P, 4, 2 * P, 1 << 25, 3 * P, 4, 0) == HIP_ERROR_INVALID_VALUE
 
 
 SHAPES = [(512, 512, 512), (2048, 2048, 2048), (3072, 3072, 3072), (8192, 8192, 4096),
@@ -128,21 +125,27 @@ SHAPES = [(512, 512, 512), (2048, 2048, 2048), (3072, 3072, 3072), (8192, 8192, 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
 def test_plan_geometry(lib, M, N, K):
-    for aligned in (0, 1):
-        p = sg.sgemm_f32_plan(M, N, K, max(K, 1), N, N, aligned, 256)
+    for cus in (256, 80):
+        p = sg.sgemm_f32_plan(M, N, K, max(K, 1), N, N, cus)
         assert p.kernel == sg.binding.SGEMM_KERNEL_MFMA
         assert p.tiles_m == metrics.ceil_div(M, p.bm)
         assert p.tiles_n == metrics.ceil_div(N, p.bn)
         assert p.grid == p.tiles_m * p.tiles_n
-        vec_ok = aligned and K % 4 == 0 and N % 4 == 0 or (aligned and K == 0 and N % 4 == 0)
-        if not vec_ok:
-            assert p.vec == 0
-        if M == 4099:
-            assert p.vec == 0      # rows are not 16-byte aligned at ld = 4099
+        assert p.threads == 64 * p.waves_m * p.waves_n
+        assert p.group_m > 0 and p.xcd_remap == 1
+
+
+def test_selector_prefers_full_waves(lib):
+    """Wave quantisation on 256 CUs: 2048^3 has only 64 tiles of 256 x 256 but
+    256 of 128 x 128, and 3072^3 144 versus 576; big squares fill either way."""
+    assert sg.sgemm_f32_plan(2048, 2048, 2048, 2048, 2048, 2048, 256).bm == 128
+    assert sg.sgemm_f32_plan(3072, 3072, 3072, 3072, 3072, 3072, 256).bm == 128
+    p = sg.sgemm_f32_plan(8192, 8192, 8192, 8192, 8192, 8192, 256)
+    assert p.grid * p.bm * p.bn == 8192 * 8192
 
 
 def test_plan_rejects_invalid(lib):
     out = sg.binding.SgemmCfg()
-    assert lib.sgemm_f32_plan(-1, 4, 4, 4, 4, 4, 1, 256, ctypes.byref(out)) == HIP_ERROR_INVALID_VALUE
-    assert lib.sgemm_f32_plan(4, 4, 8, 4, 4, 4, 1, 256, ctypes.byref(out)) == HIP_ERROR_INVALID_VALUE
-    assert lib.sgemm_f32_plan(4, 4, 4, 4, 4, 4, 1, 256, None) == HIP_ERROR_INVALID_VALUE
+    assert lib.sgemm_f32_plan(-1, 4, 4, 4, 4, 4, 256, ctypes.byref(out)) == HIP_ERROR_INVALID_VALUE
+    assert lib.sgemm_f32_plan(4, 4, 8, 4, 4, 4, 256, ctypes.byref(out)) == HIP_ERROR_INVALID_VALUE
+    assert lib.sgemm_f32_plan(4, 4, 4, 4, 4, 4, 256, None) == HIP_ERROR_INVALID_VALUE
