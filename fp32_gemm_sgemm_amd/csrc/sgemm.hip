@@ -42,8 +42,9 @@ Variant valu_variant()
 
 // The compiled variants.  Indices are part of the ABI of sgemm_f32_ex.  The
 // last argument is the fraction of the FP32 matrix peak (x1000) the variant
-// sustains at 8192^3 on MI355X, which the selector's cost model uses; 0 keeps
-// a variant out of automatic selection (comparison kernels).
+// sustains per round of full tiles on MI355X (measured at 8192^3 and divided
+// by that shape's wave quantisation), which the selector's cost model uses;
+// 0 keeps a variant out of automatic selection (comparison kernels).
 const Variant kVariants[] = {
     mfma_variant<256, 256, 16, 4, 2, 0>(894),   // 0: 8 waves of 64x128
     mfma_variant<128, 128, 16, 2, 2, 0>(879),   // 1: 4 waves of 64x64
@@ -53,6 +54,8 @@ const Variant kVariants[] = {
     mfma_variant<256, 256, 16, 4, 2, -1>(0),    // 5: plain order (comparison)
     mfma_variant<128, 128, 16, 2, 2, -1>(0),    // 6: plain order (comparison)
     valu_variant(),                             // 7: vector-FMA comparison
+    mfma_variant<192, 192, 16, 2, 6, 0>(746),   // 8: 12 waves of 96x32
+    mfma_variant<192, 192, 32, 2, 6, 1>(782),   // 9: 12 waves of 96x32, BK 32
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 

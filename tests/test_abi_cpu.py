@@ -137,9 +137,11 @@ def test_plan_geometry(lib, M, N, K):
 
 def test_selector_prefers_full_waves(lib):
     """Wave quantisation on 256 CUs: 2048^3 has only 64 tiles of 256 x 256 but
-    256 of 128 x 128, and 3072^3 144 versus 576; big squares fill either way."""
+    256 of 128 x 128; 3072^3 has 144 of 256 x 256, 576 of 128 x 128 and exactly
+    256 of 192 x 192; 8192^3 fills the chip with the largest tile."""
     assert sg.sgemm_f32_plan(2048, 2048, 2048, 2048, 2048, 2048, 256).bm == 128
-    assert sg.sgemm_f32_plan(3072, 3072, 3072, 3072, 3072, 3072, 256).bm == 128
+    p = sg.sgemm_f32_plan(3072, 3072, 3072, 3072, 3072, 3072, 256)
+    assert p.grid == 256 and p.bm == 192          # one 192 x 192 tile per CU
     p = sg.sgemm_f32_plan(8192, 8192, 8192, 8192, 8192, 8192, 256)
     assert p.grid * p.bm * p.bn == 8192 * 8192
 
