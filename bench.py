@@ -37,7 +37,7 @@ METRIC = "SGEMM TFLOP/s and % of FP32 matrix peak at 3072³ and 8192³, 1×MI355
 HEADLINE = "sgemm_8192x8192x8192_uniform_seed4"
 SECONDARY = "sgemm_3072x3072x3072_normal_seed2"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sgemm_8192x8192x8192_traffic.txt")
-KERNEL_SOURCES = ["sgemm_mfma.hpp", "common.hpp"]
+KERNEL_SOURCES = ["sgemm_mfma.hpp", "sgemm_mfma_dl.hpp", "common.hpp"]
 
 
 def kernel_source_hash():

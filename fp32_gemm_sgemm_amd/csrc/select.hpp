@@ -20,7 +20,8 @@ struct Variant {
     int kernel;
     int bm, bn, bk;
     int waves_m, waves_n;
-    int stage_at;
+    int stage_at;      // register-staged kernel: LDS write after this k group
+    int stages;        // direct-load kernel: LDS stages (0 = register-staged kernel)
     int threads;
     int lds_bytes;
     const void *fn;
@@ -90,19 +91,23 @@ inline long long estimate(const Variant &v, int M, int N, int K, int cus)
     const long long tiles = ceil_div_ll(M, v.bm) * ceil_div_ll(N, v.bn);
     const long long rounds = ceil_div_ll(tiles, cus);
     long long slices = ceil_div_ll(K, v.bk);
-    if (v.stage_at >= 0) slices += slices & 1;  // pipelined kernels take slices in pairs
+    if (v.stages == 0 && v.stage_at >= 0) slices += slices & 1;  // register pipeline takes pairs
     const long long kpad = slices * v.bk;
     const long long area = (long long)v.bm * v.bn;
     const long long work = area * (kpad / 16 + kTileOverhead);
     return rounds * work * 1000 / v.eff_permille;
 }
 
-inline int select_variant(const Variant *vs, int n, int M, int N, int K, int cus)
+// direct_ok: the operands allow direct global -> LDS loads (16-byte aligned
+// rows); otherwise the direct-load variants would fetch every slice through
+// registers and are left out.
+inline int select_variant(const Variant *vs, int n, int M, int N, int K, int cus, bool direct_ok)
 {
     int best = -1;
     long long best_cost = 0;
     for (int i = 0; i < n; ++i) {
         if (vs[i].kernel != SGEMM_KERNEL_MFMA || vs[i].eff_permille <= 0) continue;
+        if (vs[i].stages > 0 && !direct_ok) continue;
         const long long c = estimate(vs[i], M, N, K, cus);
         if (best < 0 || c < best_cost) {
             best = i;

@@ -80,7 +80,7 @@ sgemm_mfma_kernel(int M, int N, int K,
                   const float *__restrict__ A, int lda,
                   const float *__restrict__ B, int ldb,
                   float *__restrict__ C, int ldc,
-                  int tiles_m, int tiles_n, int group_m, int xcd_remap)
+                  int tiles_m, int tiles_n, int group_m, int xcd_remap, int /*direct*/)
 {
     typedef MfmaTraits<BM, BN, BK, WAVES_M, WAVES_N, STAGE_AT> T;
     constexpr int NT = T::NT, WTM = T::WTM, WTN = T::WTN, RM = T::RM, NB = T::NB;

@@ -25,7 +25,7 @@ sgemm_valu_kernel(int M, int N, int K,
                   const float *__restrict__ A, int lda,
                   const float *__restrict__ B, int ldb,
                   float *__restrict__ C, int ldc,
-                  int tiles_m, int tiles_n, int group_m, int xcd_remap)
+                  int tiles_m, int tiles_n, int group_m, int xcd_remap, int /*direct*/)
 {
     typedef ValuTraits T;
     constexpr int BM = T::BM, BN = T::BN, BK = T::BK;

@@ -45,6 +45,14 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, name)
 
 
+def test_no_undefined_own_symbols(lib):
+    """Every kernel's host-side stub is present (a kernel template whose body
+    cannot be compiled for the host would otherwise be left undefined)."""
+    out = subprocess.run(["nm", "-D", "--undefined-only", sg.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    assert "sgemm" not in out, out
+
+
 def test_version_and_variants(lib):
     assert "gfx950" in sg.sgemm_f32_version()
     n = sg.sgemm_f32_num_variants()

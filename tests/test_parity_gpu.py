@@ -261,6 +261,36 @@ def test_tile_orders_cover_every_tile(group_m, xcd):
         check_full(C, A, B)
 
 
+@pytest.mark.parametrize("M,N,K,shift", [(520, 700, 300, 0), (517, 701, 303, 0),
+                                          (300, 260, 200, 1), (257, 513, 4099, 1)])
+def test_direct_load_kernels_on_every_fetch_path(M, N, K, shift):
+    """Forced direct-load variants: 16-byte aligned operands with K and N
+    multiples of 4 (direct path, zero chunks past the edge), K or N not a
+    multiple of 4 (partial-chunk slices fetched through registers), and
+    operands one float off 16-byte alignment (register fetch for every
+    slice)."""
+    A, B = inputs.make_operands(M, N, K, seed=49 + K)
+
+    def place(x):
+        if not shift:
+            return to_device(x)
+        flat = torch.empty(x.size + shift, dtype=torch.float32, device="cuda")
+        v = flat[shift:].view(x.shape)
+        v.copy_(torch.from_numpy(x))
+        return v
+
+    for vid in range(sg.sgemm_f32_num_variants()):
+        v = sg.sgemm_f32_variant(vid)
+        if v.kernel != sg.SGEMM_KERNEL_MFMA:
+            continue
+        note(f"fetch paths variant {vid} M={M} N={N} K={K} shift={shift}")
+        Ad, Bd = place(A), place(B)
+        out = torch.full((M, N), float("nan"), device="cuda")
+        sg.sgemm(Ad, Bd, out=out, cfg=forced(vid))
+        torch.cuda.synchronize()
+        check_full(out.cpu().numpy(), A, B)
+
+
 def test_long_k_single_tile():
     """128 x 128 x 32768: the one-tile, long-K shape of the cuda-kernels README."""
     note("128x128x32768")
