@@ -19,36 +19,117 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
 typedef float f32x2u __attribute__((ext_vector_type(2), aligned(4)));
 
-// Linear workgroup id -> (tile row, tile column).
+// One GEMM launch, passed to every kernel by value.
+//
+// The launch computes, for every batch entry z and every K split s,
+//   C_z,s[i*ldc + j] = alpha * sum_{k in split s} op(A_z)(i,k) * op(B_z)(k,j)
+//                      + beta * C_z,s[i*ldc + j]
+// where op(X) is X (row-major, X[r*ld + c]) or its transpose (X[c*ld + r]).
+// Without a K split (splits == 1) that is the whole product; with one, the
+// host points C at a workspace that receives one partial result per split
+// (alpha 1, beta 0) and a second kernel adds them up in a fixed order.
+struct GemmArgs {
+    const float *A;
+    const float *B;
+    float *C;
+    int64_t batch_a, batch_b, batch_c;  // elements between batch entries
+    int64_t split_c;                    // elements between the partials of splits s and s+1
+    int M, N, K;
+    int lda, ldb, ldc;
+    int k_chunk;                        // K range of one split (>= K when splits == 1)
+    int splits;
+    int tiles_m, tiles_n;
+    int group_m, xcd_remap;
+    int wg_base;                        // logical id of this launch's first workgroup
+    int direct;                         // operands allow direct global -> LDS loads
+    float alpha, beta;
+};
+
+// Workgroup -> (tile row, tile column, K split, batch entry).
 //
 // The dispatcher hands workgroups to the 8 XCDs round-robin by linear id, and
 // each XCD has its own L2.  With xcd_remap, the workgroups that land on one
 // XCD get a contiguous run of logical ids, so tiles that share A rows and B
-// columns share an L2.  group_m > 0 then walks the logical ids down groups of
-// group_m tile rows, column by column, so a run of consecutive ids covers a
-// compact block of tiles instead of one long tile row.  Both maps are
-// bijections of [0, tiles_m * tiles_n).
-__device__ __forceinline__ void map_tile(int wg, int nwg, int tiles_m, int tiles_n,
-                                         int group_m, int xcd_remap, int &tm, int &tn)
+// columns share an L2.  A logical id walks the tiles of one (split, batch)
+// pair before the next, and inside them, with group_m > 0, groups of group_m
+// tile rows column by column, so a run of consecutive ids covers a compact
+// block of tiles instead of one long tile row.  Every map is a bijection of
+// the launch's workgroups onto [wg_base, wg_base + gridDim.x).
+struct Work {
+    int tm, tn, split, batch;
+};
+
+__device__ __forceinline__ Work map_work(const GemmArgs &g)
 {
-    if (xcd_remap) {
+    int wg = blockIdx.x;
+    if (g.xcd_remap) {
         constexpr int NX = 8;
+        const int nwg = gridDim.x;
         const int x = wg % NX, idx = wg / NX;
         const int q = nwg / NX, r = nwg % NX;
         wg = x * q + (x < r ? x : r) + idx;
     }
-    if (group_m > 0) {
-        const int per_group = group_m * tiles_n;
-        const int g = wg / per_group;
-        const int first = g * group_m;
-        const int rows = min(tiles_m - first, group_m);
-        const int in = wg - g * per_group;
-        tm = first + in % rows;
-        tn = in / rows;
+    wg += g.wg_base;
+    const int tiles = g.tiles_m * g.tiles_n;
+    const int rest = wg / tiles;
+    const int t = wg - rest * tiles;
+    Work w;
+    w.split = rest % g.splits;
+    w.batch = rest / g.splits;
+    if (g.group_m > 0) {
+        const int per_group = g.group_m * g.tiles_n;
+        const int grp = t / per_group;
+        const int first = grp * g.group_m;
+        const int rows = min(g.tiles_m - first, g.group_m);
+        const int in = t - grp * per_group;
+        w.tm = first + in % rows;
+        w.tn = in / rows;
     } else {
-        tm = wg / tiles_n;
-        tn = wg - tm * tiles_n;
+        w.tm = t / g.tiles_n;
+        w.tn = t - w.tm * g.tiles_n;
     }
+    return w;
+}
+
+// Moves A, B and C to the batch entry and K split of `w` and narrows K to
+// that split's range (the operands' k index runs along rows of B and of a
+// transposed A, along columns otherwise).
+template <bool TA, bool TB>
+__device__ __forceinline__ void locate(GemmArgs &g, const Work &w)
+{
+    const int kb = w.split * g.k_chunk;
+    g.A += w.batch * g.batch_a + (TA ? (int64_t)kb * g.lda : (int64_t)kb);
+    g.B += w.batch * g.batch_b + (TB ? (int64_t)kb : (int64_t)kb * g.ldb);
+    g.C += w.batch * g.batch_c + w.split * g.split_c;
+    g.K = min(g.K - kb, g.k_chunk);
+}
+
+// Epilogue: W adjacent results v[0..W-1] of one C row go to p[0..W-1]
+// (column col .. col+W-1), masked to columns below N, as alpha * v + beta * old.
+// C is read only when beta != 0, so with beta == 0 whatever it held (NaN
+// included) is simply overwritten.
+template <int W>
+__device__ __forceinline__ void store_row(float *p, int col, int N, const float (&v)[W],
+                                          float alpha, float beta)
+{
+    if constexpr (W > 1) {
+        if (col + W - 1 < N) {
+            typedef float vec_t __attribute__((ext_vector_type(W), aligned(4)));
+            vec_t x;
+#pragma unroll
+            for (int j = 0; j < W; ++j) x[j] = alpha * v[j];
+            if (beta != 0.0f) {
+                const vec_t old = *reinterpret_cast<const vec_t *>(p);
+#pragma unroll
+                for (int j = 0; j < W; ++j) x[j] += beta * old[j];
+            }
+            *reinterpret_cast<vec_t *>(p) = x;
+            return;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < W; ++j)
+        if (col + j < N) p[j] = beta != 0.0f ? alpha * v[j] + beta * p[j] : alpha * v[j];
 }
 
 // A raw buffer resource over [base, base + bytes): loads at or past its end

@@ -1,16 +1,21 @@
-// Variant description and the shape-aware selector: pure host integer logic,
-// no HIP calls, so it can be exercised without a device.
+// Variant description and the shape-aware selector: pure host logic, no HIP
+// calls, so it can be exercised without a device.
 //
 // Geometry uses round-up-and-guard sizing (DD2360 workbook "Applied GPU
 // Programming", Module 6, section 6.3): tiles_m = ceil(M/BM),
-// tiles_n = ceil(N/BN), one workgroup per tile.  The selector weighs per-tile
-// efficiency against wave quantisation: on S compute units a grid of n equal
-// tiles takes ceil(n/S) rounds ("4.1 CUDA GEMM operator performance
-// optimization", section 12.5 on launching at least as many blocks as SMs and
-// tuning per shape; the workbook's Module 17 on the tail effect).
+// tiles_n = ceil(N/BN), one workgroup per tile, K split and batch entry.
+// The selector weighs per-tile efficiency against wave quantisation: on S
+// compute units a grid of n equal workgroups takes ceil(n/S) rounds ("4.1
+// CUDA GEMM operator performance optimization", section 12.5 on launching at
+// least as many blocks as SMs and tuning per shape; the workbook's Module 17
+// on the tail effect).  When a grid has too few tiles, splitting K across
+// workgroups adds rounds' worth of parallel work at the price of a second,
+// memory-bound pass that adds the partial results (the split-K stage of the
+// "cuda-kernels" README).
 #pragma once
 
 #include <limits.h>
+#include <stdint.h>
 
 #include "sgemm.h"
 
@@ -24,26 +29,81 @@ struct Variant {
     int stages;        // direct-load kernel: LDS stages (0 = register-staged kernel)
     int threads;
     int lds_bytes;
-    const void *fn;
-    int eff_permille;  // measured steady-state fraction of the FP32 matrix peak
-                       // (x1000) at 8192^3; 0 = never chosen by the selector
+    const void *fn[4];  // kernel per operand layout, index transa + 2*transb (null: none)
+    int eff_permille;   // measured steady-state fraction of the FP32 matrix peak
+                        // (x1000) on full tiles; 0 = never chosen by the selector
 };
 
-// Largest sizes accepted: k0 + BK and similar sums stay in int, and the byte
-// offsets of a thread inside one slice ((BM-1)*lda + BK floats of A,
-// (BK-1)*ldb + BN floats of B) stay below 2^32.
-constexpr int kMaxDim = INT_MAX - 1024;
-constexpr int kMaxLda = (1 << 22) - 64;
-constexpr int kMaxLdb = (1 << 25) - 512;
+// One call as the planner sees it.
+struct Problem {
+    int transa, transb;
+    int M, N, K;
+    int lda, ldb, ldc;
+    int batch;
+};
 
-inline bool leading_dims_ok(int M, int N, int K, int lda, int ldb, int ldc)
+inline int op_index(const Problem &p) { return p.transa + 2 * p.transb; }
+
+// Largest sizes accepted.  k0 + BK and similar sums stay in int, and the byte
+// offsets of a thread inside one slice stay below 2^32: up to 256 rows of a
+// k-contiguous operand (A, or a transposed B) and 32 rows of an
+// index-contiguous one (B, or a transposed A).
+constexpr int kMaxDim = INT_MAX - 1024;
+constexpr int kMaxLdK = (1 << 22) - 64;
+constexpr int kMaxLdX = (1 << 25) - 512;
+// Direct global -> LDS loads keep those offsets below 2^31 (the offset given
+// to chunks that must read as zero).
+constexpr int kMaxLdKDirect = 1 << 20;
+constexpr int kMaxLdXDirect = 1 << 24;
+
+inline bool sizes_ok(const Problem &p)
 {
-    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return false;
-    const int mk = K > 1 ? K : 1, mn = N > 1 ? N : 1;
-    return lda >= mk && ldb >= mn && ldc >= mn && lda <= kMaxLda && ldb <= kMaxLdb;
+    if (p.transa < 0 || p.transa > 1 || p.transb < 0 || p.transb > 1) return false;
+    if (p.M < 0 || p.N < 0 || p.K < 0 || p.batch < 0) return false;
+    if (p.M > kMaxDim || p.N > kMaxDim || p.K > kMaxDim) return false;
+    const int a_min = p.transa ? p.M : p.K, b_min = p.transb ? p.K : p.N;
+    if (p.lda < (a_min > 1 ? a_min : 1) || p.ldb < (b_min > 1 ? b_min : 1) ||
+        p.ldc < (p.N > 1 ? p.N : 1))
+        return false;
+    return p.lda <= (p.transa ? kMaxLdX : kMaxLdK) && p.ldb <= (p.transb ? kMaxLdK : kMaxLdX);
+}
+
+inline bool direct_lds_ok(const Problem &p)
+{
+    return p.lda <= (p.transa ? kMaxLdXDirect : kMaxLdKDirect) &&
+           p.ldb <= (p.transb ? kMaxLdKDirect : kMaxLdXDirect);
 }
 
 inline long long ceil_div_ll(long long a, long long b) { return (a + b - 1) / b; }
+
+// K per split is a multiple of this: of every variant's slice depth (and of
+// the register-staged kernel's slice pairs).
+constexpr int kSplitAlign = 64;
+constexpr int kMaxSplits = 64;
+
+// Split count and K range of one split for a requested split count.
+inline void split_k(int K, int want, int &splits, int &k_chunk)
+{
+    if (want <= 1 || K <= kSplitAlign) {
+        splits = 1;
+        k_chunk = K > 0 ? K : 1;
+        return;
+    }
+    if (want > kMaxSplits) want = kMaxSplits;
+    const long long per = ceil_div_ll(K, want);
+    k_chunk = (int)(ceil_div_ll(per, kSplitAlign) * kSplitAlign);
+    splits = (int)ceil_div_ll(K, k_chunk);
+    if (splits <= 1) k_chunk = K;
+}
+
+// Row stride of the partial results (16-byte rows).
+inline long long partial_ld(int N) { return ((long long)N + 3) & ~3ll; }
+
+inline long long split_workspace_bytes(const Problem &p, int splits)
+{
+    if (splits <= 1) return 0;
+    return (long long)p.batch * splits * p.M * partial_ld(p.N) * 4;
+}
 
 inline void describe(const Variant &v, int id, sgemm_cfg *out)
 {
@@ -56,65 +116,109 @@ inline void describe(const Variant &v, int id, sgemm_cfg *out)
     out->waves_n = v.waves_n;
     out->group_m = 0;
     out->xcd_remap = 0;
+    out->splits = 1;
+    out->k_chunk = 0;
     out->grid = 0;
     out->threads = v.threads;
     out->lds_bytes = v.lds_bytes;
     out->tiles_m = 0;
     out->tiles_n = 0;
+    out->workspace_bytes = 0;
 }
 
 // Default tile order: groups of 8 tile rows and the XCD remap.
 constexpr int kDefaultGroupM = 8;
 constexpr int kDefaultXcdRemap = 1;
 
-inline bool finish_cfg(const Variant &v, int id, int M, int N, sgemm_cfg *out)
+// Fills the geometry of variant v with `want` K splits; false if the grid
+// does not fit in an int.
+inline bool finish_cfg(const Variant &v, int id, const Problem &p, int want, sgemm_cfg *out)
 {
     describe(v, id, out);
-    const long long tm = ceil_div_ll(M, v.bm), tn = ceil_div_ll(N, v.bn);
-    if (tm * tn > INT_MAX) return false;
+    int splits, k_chunk;
+    split_k(p.K, want, splits, k_chunk);
+    const long long tm = ceil_div_ll(p.M, v.bm), tn = ceil_div_ll(p.N, v.bn);
+    const long long grid = tm * tn * splits * (long long)p.batch;
+    if (tm * tn > INT_MAX || grid > INT_MAX) return false;
     out->tiles_m = (int)tm;
     out->tiles_n = (int)tn;
-    out->grid = (int)(tm * tn);
+    out->grid = (int)grid;
+    out->splits = splits;
+    out->k_chunk = k_chunk;
+    out->workspace_bytes = split_workspace_bytes(p, splits);
     out->group_m = kDefaultGroupM;
     out->xcd_remap = kDefaultXcdRemap;
     return true;
 }
 
-// Per-tile overhead (prologue fetch, epilogue stores, pipeline fill), in
-// 16-deep slices of the same tile.
-constexpr long long kTileOverhead = 24;
+// ---- cost model (nanoseconds) ---------------------------------------------------
+// One compute unit at the FP32 matrix peak: 157.3 TFLOP/s over 256 CUs.
+constexpr double kCuFlopPerNs = 157.3e3 / 256.0;
+// Fixed cost of one tile (prologue fetch, pipeline fill, epilogue stores).
+constexpr double kTileFixedNs = 2500.0;
+// The reduction pass: start-up of the second launch, and the rate at which
+// it streams partials (mostly from L2 and MALL) and writes C.
+constexpr double kReduceFixedNs = 3000.0;
+constexpr double kReduceBytesPerNs = 3000.0;
 
-// Estimated cost of running variant v on M x N x K (arbitrary units):
-// rounds * tile area * (K slices + overhead) / efficiency.
-inline long long estimate(const Variant &v, int M, int N, int K, int cus)
+inline double estimate_ns(const Variant &v, const Problem &p, int splits, int k_chunk, int cus)
 {
-    const long long tiles = ceil_div_ll(M, v.bm) * ceil_div_ll(N, v.bn);
+    const long long tiles = ceil_div_ll(p.M, v.bm) * ceil_div_ll(p.N, v.bn) * splits * (long long)p.batch;
     const long long rounds = ceil_div_ll(tiles, cus);
-    long long slices = ceil_div_ll(K, v.bk);
+    const int kc = splits > 1 ? k_chunk : p.K;
+    long long slices = ceil_div_ll(kc, v.bk);
     if (v.stages == 0 && v.stage_at >= 0) slices += slices & 1;  // register pipeline takes pairs
-    const long long kpad = slices * v.bk;
-    const long long area = (long long)v.bm * v.bn;
-    const long long work = area * (kpad / 16 + kTileOverhead);
-    return rounds * work * 1000 / v.eff_permille;
+    const double slice_ns = 2.0 * v.bm * v.bn * v.bk / (kCuFlopPerNs * v.eff_permille / 1000.0);
+    double t = (double)rounds * (kTileFixedNs + (double)slices * slice_ns);
+    if (splits > 1)
+        t += kReduceFixedNs +
+             4.0 * (double)p.batch * p.M * (double)partial_ld(p.N) * (splits + 1) / kReduceBytesPerNs;
+    return t;
 }
 
-// direct_ok: the operands allow direct global -> LDS loads (16-byte aligned
-// rows); otherwise the direct-load variants would fetch every slice through
-// registers and are left out.
-inline int select_variant(const Variant *vs, int n, int M, int N, int K, int cus, bool direct_ok)
+struct Choice {
+    int id;
+    int splits;
+};
+
+// Candidate split counts tried by the selector.
+constexpr int kSplitCandidates[] = {1, 2, 3, 4, 5, 6, 8, 10, 12, 16, 20, 24, 32, 48, 64};
+
+// The fastest (variant, split count) by the cost model among the variants
+// compiled for the operand layout whose workspace fits in `workspace_bytes`.
+// direct_ok: the operands allow direct global -> LDS loads; otherwise a
+// direct-load variant would fetch every slice through registers and is used
+// only when nothing else is compiled for the layout.  Returns id -1 if no
+// variant serves the layout.
+inline Choice select_plan(const Variant *vs, int n, const Problem &p, int cus, bool direct_ok,
+                          long long workspace_bytes)
 {
-    int best = -1;
-    long long best_cost = 0;
-    for (int i = 0; i < n; ++i) {
-        if (vs[i].kernel != SGEMM_KERNEL_MFMA || vs[i].eff_permille <= 0) continue;
-        if (vs[i].stages > 0 && !direct_ok) continue;
-        const long long c = estimate(vs[i], M, N, K, cus);
-        if (best < 0 || c < best_cost) {
-            best = i;
-            best_cost = c;
+    const int op = op_index(p);
+    Choice best = {-1, 1};
+    double best_t = 0;
+    for (int pass = 0; pass < 2 && best.id < 0; ++pass) {
+        for (int i = 0; i < n; ++i) {
+            const Variant &v = vs[i];
+            if (v.kernel != SGEMM_KERNEL_MFMA || v.eff_permille <= 0 || !v.fn[op]) continue;
+            if (pass == 0 && v.stages > 0 && !direct_ok) continue;
+            int last = 0;
+            for (int want : kSplitCandidates) {
+                int splits, k_chunk;
+                split_k(p.K, want, splits, k_chunk);
+                if (splits <= last) continue;
+                last = splits;
+                if (split_workspace_bytes(p, splits) > workspace_bytes) break;
+                const long long grid = ceil_div_ll(p.M, v.bm) * ceil_div_ll(p.N, v.bn) * splits * (long long)p.batch;
+                if (grid > INT_MAX) break;
+                const double t = estimate_ns(v, p, splits, k_chunk, cus);
+                if (best.id < 0 || t < best_t) {
+                    best = {i, splits};
+                    best_t = t;
+                }
+            }
         }
     }
-    return best < 0 ? 0 : best;
+    return best;
 }
 
 }  // namespace sgemm

@@ -15,11 +15,15 @@
 #include "sgemm.h"
 #include "sgemm_mfma.hpp"
 #include "sgemm_mfma_dl.hpp"
+#include "sgemm_reduce.hpp"
 #include "sgemm_valu.hpp"
 #include "select.hpp"
 
 namespace {
 
+using sgemm::Choice;
+using sgemm::GemmArgs;
+using sgemm::Problem;
 using sgemm::Variant;
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGE_AT>
@@ -28,20 +32,32 @@ Variant mfma_variant(int eff_permille)
     typedef sgemm::MfmaTraits<BM, BN, BK, WM, WN, STAGE_AT> T;
     return Variant{SGEMM_KERNEL_MFMA, BM, BN, BK, WM, WN, STAGE_AT, 0,
                    T::NT, (int)(T::LDS_FLOATS * sizeof(float)),
-                   reinterpret_cast<const void *>(
-                       &sgemm::sgemm_mfma_kernel<BM, BN, BK, WM, WN, STAGE_AT>),
+                   {reinterpret_cast<const void *>(
+                        &sgemm::sgemm_mfma_kernel<BM, BN, BK, WM, WN, STAGE_AT>),
+                    nullptr, nullptr, nullptr},
                    eff_permille};
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int STAGES>
+// OPS: bit (transa + 2*transb) set for each operand layout to compile.
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int OPS>
 Variant dl_variant(int eff_permille)
 {
-    typedef sgemm::DlTraits<BM, BN, BK, WM, WN, STAGES> T;
-    return Variant{SGEMM_KERNEL_MFMA, BM, BN, BK, WM, WN, -1, STAGES,
-                   T::NT, (int)(T::LDS_FLOATS * sizeof(float)),
-                   reinterpret_cast<const void *>(
-                       &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES>),
-                   eff_permille};
+    typedef sgemm::DlTraits<BM, BN, BK, WM, WN, STAGES, false, false> T;
+    Variant v{SGEMM_KERNEL_MFMA, BM, BN, BK, WM, WN, -1, STAGES,
+              T::NT, (int)(T::LDS_FLOATS * sizeof(float)),
+              {nullptr, nullptr, nullptr, nullptr}, eff_permille};
+    v.fn[0] = reinterpret_cast<const void *>(
+        &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, false, false>);
+    if constexpr ((OPS & 2) != 0)
+        v.fn[1] = reinterpret_cast<const void *>(
+            &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, true, false>);
+    if constexpr ((OPS & 4) != 0)
+        v.fn[2] = reinterpret_cast<const void *>(
+            &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, false, true>);
+    if constexpr ((OPS & 8) != 0)
+        v.fn[3] = reinterpret_cast<const void *>(
+            &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, true, true>);
+    return v;
 }
 
 Variant valu_variant()
@@ -49,8 +65,13 @@ Variant valu_variant()
     typedef sgemm::ValuTraits T;
     return Variant{SGEMM_KERNEL_VALU, T::BM, T::BN, T::BK, 1, 1, -1, 0,
                    T::NT, (int)(T::LDS_FLOATS * sizeof(float)),
-                   reinterpret_cast<const void *>(&sgemm::sgemm_valu_kernel), 0};
+                   {reinterpret_cast<const void *>(&sgemm::sgemm_valu_kernel),
+                    nullptr, nullptr, nullptr},
+                   0};
 }
+
+constexpr int kAllOps = 0xf;
+constexpr int kNnNt = 0x5;  // no transposed A: its 96-row wave tiles need 3-wide fragment reads
 
 // The compiled variants.  Indices are part of the ABI of sgemm_f32_ex.  The
 // last argument is the fraction of the FP32 matrix peak (x1000) the variant
@@ -59,21 +80,21 @@ Variant valu_variant()
 // (exactly one 192 x 192 tile per CU) for the 192 x 192 tiles.  0 keeps a
 // variant out of automatic selection (comparison kernels, dominated tiles).
 const Variant kVariants[] = {
-    mfma_variant<256, 256, 16, 4, 2, 0>(894),   // 0: 8 waves of 64x128
-    mfma_variant<128, 128, 16, 2, 2, 0>(861),   // 1: 4 waves of 64x64
-    mfma_variant<128, 128, 32, 2, 2, 1>(0),     // 2: 4 waves of 64x64, BK 32
-    mfma_variant<128, 256, 16, 2, 2, 0>(0),     // 3: 4 waves of 64x128
-    mfma_variant<256, 128, 16, 4, 1, 0>(0),     // 4: 4 waves of 64x128
-    mfma_variant<256, 256, 16, 4, 2, -1>(0),    // 5: plain order (comparison)
-    mfma_variant<128, 128, 16, 2, 2, -1>(0),    // 6: plain order (comparison)
-    valu_variant(),                             // 7: vector-FMA comparison
-    mfma_variant<192, 192, 16, 2, 6, 0>(0),     // 8: 12 waves of 96x32
-    mfma_variant<192, 192, 32, 2, 6, 1>(869),   // 9: 12 waves of 96x32, BK 32
-    dl_variant<256, 256, 16, 4, 2, 4>(0),       // 10: direct loads, 4 stages
-    dl_variant<256, 256, 32, 4, 2, 2>(912),     // 11: direct loads, 2 stages of BK 32
-    dl_variant<128, 128, 32, 2, 2, 3>(775),     // 12: direct loads
-    dl_variant<192, 192, 32, 2, 6, 3>(854),     // 13: direct loads
-    dl_variant<256, 256, 16, 4, 2, 3>(0),       // 14: direct loads, 3 stages
+    mfma_variant<256, 256, 16, 4, 2, 0>(894),       // 0: 8 waves of 64x128
+    mfma_variant<128, 128, 16, 2, 2, 0>(861),       // 1: 4 waves of 64x64
+    mfma_variant<128, 128, 32, 2, 2, 1>(0),         // 2: 4 waves of 64x64, BK 32
+    mfma_variant<128, 256, 16, 2, 2, 0>(0),         // 3: 4 waves of 64x128
+    mfma_variant<256, 128, 16, 4, 1, 0>(0),         // 4: 4 waves of 64x128
+    mfma_variant<256, 256, 16, 4, 2, -1>(0),        // 5: plain order (comparison)
+    mfma_variant<128, 128, 16, 2, 2, -1>(0),        // 6: plain order (comparison)
+    valu_variant(),                                 // 7: vector-FMA comparison
+    mfma_variant<192, 192, 16, 2, 6, 0>(0),         // 8: 12 waves of 96x32
+    mfma_variant<192, 192, 32, 2, 6, 1>(869),       // 9: 12 waves of 96x32, BK 32
+    dl_variant<256, 256, 16, 4, 2, 4, 1>(0),        // 10: direct loads, 4 stages
+    dl_variant<256, 256, 32, 4, 2, 2, kAllOps>(912),  // 11: direct loads, 2 stages of BK 32
+    dl_variant<128, 128, 32, 2, 2, 3, kAllOps>(775),  // 12: direct loads
+    dl_variant<192, 192, 32, 2, 6, 3, kNnNt>(854),  // 13: direct loads
+    dl_variant<256, 256, 16, 4, 2, 3, 1>(0),        // 14: direct loads, 3 stages
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -100,56 +121,238 @@ hipError_t device_cus(int *cus)
 }
 
 // ---- validation ---------------------------------------------------------------
-bool misaligned4(const void *p) { return ((uintptr_t)p & 3u) != 0; }
+bool misaligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) != 0; }
 
-// Address range [lo, hi) spanned by a rows x cols row-major matrix with stride ld.
-void span(const void *p, int rows, int cols, int ld, uintptr_t &lo, uintptr_t &hi)
+// Address range [lo, hi) spanned by `count` row-major rows x cols matrices
+// with row stride ld, `stride` elements apart.
+struct Span {
+    uintptr_t lo, hi;
+};
+
+Span span(const void *p, int rows, int cols, int ld, long long stride, int count)
 {
-    lo = (uintptr_t)p;
-    hi = lo + ((uint64_t)(rows - 1) * (uint64_t)ld + (uint64_t)cols) * sizeof(float);
+    const uint64_t one = (uint64_t)(rows - 1) * (uint64_t)ld + (uint64_t)cols;
+    Span s;
+    s.lo = (uintptr_t)p;
+    s.hi = s.lo + ((uint64_t)(count - 1) * (uint64_t)stride + one) * sizeof(float);
+    return s;
 }
 
-bool overlaps(const void *a, int ar, int ac, int lda, const void *c, int cr, int cc, int ldc)
-{
-    if (ar == 0 || ac == 0 || cr == 0 || cc == 0) return false;
-    uintptr_t alo, ahi, clo, chi;
-    span(a, ar, ac, lda, alo, ahi);
-    span(c, cr, cc, ldc, clo, chi);
-    return clo < ahi && alo < chi;
-}
+bool overlap(const Span &a, const Span &b) { return a.lo < b.hi && b.lo < a.hi; }
 
-hipError_t validate(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
-                    const float *C, int ldc)
+// A call after the sizes are known valid: the pointers, strides and workspace.
+struct Call {
+    Problem p;
+    float alpha, beta;
+    const float *A;
+    const float *B;
+    float *C;
+    long long sa, sb, sc;
+    void *ws;
+    size_t ws_bytes;
+};
+
+// Whether A and B are read at all.
+bool reads_operands(const Call &c) { return c.p.K > 0 && c.alpha != 0.0f; }
+
+hipError_t validate(const Call &c)
 {
-    if (M < 0 || N < 0 || K < 0) return hipErrorInvalidValue;
-    if (!sgemm::leading_dims_ok(M, N, K, lda, ldb, ldc)) return hipErrorInvalidValue;
-    if (M == 0 || N == 0) return hipSuccess;
-    if (K > 0 && (!A || !B || misaligned4(A) || misaligned4(B))) return hipErrorInvalidValue;
-    if (!C || misaligned4(C)) return hipErrorInvalidValue;
-    if (K > 0 && (overlaps(A, M, K, lda, C, M, N, ldc) || overlaps(B, K, N, ldb, C, M, N, ldc)))
-        return hipErrorInvalidValue;
+    const Problem &p = c.p;
+    if (!sgemm::sizes_ok(p)) return hipErrorInvalidValue;
+    if (c.sa < 0 || c.sb < 0 || c.sc < 0) return hipErrorInvalidValue;
+    if (p.M == 0 || p.N == 0 || p.batch == 0) return hipSuccess;
+    if (!c.C || misaligned(c.C, 4)) return hipErrorInvalidValue;
+    if (p.batch > 1 && c.sc < (long long)(p.M - 1) * p.ldc + p.N) return hipErrorInvalidValue;
+    const Span cs = span(c.C, p.M, p.N, p.ldc, c.sc, p.batch);
+    if (c.ws_bytes > 0) {
+        if (!c.ws || misaligned(c.ws, 16)) return hipErrorInvalidValue;
+        const Span w{(uintptr_t)c.ws, (uintptr_t)c.ws + c.ws_bytes};
+        if (overlap(w, cs)) return hipErrorInvalidValue;
+    }
+    if (p.K == 0) return hipSuccess;
+    if (!c.A || !c.B || misaligned(c.A, 4) || misaligned(c.B, 4)) return hipErrorInvalidValue;
+    const Span as = p.transa ? span(c.A, p.K, p.M, p.lda, c.sa, p.batch)
+                             : span(c.A, p.M, p.K, p.lda, c.sa, p.batch);
+    const Span bs = p.transb ? span(c.B, p.N, p.K, p.ldb, c.sb, p.batch)
+                             : span(c.B, p.K, p.N, p.ldb, c.sb, p.batch);
+    if (overlap(as, cs) || overlap(bs, cs)) return hipErrorInvalidValue;
+    if (c.ws_bytes > 0) {
+        const Span w{(uintptr_t)c.ws, (uintptr_t)c.ws + c.ws_bytes};
+        if (overlap(w, as) || overlap(w, bs)) return hipErrorInvalidValue;
+    }
     return hipSuccess;
 }
 
-// Direct global -> LDS loads need 16-byte aligned rows, and byte offsets inside
-// a slice below 2^31 (the offset given to chunks that must read as zero).
-bool direct_loads_ok(const float *A, int lda, const float *B, int ldb)
+// Direct global -> LDS loads need every batch entry's rows to start 16-byte
+// aligned (a null pointer stands for an aligned start: used by plan).
+bool direct_loads_ok(const Call &c)
 {
-    const bool al = (((uintptr_t)A | (uintptr_t)B) & 15u) == 0 && lda % 4 == 0 && ldb % 4 == 0;
-    // (a null pointer stands for an aligned start: used by sgemm_f32_plan)
-    return al && lda <= (1 << 20) && ldb <= (1 << 24);
+    const uintptr_t a = (uintptr_t)c.A, b = (uintptr_t)c.B;
+    const bool al = ((a | b) & 15u) == 0 && c.p.lda % 4 == 0 && c.p.ldb % 4 == 0 &&
+                    (c.p.batch <= 1 || (c.sa % 4 == 0 && c.sb % 4 == 0));
+    return al && sgemm::direct_lds_ok(c.p);
 }
 
-hipError_t launch(const Variant &v, const sgemm_cfg &cfg, int M, int N, int K,
-                  const float *A, int lda, const float *B, int ldb, float *C, int ldc,
-                  hipStream_t stream)
+// Workgroups per launch: the dispatch packet counts work-items in 32 bits.
+long long max_wgs_per_launch(int threads) { return (long long)(UINT32_MAX / (uint32_t)threads) & ~7ll; }
+
+hipError_t launch_gemm(const Variant &v, const sgemm_cfg &cfg, const Call &c, hipStream_t stream)
 {
-    int tiles_m = cfg.tiles_m, tiles_n = cfg.tiles_n;
-    int group_m = cfg.group_m, xcd = cfg.xcd_remap;
-    int direct = direct_loads_ok(A, lda, B, ldb) ? 1 : 0;
-    void *args[] = {&M, &N, &K, (void *)&A, &lda, (void *)&B, &ldb, &C, &ldc,
-                    &tiles_m, &tiles_n, &group_m, &xcd, &direct};
-    return hipLaunchKernel(v.fn, dim3((unsigned)cfg.grid), dim3((unsigned)v.threads), args, 0, stream);
+    const Problem &p = c.p;
+    const void *fn = v.fn[sgemm::op_index(p)];
+    GemmArgs g;
+    g.A = c.A;
+    g.B = c.B;
+    g.batch_a = c.sa;
+    g.batch_b = c.sb;
+    g.M = p.M;
+    g.N = p.N;
+    g.K = p.K;
+    g.lda = p.lda;
+    g.ldb = p.ldb;
+    g.k_chunk = cfg.k_chunk;
+    g.splits = cfg.splits;
+    g.tiles_m = cfg.tiles_m;
+    g.tiles_n = cfg.tiles_n;
+    g.group_m = cfg.group_m;
+    g.xcd_remap = cfg.xcd_remap;
+    g.direct = direct_loads_ok(c) ? 1 : 0;
+    const long long ldp = sgemm::partial_ld(p.N);
+    if (cfg.splits > 1) {
+        // partials: [batch][split][M][ldp] in the workspace
+        g.C = static_cast<float *>(c.ws);
+        g.ldc = (int)ldp;
+        g.split_c = (long long)p.M * ldp;
+        g.batch_c = g.split_c * cfg.splits;
+        g.alpha = 1.0f;
+        g.beta = 0.0f;
+    } else {
+        g.C = c.C;
+        g.ldc = p.ldc;
+        g.split_c = 0;
+        g.batch_c = c.sc;
+        g.alpha = c.alpha;
+        g.beta = c.beta;
+    }
+    const long long per = max_wgs_per_launch(v.threads);
+    for (long long base = 0; base < cfg.grid; base += per) {
+        const long long n = cfg.grid - base < per ? cfg.grid - base : per;
+        g.wg_base = (int)base;
+        void *args[] = {&g};
+        hipError_t e = hipLaunchKernel(fn, dim3((unsigned)n), dim3((unsigned)v.threads), args, 0, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+// C = alpha * (sum of `splits` partials) + beta * C; splits == 0: C = beta * C.
+hipError_t launch_reduce(const Call &c, int splits, float alpha, hipStream_t stream)
+{
+    const Problem &p = c.p;
+    sgemm::ReduceArgs r;
+    r.ldp = (int)sgemm::partial_ld(p.N);
+    r.P = static_cast<const float *>(c.ws);
+    r.split_p = (long long)p.M * r.ldp;
+    r.batch_p = r.split_p * splits;
+    r.quads = r.split_p / 4;
+    r.M = p.M;
+    r.N = p.N;
+    r.ldc = p.ldc;
+    r.splits = splits;
+    r.alpha = alpha;
+    r.beta = c.beta;
+    const long long blocks = (r.quads + 255) / 256;
+    if (blocks > INT_MAX) return hipErrorInvalidValue;
+    constexpr int kMaxY = 65535;
+    for (int z0 = 0; z0 < p.batch; z0 += kMaxY) {
+        const int nz = p.batch - z0 < kMaxY ? p.batch - z0 : kMaxY;
+        sgemm::ReduceArgs rz = r;
+        rz.P = r.P ? r.P + (long long)z0 * r.batch_p : nullptr;
+        rz.C = c.C + (long long)z0 * c.sc;
+        rz.batch_c = c.sc;
+        void *args[] = {&rz};
+        hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&sgemm::splitk_reduce_kernel),
+                                       dim3((unsigned)blocks, (unsigned)nz), dim3(256), args, 0, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+int plan_for(const Call &c, int cus, sgemm_cfg *out)
+{
+    if (!out || !sgemm::sizes_ok(c.p)) return hipErrorInvalidValue;
+    const long long ws = c.ws_bytes > (size_t)LLONG_MAX ? LLONG_MAX : (long long)c.ws_bytes;
+    const Choice ch = sgemm::select_plan(kVariants, kNumVariants, c.p, cus > 0 ? cus : 256,
+                                         direct_loads_ok(c), ws);
+    if (ch.id < 0) return hipErrorInvalidValue;
+    return sgemm::finish_cfg(kVariants[ch.id], ch.id, c.p, ch.splits, out) ? hipSuccess
+                                                                           : hipErrorInvalidValue;
+}
+
+// A forced configuration completed for this call (see sgemm_f32_cfg_geometry).
+int forced_cfg(const Problem &p, const sgemm_cfg *force, sgemm_cfg *cfg)
+{
+    if (!sgemm::sizes_ok(p)) return hipErrorInvalidValue;
+    if (force->id < 0 || force->id >= kNumVariants || force->group_m < 0) return hipErrorInvalidValue;
+    const int id = force->id;
+    if (!kVariants[id].fn[sgemm::op_index(p)]) return hipErrorInvalidValue;
+    const int group_m = force->group_m, xcd = force->xcd_remap ? 1 : 0;
+    if (!sgemm::finish_cfg(kVariants[id], id, p, force->splits, cfg)) return hipErrorInvalidValue;
+    cfg->group_m = group_m;
+    cfg->xcd_remap = xcd;
+    return hipSuccess;
+}
+
+int run(const Call &c, hipStream_t stream, const sgemm_cfg *force)
+{
+    hipError_t e = validate(c);
+    if (e != hipSuccess) return e;
+    const Problem &p = c.p;
+    sgemm_cfg cfg;
+    if (force) {
+        const int r = forced_cfg(p, force, &cfg);
+        if (r != hipSuccess) return r;
+    }
+    if (p.M == 0 || p.N == 0 || p.batch == 0) return hipSuccess;
+    if (!reads_operands(c)) {
+        // alpha * (empty or ignored product) + beta * C
+        if (c.beta == 1.0f) return hipSuccess;
+        return launch_reduce(c, 0, 0.0f, stream);
+    }
+    int id;
+    if (force) {
+        id = cfg.id;
+        if ((unsigned long long)cfg.workspace_bytes > c.ws_bytes) return hipErrorInvalidValue;
+    } else {
+        int cus = 0;
+        e = device_cus(&cus);
+        if (e != hipSuccess) return e;
+        const int r = plan_for(c, cus, &cfg);
+        if (r != hipSuccess) return r;
+        id = cfg.id;
+    }
+    e = launch_gemm(kVariants[id], cfg, c, stream);
+    if (e != hipSuccess || cfg.splits <= 1) return e;
+    return launch_reduce(c, cfg.splits, c.alpha, stream);
+}
+
+Call make_call(int transa, int transb, int M, int N, int K, float alpha,
+               const float *A, int lda, long long sa, const float *B, int ldb, long long sb,
+               float beta, float *C, int ldc, long long sc, int batch, void *ws, size_t ws_bytes)
+{
+    Call c;
+    c.p = Problem{transa, transb, M, N, K, lda, ldb, ldc, batch};
+    c.alpha = alpha;
+    c.beta = beta;
+    c.A = A;
+    c.B = B;
+    c.C = C;
+    c.sa = sa;
+    c.sb = sb;
+    c.sc = sc;
+    c.ws = ws;
+    c.ws_bytes = ws ? ws_bytes : 0;
+    return c;
 }
 
 }  // namespace
@@ -165,66 +368,108 @@ int sgemm_f32_variant(int id, sgemm_cfg *out)
     return hipSuccess;
 }
 
-const char *sgemm_f32_version(void) { return "libsgemm 0.2.0 gfx950 fp32 (mfma_f32_32x32x2 + valu comparison)"; }
-
-namespace {
-int plan_for(int M, int N, int K, int lda, int ldb, int ldc, int num_cus, bool direct, sgemm_cfg *out)
+int sgemm_f32_variant_ops(int id)
 {
-    if (!out || M < 0 || N < 0 || K < 0) return hipErrorInvalidValue;
-    if (!sgemm::leading_dims_ok(M, N, K, lda, ldb, ldc)) return hipErrorInvalidValue;
-    const int id = sgemm::select_variant(kVariants, kNumVariants, M, N, K,
-                                         num_cus > 0 ? num_cus : 256, direct);
-    return sgemm::finish_cfg(kVariants[id], id, M, N, out) ? hipSuccess : hipErrorInvalidValue;
+    if (id < 0 || id >= kNumVariants) return -1;
+    int m = 0;
+    for (int o = 0; o < 4; ++o)
+        if (kVariants[id].fn[o]) m |= 1 << o;
+    return m;
 }
-}  // namespace
 
-int sgemm_f32_plan(int M, int N, int K, int lda, int ldb, int ldc, int num_cus, sgemm_cfg *out)
+const char *sgemm_f32_version(void)
+{
+    return "libsgemm 0.3.0 gfx950 fp32 (mfma_f32_32x32x2; NN/NT/TN/TT, alpha/beta, split-K, strided batch; "
+           "valu comparison)";
+}
+
+int sgemm_f32_plan(int transa, int transb, int M, int N, int K, int lda, int ldb, int ldc, int batch,
+                   int num_cus, long long workspace_bytes, sgemm_cfg *out)
 {
     // operands are assumed to start 16-byte aligned (as allocations do)
-    return plan_for(M, N, K, lda, ldb, ldc, num_cus, direct_loads_ok(nullptr, lda, nullptr, ldb), out);
+    Call c = make_call(transa, transb, M, N, K, 1.0f, nullptr, lda, 0, nullptr, ldb, 0, 0.0f,
+                       nullptr, ldc, 0, batch, nullptr, 0);
+    c.ws_bytes = workspace_bytes > 0 ? (size_t)workspace_bytes : 0;
+    return plan_for(c, num_cus, out);
 }
 
-int sgemm_f32_query(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
-                    float *C, int ldc, sgemm_cfg *out)
+int sgemm_f32_cfg_geometry(int transa, int transb, int M, int N, int K, int lda, int ldb, int ldc,
+                           int batch, sgemm_cfg *cfg)
+{
+    if (!cfg) return hipErrorInvalidValue;
+    const Problem p{transa, transb, M, N, K, lda, ldb, ldc, batch};
+    sgemm_cfg out;
+    const int r = forced_cfg(p, cfg, &out);
+    if (r == hipSuccess) *cfg = out;
+    return r;
+}
+
+int sgemm_f32_workspace_size(int transa, int transb, int M, int N, int K, int lda, int ldb, int ldc,
+                             int batch, size_t *bytes)
+{
+    if (!bytes) return hipErrorInvalidValue;
+    int cus = 0;
+    hipError_t e = device_cus(&cus);
+    if (e != hipSuccess) return e;
+    sgemm_cfg cfg;
+    const int r = sgemm_f32_plan(transa, transb, M, N, K, lda, ldb, ldc, batch, cus, LLONG_MAX, &cfg);
+    if (r != hipSuccess) return r;
+    *bytes = (size_t)cfg.workspace_bytes;
+    return hipSuccess;
+}
+
+int sgemm_f32_query(int transa, int transb, int M, int N, int K,
+                    const float *A, int lda, long long stride_a,
+                    const float *B, int ldb, long long stride_b,
+                    float *C, int ldc, long long stride_c,
+                    int batch, void *workspace, size_t workspace_bytes, sgemm_cfg *out)
 {
     if (!out) return hipErrorInvalidValue;
-    hipError_t e = validate(M, N, K, A, lda, B, ldb, C, ldc);
+    const Call c = make_call(transa, transb, M, N, K, 1.0f, A, lda, stride_a, B, ldb, stride_b, 0.0f,
+                             C, ldc, stride_c, batch, workspace, workspace_bytes);
+    hipError_t e = validate(c);
     if (e != hipSuccess) return e;
     int cus = 0;
     e = device_cus(&cus);
     if (e != hipSuccess) return e;
-    return plan_for(M, N, K, lda, ldb, ldc, cus, direct_loads_ok(A, lda, B, ldb), out);
+    return plan_for(c, cus, out);
 }
 
-int sgemm_f32_ex(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
-                 float *C, int ldc, hipStream_t stream, const sgemm_cfg *force)
+int sgemm_f32_ex(int transa, int transb, int M, int N, int K, float alpha,
+                 const float *A, int lda, long long stride_a,
+                 const float *B, int ldb, long long stride_b,
+                 float beta, float *C, int ldc, long long stride_c, int batch,
+                 void *workspace, size_t workspace_bytes, hipStream_t stream, const sgemm_cfg *cfg)
 {
-    hipError_t e = validate(M, N, K, A, lda, B, ldb, C, ldc);
-    if (e != hipSuccess) return e;
-    if (M == 0 || N == 0) return hipSuccess;
-    sgemm_cfg cfg;
-    int id;
-    if (force) {
-        id = force->id;
-        if (id < 0 || id >= kNumVariants || force->group_m < 0) return hipErrorInvalidValue;
-        if (!sgemm::finish_cfg(kVariants[id], id, M, N, &cfg)) return hipErrorInvalidValue;
-        cfg.group_m = force->group_m;
-        cfg.xcd_remap = force->xcd_remap ? 1 : 0;
-    } else {
-        int cus = 0;
-        e = device_cus(&cus);
-        if (e != hipSuccess) return e;
-        id = sgemm::select_variant(kVariants, kNumVariants, M, N, K, cus,
-                                   direct_loads_ok(A, lda, B, ldb));
-        if (!sgemm::finish_cfg(kVariants[id], id, M, N, &cfg)) return hipErrorInvalidValue;
-    }
-    return launch(kVariants[id], cfg, M, N, K, A, lda, B, ldb, C, ldc, stream);
+    const Call c = make_call(transa, transb, M, N, K, alpha, A, lda, stride_a, B, ldb, stride_b, beta,
+                             C, ldc, stride_c, batch, workspace, workspace_bytes);
+    return run(c, stream, cfg);
+}
+
+int sgemm_f32_strided_batched(int transa, int transb, int M, int N, int K, float alpha,
+                              const float *A, int lda, long long stride_a,
+                              const float *B, int ldb, long long stride_b,
+                              float beta, float *C, int ldc, long long stride_c, int batch,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return sgemm_f32_ex(transa, transb, M, N, K, alpha, A, lda, stride_a, B, ldb, stride_b, beta,
+                        C, ldc, stride_c, batch, workspace, workspace_bytes, stream, nullptr);
+}
+
+int sgemm_f32_gemm(int transa, int transb, int M, int N, int K, float alpha,
+                   const float *A, int lda, const float *B, int ldb,
+                   float beta, float *C, int ldc,
+                   void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return sgemm_f32_ex(transa, transb, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1,
+                        workspace, workspace_bytes, stream, nullptr);
 }
 
 int sgemm_f32(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
               float *C, int ldc, hipStream_t stream)
 {
-    return sgemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, stream, nullptr);
+    return sgemm_f32_ex(SGEMM_OP_N, SGEMM_OP_N, M, N, K, 1.0f, A, lda, 0, B, ldb, 0, 0.0f, C, ldc, 0, 1,
+                        nullptr, 0, stream, nullptr);
 }
 
 }  // extern "C"

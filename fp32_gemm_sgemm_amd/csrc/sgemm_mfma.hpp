@@ -76,11 +76,7 @@ struct MfmaTraits {
 
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGE_AT>
 __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64)
-sgemm_mfma_kernel(int M, int N, int K,
-                  const float *__restrict__ A, int lda,
-                  const float *__restrict__ B, int ldb,
-                  float *__restrict__ C, int ldc,
-                  int tiles_m, int tiles_n, int group_m, int xcd_remap, int /*direct*/)
+sgemm_mfma_kernel(GemmArgs g)
 {
     typedef MfmaTraits<BM, BN, BK, WAVES_M, WAVES_N, STAGE_AT> T;
     constexpr int NT = T::NT, WTM = T::WTM, WTN = T::WTN, RM = T::RM, NB = T::NB;
@@ -99,9 +95,12 @@ sgemm_mfma_kernel(int M, int N, int K,
     // shared with the LDS fragments, staging registers and addresses.
     asm volatile("" ::: "a0");
 
-    int tm, tn;
-    map_tile(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, xcd_remap, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
+    const Work w = map_work(g);
+    locate<false, false>(g, w);
+    const float *__restrict__ A = g.A;
+    const float *__restrict__ B = g.B;
+    const int M = g.M, N = g.N, K = g.K, lda = g.lda, ldb = g.ldb;
+    const int m0 = w.tm * BM, n0 = w.tn * BN;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -286,7 +285,9 @@ sgemm_mfma_kernel(int M, int N, int K,
 
     // ---- epilogue -----------------------------------------------------------------
     // Lane l holds rows 8*(r/4) + 4*(l/32) + r%4 of each 32-row block and NB
-    // adjacent columns c0 + NB*(l%32) .. +NB-1; C is written, never read.
+    // adjacent columns c0 + NB*(l%32) .. +NB-1.
+    float *__restrict__ C = g.C;
+    const int ldc = g.ldc;
     const int col = n0 + wn * WTN + NB * (lane & 31);
 #pragma unroll
     for (int i = 0; i < RM; ++i) {
@@ -294,19 +295,10 @@ sgemm_mfma_kernel(int M, int N, int K,
         for (int r = 0; r < 16; ++r) {
             const int row = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
             if (row >= M) continue;
-            float *p = C + (int64_t)row * ldc + col;
-            if (NB == 4 && col + 3 < N) {
-                f32x4 v = {acc[i][0][r], acc[i][NB > 1 ? 1 : 0][r],
-                           acc[i][NB > 2 ? 2 : 0][r], acc[i][NB > 3 ? 3 : 0][r]};
-                *reinterpret_cast<f32x4u *>(p) = v;
-            } else if (NB == 2 && col + 1 < N) {
-                f32x2 v = {acc[i][0][r], acc[i][NB > 1 ? 1 : 0][r]};
-                *reinterpret_cast<f32x2u *>(p) = v;
-            } else {
+            float v[NB];
 #pragma unroll
-                for (int j = 0; j < NB; ++j)
-                    if (col + j < N) p[j] = acc[i][j][r];
-            }
+            for (int j = 0; j < NB; ++j) v[j] = acc[i][j][r];
+            store_row<NB>(C + (int64_t)row * ldc + col, col, N, v, g.alpha, g.beta);
         }
     }
 }

@@ -45,19 +45,67 @@ template <int BK> __device__ __forceinline__ int chunk_swizzle(int r)
     else return (r ^ ((r >> 3) & 1)) & 7;
 }
 
-template <int NB> struct DlFragB;
-template <> struct DlFragB<1> { typedef float T; };
-template <> struct DlFragB<2> { typedef f32x2 T; };
-template <> struct DlFragB<4> { typedef f32x4 T; };
+template <int W> struct DlVec;
+template <> struct DlVec<1> { typedef float T; };
+template <> struct DlVec<2> { typedef f32x2 T; };
+template <> struct DlVec<4> { typedef f32x4 T; };
 
-template <int NB>
-__device__ __forceinline__ float dl_frag_elem(const typename DlFragB<NB>::T &v, int cb)
+// Fragment vector of an index-contiguous operand (unused, and a plain float,
+// for a k-contiguous one).
+template <bool XC, int W> struct DlXVec { typedef float T; };
+template <int W> struct DlXVec<true, W> { typedef typename DlVec<W>::T T; };
+
+template <int W, typename V>
+__device__ __forceinline__ float dl_elem(const V &v, int b)
 {
-    if constexpr (NB == 1) return v;
-    else return v[cb];
+    if constexpr (W == 1) return v;
+    else return v[b];
 }
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES>
+// One operand's tile in LDS.  X is the operand's own index (rows of C for A,
+// columns of C for B); a tile covers E of them, a wave WT, in W blocks of 32.
+// Block b of a wave holds the indices x = wave_offset + W*l + b, l = 0..31
+// (interleaved), so a lane's W results of one C row or column are adjacent.
+//
+//  KC ("k contiguous": A, or a transposed B): the operand's rows run along k.
+//     LDS holds E rows of BK floats; row L holds index P(L) = wave offset +
+//     W*(L%32) + (L%WT)/32, so the 32 rows a fragment read touches are
+//     consecutive; chunk p of row L is stored at chunk p ^ f(L).  A fragment
+//     read is one 16-byte read per block: 4 successive k of one index.
+//  XC ("index contiguous": B, or a transposed A): the operand's rows run
+//     along X.  LDS holds BK rows of E floats; a fragment read is one W-wide
+//     read per k: the W blocks' values at one k.
+template <int E, int BK, int WT, int NW, bool KC>
+struct DlOperand {
+    static constexpr int W = WT / 32;
+    static constexpr int CPR = KC ? BK / 4 : E / 4;    // 16-byte chunks per LDS row
+    static constexpr int LOADS = E * BK / 4 / (NW * 64);  // per thread per slice
+    static constexpr int FLOATS = E * BK;
+    static_assert(WT % 32 == 0 && W >= 1, "wave tiles must be multiples of 32");
+    static_assert(KC || W == 1 || W == 2 || W == 4, "index-contiguous fragments are 1, 2 or 4 wide");
+    static_assert(LOADS * NW * 64 * 4 == E * BK, "slices must split into whole 1 KB blocks per wave");
+
+    // Fetch assignment of load j: byte offset from the slice's base (the
+    // tile's first index at the slice's first k) and the chunk's first
+    // column along the contiguous dimension (k for KC, the index for XC).
+    __device__ __forceinline__ static void assign(int j, int wave, int lane, int ld,
+                                                  uint32_t &off, int &col)
+    {
+        const int q = (j * NW + wave) * 64 + lane;
+        const int row = q / CPR;
+        int c = q % CPR;
+        int r = row;
+        if constexpr (KC) {
+            c ^= chunk_swizzle<BK>(row);
+            const int in = row % WT;
+            r = row - in + W * (in % 32) + in / 32;
+        }
+        col = 4 * c;
+        off = 4u * ((uint32_t)r * (uint32_t)ld + 4u * (uint32_t)c);
+    }
+};
+
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, bool TA, bool TB>
 struct DlTraits {
     static constexpr int NW = WAVES_M * WAVES_N;
     static constexpr int NT = NW * 64;
@@ -65,17 +113,13 @@ struct DlTraits {
     static constexpr int WTN = BN / WAVES_N;
     static constexpr int RM = WTM / 32;
     static constexpr int NB = WTN / 32;
-    static constexpr int CPR = BK / 4;                 // 16-byte chunks per A row
-    static constexpr int A_LOADS = BM * BK / 4 / NT;   // per thread per slice
-    static constexpr int B_LOADS = BK * BN / 4 / NT;
+    typedef DlOperand<BM, BK, WTM, NW, !TA> OpA;
+    typedef DlOperand<BN, BK, WTN, NW, TB> OpB;
     static constexpr int A_FLOATS = BM * BK;
     static constexpr int STAGE_FLOATS = BM * BK + BK * BN;
     static constexpr int LDS_FLOATS = STAGES * STAGE_FLOATS;
     static_assert(BK == 16 || BK == 32, "swizzle defined for BK 16 and 32");
-    static_assert(WTM % 32 == 0 && RM >= 1, "wave tile rows must be a multiple of 32");
     static_assert(NB == 1 || NB == 2 || NB == 4, "wave tile columns must be 32, 64 or 128");
-    static_assert(A_LOADS * NT * 4 == BM * BK && B_LOADS * NT * 4 == BK * BN,
-                  "slices must split into whole 1 KB blocks per wave");
     static_assert(STAGES >= 2, "at least two LDS stages");
     static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS budget of one CU");
 };
@@ -84,21 +128,17 @@ struct DlTraits {
 // (resources are clamped below it when direct loads are used).
 constexpr uint32_t kOobOffset = 0x80000000u;
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES>
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, bool TA, bool TB>
 __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64)
-sgemm_mfma_dl_kernel(int M, int N, int K,
-                     const float *__restrict__ A, int lda,
-                     const float *__restrict__ B, int ldb,
-                     float *__restrict__ C, int ldc,
-                     int tiles_m, int tiles_n, int group_m, int xcd_remap, int direct)
+sgemm_mfma_dl_kernel(GemmArgs g)
 {
-    typedef DlTraits<BM, BN, BK, WAVES_M, WAVES_N, STAGES> T;
+    typedef DlTraits<BM, BN, BK, WAVES_M, WAVES_N, STAGES, TA, TB> T;
+    typedef typename T::OpA OpA;
+    typedef typename T::OpB OpB;
     constexpr int NW = T::NW, WTM = T::WTM, WTN = T::WTN, RM = T::RM, NB = T::NB;
-    constexpr int CPR = T::CPR, A_LOADS = T::A_LOADS, B_LOADS = T::B_LOADS;
+    constexpr int A_LOADS = OpA::LOADS, B_LOADS = OpB::LOADS;
     constexpr int STAGE_FLOATS = T::STAGE_FLOATS, A_FLOATS = T::A_FLOATS;
     constexpr int G = BK / 8;
-    constexpr int BCH = BN / 4;  // 16-byte chunks per B row
-    typedef typename DlFragB<NB>::T fragb_t;
 
     __shared__ __attribute__((aligned(1024))) float smem[T::LDS_FLOATS];
 
@@ -106,9 +146,12 @@ sgemm_mfma_dl_kernel(int M, int N, int K,
     // ArchVGPRs, and with the hint the allocator rotates them through copies
     // at the loop back-edge.)
 
-    int tm, tn;
-    map_tile(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, xcd_remap, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
+    const Work w = map_work(g);
+    locate<TA, TB>(g, w);
+    const float *__restrict__ A = g.A;
+    const float *__restrict__ B = g.B;
+    const int M = g.M, N = g.N, K = g.K, lda = g.lda, ldb = g.ldb;
+    const int m0 = w.tm * BM, n0 = w.tn * BN;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -123,50 +166,49 @@ sgemm_mfma_dl_kernel(int M, int N, int K,
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     // ---- fetch assignment ------------------------------------------------------
-    // Load j of this thread fills 16 bytes at LDS chunk q = (j*NW + wave)*64 +
-    // lane of the A (or B) region of a stage.
+    // Load j of this thread fills 16 bytes at LDS chunk (j*NW + wave)*64 + lane
+    // of the operand's region of a stage.
     uint32_t a_off[A_LOADS], b_off[B_LOADS];
-    int a_col[A_LOADS], b_colv[B_LOADS];
+    int a_col[A_LOADS], b_col[B_LOADS];
 #pragma unroll
-    for (int j = 0; j < A_LOADS; ++j) {
-        const int q = (j * NW + wave) * 64 + lane;
-        const int r = q / CPR, p = (q % CPR) ^ chunk_swizzle<BK>(r);
-        a_col[j] = 4 * p;
-        a_off[j] = 4u * ((uint32_t)r * (uint32_t)lda + 4u * (uint32_t)p);
-    }
+    for (int j = 0; j < A_LOADS; ++j) OpA::assign(j, wave, lane, lda, a_off[j], a_col[j]);
 #pragma unroll
-    for (int j = 0; j < B_LOADS; ++j) {
-        const int q = (j * NW + wave) * 64 + lane;
-        const int kr = q / BCH, c = q % BCH;
-        b_colv[j] = 4 * c;
-        b_off[j] = 4u * ((uint32_t)kr * (uint32_t)ldb + 4u * (uint32_t)c);
-    }
+    for (int j = 0; j < B_LOADS; ++j) OpB::assign(j, wave, lane, ldb, b_off[j], b_col[j]);
+
     // LDS destinations are cast to the LDS address space right at the load:
     // a helper lambda returning such a pointer cannot be compiled for the
     // host, which would silently drop this kernel's host-side stub.
     typedef __attribute__((address_space(3))) void lds_void;
 
-    // Fetch slice kt into stage s.
+    // Fetch slice kt into stage s.  Per operand: the slice's base (its first
+    // index at k0), the resource extent up to the operand's last element, and
+    // the limit of the contiguous column (k for KC, the index for XC) below
+    // which a chunk holds data.
     auto fetch = [&](int kt, int s) {
         const int k0 = kt * BK;
-        const float *abase = A + (int64_t)m0 * lda + k0;
-        const float *bbase = B + (int64_t)k0 * ldb + n0;
-        const int64_t abytes = 4 * ((int64_t)(M - 1 - m0) * lda + (K - k0));
-        const int64_t bbytes = 4 * ((int64_t)(K - 1 - k0) * ldb + (N - n0));
-        const bool partial = ((K & 3) && k0 + BK > K) || ((N & 3) && n0 + BN > N);
-        if (direct && !partial) {
+        const float *abase = TA ? A + (int64_t)k0 * lda + m0 : A + (int64_t)m0 * lda + k0;
+        const float *bbase = TB ? B + (int64_t)n0 * ldb + k0 : B + (int64_t)k0 * ldb + n0;
+        const int64_t abytes = TA ? 4 * ((int64_t)(K - 1 - k0) * lda + (M - m0))
+                                  : 4 * ((int64_t)(M - 1 - m0) * lda + (K - k0));
+        const int64_t bbytes = TB ? 4 * ((int64_t)(N - 1 - n0) * ldb + (K - k0))
+                                  : 4 * ((int64_t)(K - 1 - k0) * ldb + (N - n0));
+        const int a_lim = TA ? M - m0 : K - k0;
+        const int b_lim = TB ? K - k0 : N - n0;
+        const bool partial = ((a_lim & 3) && a_lim < (TA ? BM : BK)) ||
+                             ((b_lim & 3) && b_lim < (TB ? BK : BN));
+        if (g.direct && !partial) {
             const auto ar = make_rsrc(abase, abytes < (int64_t)kOobOffset ? abytes : (int64_t)kOobOffset);
             const auto br = make_rsrc(bbase, bbytes < (int64_t)kOobOffset ? bbytes : (int64_t)kOobOffset);
 #pragma unroll
             for (int j = 0; j < A_LOADS; ++j)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     ar, (lds_void *)(smem + s * STAGE_FLOATS + (j * NW + wave) * 256), 16,
-                    (int)(k0 + a_col[j] < K ? a_off[j] : kOobOffset), 0, 0, 0);
+                    (int)(a_col[j] < a_lim ? a_off[j] : kOobOffset), 0, 0, 0);
 #pragma unroll
             for (int j = 0; j < B_LOADS; ++j)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     br, (lds_void *)(smem + s * STAGE_FLOATS + A_FLOATS + (j * NW + wave) * 256), 16,
-                    (int)(n0 + b_colv[j] < N ? b_off[j] : kOobOffset), 0, 0, 0);
+                    (int)(b_col[j] < b_lim ? b_off[j] : kOobOffset), 0, 0, 0);
         } else {
             const auto ar = make_rsrc(abase, abytes);
             const auto br = make_rsrc(bbase, bbytes);
@@ -176,14 +218,14 @@ sgemm_mfma_dl_kernel(int M, int N, int K,
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float x = buffer_load_f32(ar, a_off[j] + 4u * e);
-                    va[j][e] = (k0 + a_col[j] + e < K) ? x : 0.0f;
+                    va[j][e] = (a_col[j] + e < a_lim) ? x : 0.0f;
                 }
 #pragma unroll
             for (int j = 0; j < B_LOADS; ++j)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float x = buffer_load_f32(br, b_off[j] + 4u * e);
-                    vb[j][e] = (n0 + b_colv[j] + e < N) ? x : 0.0f;
+                    vb[j][e] = (b_col[j] + e < b_lim) ? x : 0.0f;
                 }
 #pragma unroll
             for (int j = 0; j < A_LOADS; ++j)
@@ -195,26 +237,46 @@ sgemm_mfma_dl_kernel(int M, int N, int K,
     };
 
     // ---- fragments -----------------------------------------------------------------
-    // A: row R = wm*WTM + 32i + (lane & 31), logical chunk 2g + (lane >> 5),
-    // stored at chunk (2g + h) ^ f(R) = 2g ^ (h ^ f(R)) (2g is even), and
-    // f(R) = f(lane & 31) since 32i and wm*WTM only change row bits >= 5.
-    const int l31 = lane & 31;
-    const int u = (lane >> 5) ^ chunk_swizzle<BK>(l31);
-    const int a_row0 = (wm * WTM + l31) * BK;
-    const int b_base = (4 * (lane >> 5)) * BN + wn * WTN + NB * l31;
+    // MFMA step t (0..3) of k group g takes k = 8g + t from lanes 0-31 and
+    // k = 8g + 4 + t from lanes 32-63 (h = lane >> 5).
+    //  KC: block b's index for lane l is LDS row wave_offset + 32b + (l & 31),
+    //      whose k values 8g + 4h .. +3 are logical chunk 2g + h, stored at
+    //      (2g + h) ^ f(row) = 2g ^ (h ^ f(l & 31)) (2g is even, and f only
+    //      sees row bits 0-3).
+    //  XC: LDS row k, W floats at column wave_offset + W*(l & 31).
+    const int l31 = lane & 31, h = lane >> 5;
+    const int u = h ^ chunk_swizzle<BK>(l31);
+    typedef typename DlXVec<TA, RM>::T xa_t;
+    typedef typename DlXVec<!TB, NB>::T xb_t;
     struct Frag {
-        f32x4 a[RM];
-        fragb_t b[4];
+        f32x4 ka[OpA::W];  // KC A: [block][t]
+        xa_t xa[4];        // XC A: [t][block]
+        f32x4 kb[OpB::W];
+        xb_t xb[4];
     };
-    auto read_frag = [&](int s, int g, Frag &f) {
-        const float *as = smem + s * STAGE_FLOATS + a_row0 + 4 * ((2 * g) ^ u);
-        const float *bs = smem + s * STAGE_FLOATS + A_FLOATS + b_base + 8 * g * BN;
+    const int a_base = TA ? (4 * h) * BM + wm * WTM + RM * l31 : (wm * WTM + l31) * BK;
+    const int b_base = TB ? (wn * WTN + l31) * BK : (4 * h) * BN + wn * WTN + NB * l31;
+    auto read_frag = [&](int s, int gi, Frag &f) {
+        const float *as = smem + s * STAGE_FLOATS + a_base;
+        const float *bs = smem + s * STAGE_FLOATS + A_FLOATS + b_base;
+        if constexpr (TA) {
 #pragma unroll
-        for (int i = 0; i < RM; ++i)
-            f.a[i] = *reinterpret_cast<const f32x4 *>(as + i * 32 * BK);
+            for (int t = 0; t < 4; ++t)
+                f.xa[t] = *reinterpret_cast<const xa_t *>(as + (8 * gi + t) * BM);
+        } else {
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-            f.b[t] = *reinterpret_cast<const fragb_t *>(bs + t * BN);
+            for (int i = 0; i < RM; ++i)
+                f.ka[i] = *reinterpret_cast<const f32x4 *>(as + i * 32 * BK + 4 * ((2 * gi) ^ u));
+        }
+        if constexpr (TB) {
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                f.kb[j] = *reinterpret_cast<const f32x4 *>(bs + j * 32 * BK + 4 * ((2 * gi) ^ u));
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                f.xb[t] = *reinterpret_cast<const xb_t *>(bs + (8 * gi + t) * BN);
+        }
     };
     auto mfma_frag = [&](const Frag &f) {
 #pragma unroll
@@ -222,9 +284,14 @@ sgemm_mfma_dl_kernel(int M, int N, int K,
 #pragma unroll
             for (int i = 0; i < RM; ++i)
 #pragma unroll
-                for (int j = 0; j < NB; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                        f.a[i][t], dl_frag_elem<NB>(f.b[t], j), acc[i][j], 0, 0, 0);
+                for (int j = 0; j < NB; ++j) {
+                    float a, b;
+                    if constexpr (TA) a = dl_elem<RM>(f.xa[t], i);
+                    else a = f.ka[i][t];
+                    if constexpr (TB) b = f.kb[j][t];
+                    else b = dl_elem<NB>(f.xb[t], j);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc[i][j], 0, 0, 0);
+                }
     };
 
     // ---- main loop -------------------------------------------------------------------
@@ -263,35 +330,31 @@ sgemm_mfma_dl_kernel(int M, int N, int K,
         Frag f[2];
         read_frag(s, 0, f[0]);
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            if (g + 1 < G) read_frag(s, g + 1, f[(g + 1) & 1]);
+        for (int gi = 0; gi < G; ++gi) {
+            if (gi + 1 < G) read_frag(s, gi + 1, f[(gi + 1) & 1]);
             __builtin_amdgcn_sched_barrier(0);
-            mfma_frag(f[g & 1]);
+            mfma_frag(f[gi & 1]);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
 
-    // ---- epilogue (as sgemm_mfma.hpp) ------------------------------------------------
+    // ---- epilogue ----------------------------------------------------------------------
+    // Accumulator r of block (i, j) in lane l is D[8*(r/4) + 4*h + r%4][l & 31]
+    // of that block: C row wave_offset + RM*(8*(r/4) + 4*h + r%4) + i, column
+    // wave_offset + NB*(l & 31) + j, so a lane holds NB adjacent columns.
+    float *__restrict__ C = g.C;
+    const int ldc = g.ldc;
     const int col = n0 + wn * WTN + NB * l31;
 #pragma unroll
     for (int i = 0; i < RM; ++i) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int row = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            const int row = m0 + wm * WTM + RM * (8 * (r >> 2) + 4 * h + (r & 3)) + i;
             if (row >= M) continue;
-            float *p = C + (int64_t)row * ldc + col;
-            if (NB == 4 && col + 3 < N) {
-                f32x4 v = {acc[i][0][r], acc[i][NB > 1 ? 1 : 0][r],
-                           acc[i][NB > 2 ? 2 : 0][r], acc[i][NB > 3 ? 3 : 0][r]};
-                *reinterpret_cast<f32x4u *>(p) = v;
-            } else if (NB == 2 && col + 1 < N) {
-                f32x2 v = {acc[i][0][r], acc[i][NB > 1 ? 1 : 0][r]};
-                *reinterpret_cast<f32x2u *>(p) = v;
-            } else {
+            float v[NB];
 #pragma unroll
-                for (int j = 0; j < NB; ++j)
-                    if (col + j < N) p[j] = acc[i][j][r];
-            }
+            for (int j = 0; j < NB; ++j) v[j] = acc[i][j][r];
+            store_row<NB>(C + (int64_t)row * ldc + col, col, N, v, g.alpha, g.beta);
         }
     }
 }

@@ -21,11 +21,7 @@ struct ValuTraits {
 };
 
 __global__ void __launch_bounds__(256)
-sgemm_valu_kernel(int M, int N, int K,
-                  const float *__restrict__ A, int lda,
-                  const float *__restrict__ B, int ldb,
-                  float *__restrict__ C, int ldc,
-                  int tiles_m, int tiles_n, int group_m, int xcd_remap, int /*direct*/)
+sgemm_valu_kernel(GemmArgs g)
 {
     typedef ValuTraits T;
     constexpr int BM = T::BM, BN = T::BN, BK = T::BK;
@@ -35,9 +31,12 @@ sgemm_valu_kernel(int M, int N, int K,
     __shared__ __attribute__((aligned(16))) float As[2][BK * LDA_S];
     __shared__ __attribute__((aligned(16))) float Bs[2][BK * LDB_S];
 
-    int tm, tn;
-    map_tile(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, xcd_remap, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
+    const Work w = map_work(g);
+    locate<false, false>(g, w);
+    const float *__restrict__ A = g.A;
+    const float *__restrict__ B = g.B;
+    const int M = g.M, N = g.N, K = g.K, lda = g.lda, ldb = g.ldb;
+    const int m0 = w.tm * BM, n0 = w.tn * BN;
     const int tid = threadIdx.x;
     const int tx = tid & 15, ty = tid >> 4;
     const bool tile_inside = (m0 + BM <= M) && (n0 + BN <= N);
@@ -116,22 +115,17 @@ sgemm_valu_kernel(int M, int N, int K,
     }
 
     // rows 4*ty + {0..3} and 64 + 4*ty + {0..3}; columns likewise with tx
+    float *__restrict__ C = g.C;
+    const int ldc = g.ldc;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int row = m0 + (i < 4 ? 4 * ty + i : 64 + 4 * ty + (i - 4));
         if (row >= M) continue;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int col = n0 + 64 * h + 4 * tx;
-            float *p = C + (int64_t)row * ldc + col;
-            if (col + 3 < N) {
-                f4 v = {acc[i][4 * h], acc[i][4 * h + 1], acc[i][4 * h + 2], acc[i][4 * h + 3]};
-                *reinterpret_cast<f32x4u *>(p) = v;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (col + e < N) p[e] = acc[i][4 * h + e];
-            }
+        for (int hh = 0; hh < 2; ++hh) {
+            const int col = n0 + 64 * hh + 4 * tx;
+            const float v[4] = {acc[i][4 * hh], acc[i][4 * hh + 1], acc[i][4 * hh + 2], acc[i][4 * hh + 3]};
+            store_row<4>(C + (int64_t)row * ldc + col, col, N, v, g.alpha, g.beta);
         }
     }
 }

@@ -21,6 +21,8 @@
 #ifndef SGEMM_H
 #define SGEMM_H
 
+#include <stddef.h>
+
 #include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
@@ -31,6 +33,10 @@ extern "C" {
 #define SGEMM_KERNEL_MFMA 0 /* matrix cores: v_mfma_f32_32x32x2_f32 */
 #define SGEMM_KERNEL_VALU 1 /* vector FMA, kept only as a measured comparison */
 
+/* Operand layouts (transa, transb). */
+#define SGEMM_OP_N 0 /* the operand as stored, row-major */
+#define SGEMM_OP_T 1 /* its transpose */
+
 /* A launch configuration: what a variant is and how it is launched. */
 typedef struct sgemm_cfg {
     int id;        /* variant index, 0 .. sgemm_f32_num_variants()-1 */
@@ -40,11 +46,14 @@ typedef struct sgemm_cfg {
     int group_m;   /* raster: tile rows per group, walked column by column
                       (0 = plain row-major order over tiles) */
     int xcd_remap; /* 1: give each XCD a contiguous run of logical tiles */
+    int splits;    /* K split across workgroups (1 = none) */
     /* filled in by plan/query: */
-    int grid;      /* workgroups launched */
+    int k_chunk;   /* K range of one split */
+    int grid;      /* workgroups launched: tiles_m * tiles_n * splits * batch */
     int threads;   /* threads per workgroup */
     int lds_bytes; /* LDS per workgroup */
     int tiles_m, tiles_n;
+    long long workspace_bytes; /* workspace the configuration needs */
 } sgemm_cfg;
 
 /*
@@ -58,23 +67,25 @@ typedef struct sgemm_cfg {
  *             C is overwritten and never read; elements j >= N of each row
  *             (the padding up to ldc) are left untouched.
  *   stream    a HIP stream of the current device.
- * Pointers must be 4-byte aligned; any dword-aligned start and stride runs on
- * the same kernels (16-byte loads and stores need only dword alignment on
- * gfx950).  Limits: M, N, K <= INT_MAX - 1024, lda <= 2^22 - 64,
- * ldb <= 2^25 - 512 (byte offsets inside one K slice are 32-bit).
+ * Pointers must be 4-byte aligned; any dword-aligned start and stride runs
+ * (16-byte loads and stores need only dword alignment on gfx950; rows that
+ * start 16-byte aligned also allow direct global-to-LDS loads).  Limits:
+ * M, N, K <= INT_MAX - 1024, lda <= 2^22 - 64, ldb <= 2^25 - 512 (byte
+ * offsets inside one K slice are 32-bit).
  *
  * Semantics of degenerate sizes: M == 0 or N == 0 does nothing; K == 0 sets
  * the M x N block of C to zero (an empty sum).
  *
  * Ownership: A, B and C belong to the caller and must stay valid until the
  * work on `stream` completes.  The library allocates no device memory, keeps
- * no pointer after returning and never synchronises; it is re-entrant.
+ * no pointer after returning and never synchronises; it is re-entrant.  This
+ * entry point has no workspace, so it never splits K.
  *
  * Errors (returned before anything is launched):
  *   hipErrorInvalidValue  negative size; a leading dimension below its
- *                         minimum; a null or misaligned pointer for an operand
- *                         with a non-zero extent; C overlapping A or B; a grid
- *                         too large to launch.
+ *                         minimum or above its limit; a null or misaligned
+ *                         pointer for an operand with a non-zero extent; C
+ *                         overlapping A or B; a grid too large to launch.
  *   otherwise             the error of the device query or of the launch.
  * Faults during execution surface at the caller's next synchronisation.
  */
@@ -85,42 +96,153 @@ int sgemm_f32(int M, int N, int K,
               hipStream_t stream);
 
 /*
- * sgemm_f32_ex: sgemm_f32 with a forced configuration, for sweeps and for the
- * measured comparison kernels.  cfg == NULL behaves as sgemm_f32.  Otherwise
- * cfg->id selects the variant (see sgemm_f32_variant; an id out of range, or
- * cfg->group_m < 0, returns hipErrorInvalidValue) and cfg->group_m and
- * cfg->xcd_remap set the tile order; the other fields are ignored.  Same
- * arguments, ownership and errors as sgemm_f32.
+ * sgemm_f32_gemm: the BLAS-style product
+ *
+ *   C = alpha * op(A) x op(B) + beta * C,   op(A) M x K, op(B) K x N,
+ *
+ * where op(X) = X for SGEMM_OP_N and the transpose of X for SGEMM_OP_T.  All
+ * matrices are row-major; a transposed operand is the one stored the other
+ * way round, which is how a row-major matrix looks to a column-major library
+ * (DD2360 workbook, Module 15, section 15.2: passing a transpose flag instead
+ * of moving data), and how the products with a transposed operand in
+ * attention arise ("4.1 CUDA GEMM operator performance optimization",
+ * section 1.2).  No operand is copied: transposed operands are loaded as
+ * they are stored.
+ *
+ *   transa    SGEMM_OP_N: A is M x K (lda >= max(1,K));
+ *             SGEMM_OP_T: A is stored K x M (lda >= max(1,M)).
+ *   transb    SGEMM_OP_N: B is K x N (ldb >= max(1,N));
+ *             SGEMM_OP_T: B is stored N x K (ldb >= max(1,K)).
+ *   alpha, beta  scalars.  C is read only when beta != 0; with beta == 0 its
+ *             previous contents (NaN included) are ignored.  alpha == 0 or
+ *             K == 0 gives C = beta * C without reading A or B (beta == 1
+ *             then launches nothing).
+ *   workspace, workspace_bytes
+ *             optional device memory (16-byte aligned, not overlapping A, B
+ *             or C; NULL with 0 bytes for none) that lets the selector split K
+ *             across workgroups when the output has too few tiles to fill the
+ *             chip.  Each split writes its partial product to the workspace
+ *             and a second kernel adds the partials in a fixed order, so the
+ *             result is reproducible bit for bit.  The library uses at most
+ *             workspace_bytes; sgemm_f32_workspace_size gives what the
+ *             selector would like.  The workspace is scratch: its contents
+ *             on entry do not matter, and the caller must not touch it until
+ *             the work on `stream` completes.
+ * Limits: the leading dimension of a k-contiguous operand (A, or a
+ * transposed B) <= 2^22 - 64, of the other (B, or a transposed A)
+ * <= 2^25 - 512.  Otherwise as sgemm_f32 (the two are the same for
+ * transa = transb = SGEMM_OP_N, alpha = 1, beta = 0 and no workspace).
  */
-int sgemm_f32_ex(int M, int N, int K,
-                 const float *A, int lda,
-                 const float *B, int ldb,
-                 float *C, int ldc,
+int sgemm_f32_gemm(int transa, int transb, int M, int N, int K,
+                   float alpha,
+                   const float *A, int lda,
+                   const float *B, int ldb,
+                   float beta,
+                   float *C, int ldc,
+                   void *workspace, size_t workspace_bytes,
+                   hipStream_t stream);
+
+/*
+ * sgemm_f32_strided_batched: `batch` independent products
+ *
+ *   C_z = alpha * op(A_z) x op(B_z) + beta * C_z,   z = 0 .. batch-1,
+ *
+ * with X_z = X + z * stride_x (elements), as in the batched matrix products
+ * of multi-head attention ("4.1 CUDA GEMM operator performance
+ * optimization", section 1.2), in one launch.  Strides are >= 0 (0 reuses one
+ * operand for every entry); stride_c must keep the C_z apart
+ * (stride_c >= (M-1)*ldc + N when batch > 1).  batch == 0 does nothing.  The
+ * memory spanned by all C_z must not overlap that of all A_z or all B_z.
+ * Workspace as for sgemm_f32_gemm (a split needs room for every entry's
+ * partials).  Other arguments as sgemm_f32_gemm.
+ */
+int sgemm_f32_strided_batched(int transa, int transb, int M, int N, int K,
+                              float alpha,
+                              const float *A, int lda, long long stride_a,
+                              const float *B, int ldb, long long stride_b,
+                              float beta,
+                              float *C, int ldc, long long stride_c,
+                              int batch,
+                              void *workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/*
+ * sgemm_f32_workspace_size: *bytes = the workspace the selector's preferred
+ * configuration uses for these sizes on the current device, assuming
+ * 16-byte aligned operands (0 when it does not split K).  Passing that much
+ * to sgemm_f32_gemm / sgemm_f32_strided_batched lets them run it.
+ */
+int sgemm_f32_workspace_size(int transa, int transb, int M, int N, int K,
+                             int lda, int ldb, int ldc, int batch, size_t *bytes);
+
+/*
+ * sgemm_f32_ex: sgemm_f32_strided_batched with a forced configuration, for
+ * sweeps and for the measured comparison kernels.  cfg == NULL behaves as
+ * sgemm_f32_strided_batched.  Otherwise cfg->id selects the variant (see
+ * sgemm_f32_variant), cfg->splits the requested K split (<= 1: none; the
+ * split actually used is reported by sgemm_f32_plan), and cfg->group_m and
+ * cfg->xcd_remap the tile order; the other fields are ignored.  Returns
+ * hipErrorInvalidValue for an id out of range, a variant not compiled for
+ * the operand layout, cfg->group_m < 0, or a workspace too small for the
+ * split.  Same arguments, ownership and errors as sgemm_f32_strided_batched.
+ */
+int sgemm_f32_ex(int transa, int transb, int M, int N, int K,
+                 float alpha,
+                 const float *A, int lda, long long stride_a,
+                 const float *B, int ldb, long long stride_b,
+                 float beta,
+                 float *C, int ldc, long long stride_c,
+                 int batch,
+                 void *workspace, size_t workspace_bytes,
                  hipStream_t stream, const sgemm_cfg *cfg);
 
 /*
- * sgemm_f32_plan: the configuration sgemm_f32 chooses for these sizes on a
- * device with `num_cus` compute units (<= 0 means 256).  Pure host logic, no
- * HIP call.  Writes *out; returns hipErrorInvalidValue for invalid sizes or
- * leading dimensions, or out == NULL.  The geometry fields follow the
- * round-up-and-guard rule (DD2360 workbook, Module 6, section 6.3):
- * tiles_m = ceil(M/BM), tiles_n = ceil(N/BN), grid = tiles_m * tiles_n.
+ * sgemm_f32_plan: the configuration the library chooses for these sizes on
+ * a device with `num_cus` compute units (<= 0 means 256), given
+ * `workspace_bytes` of workspace and 16-byte aligned operands.  Pure host
+ * logic, no HIP call.  Writes *out; returns hipErrorInvalidValue for invalid
+ * sizes, layouts or leading dimensions, or out == NULL.  The geometry follows
+ * the round-up-and-guard rule (DD2360 workbook, Module 6, section 6.3):
+ * tiles_m = ceil(M/BM), tiles_n = ceil(N/BN), grid = tiles_m * tiles_n *
+ * splits * batch.
  */
-int sgemm_f32_plan(int M, int N, int K, int lda, int ldb, int ldc,
-                   int num_cus, sgemm_cfg *out);
+int sgemm_f32_plan(int transa, int transb, int M, int N, int K,
+                   int lda, int ldb, int ldc, int batch,
+                   int num_cus, long long workspace_bytes, sgemm_cfg *out);
 
 /*
- * sgemm_f32_query: the configuration sgemm_f32 would launch for these
- * arguments on the current device (queries the device once and caches it).
+ * sgemm_f32_cfg_geometry: completes a forced configuration.  Reads cfg->id,
+ * cfg->splits, cfg->group_m and cfg->xcd_remap (as sgemm_f32_ex does) and
+ * fills in the rest as sgemm_f32_plan would for that variant and requested
+ * split: the split actually used, k_chunk, the grid and the workspace bytes
+ * it needs.  Pure host logic.  Returns hipErrorInvalidValue for invalid
+ * sizes, an id out of range, a variant not compiled for the operand layout
+ * or cfg->group_m < 0.
  */
-int sgemm_f32_query(int M, int N, int K,
-                    const float *A, int lda,
-                    const float *B, int ldb,
-                    float *C, int ldc, sgemm_cfg *out);
+int sgemm_f32_cfg_geometry(int transa, int transb, int M, int N, int K,
+                           int lda, int ldb, int ldc, int batch, sgemm_cfg *cfg);
+
+/*
+ * sgemm_f32_query: the configuration sgemm_f32_ex(..., cfg = NULL) would
+ * launch for these arguments on the current device (queries the device once
+ * and caches it).  Same validation as the launch.
+ */
+int sgemm_f32_query(int transa, int transb, int M, int N, int K,
+                    const float *A, int lda, long long stride_a,
+                    const float *B, int ldb, long long stride_b,
+                    float *C, int ldc, long long stride_c,
+                    int batch, void *workspace, size_t workspace_bytes,
+                    sgemm_cfg *out);
 
 /* Number of compiled variants, and the description of variant `id`. */
 int sgemm_f32_num_variants(void);
 int sgemm_f32_variant(int id, sgemm_cfg *out);
+
+/*
+ * sgemm_f32_variant_ops: bit (transa + 2*transb) is set when variant `id` is
+ * compiled for that operand layout; -1 for an id out of range.
+ */
+int sgemm_f32_variant_ops(int id);
 
 /* Library version string (static storage). */
 const char *sgemm_f32_version(void);

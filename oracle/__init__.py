@@ -13,6 +13,20 @@ for row-major A (M x K) and B (K x N): the definition C = A x B of
 double-accumulating CPU reference of the DD2360 workbook ("Applied GPU
 Programming"), section 14.3, lab "tiled matmul, square case".
 
+The general form used by the library's BLAS-style entry points,
+  C = alpha * op(A) x op(B) + beta * C0,   op(X) = X or its transpose,
+is taken in float64 on top of that: gemm_ref forms op(A) and op(B) with
+numpy's transpose of the stored operand (a transposed operand is the matrix
+stored the other way round, as a row-major matrix looks to a column-major
+library: DD2360 workbook, Module 15, section 15.2), computes the product
+above, and returns
+  ref  = alpha * ref_AB + beta * C0
+  absb = |alpha| * absb_AB + |beta * C0|
+with C0 not read at all when beta == 0 and A, B not read when alpha == 0
+(BLAS conventions, which the pages do not spell out).  gemm_ref_batched
+repeats it per batch entry, as for the batched products of multi-head
+attention ("4.1 CUDA GEMM operator performance optimization", section 1.2).
+
 Acceptance: |C - ref| <= 1e-4 * absb for every checked element, and C finite.
 The workbook's lab uses 1e-4 relative to |ref|; absb >= |ref| always and does
 not collapse when the terms cancel, so the bound is taken relative to absb.
@@ -117,6 +131,64 @@ def sgemm_ref_sampled(A, B, rows, cols, nthreads=None):
     if rc != 0:
         raise RuntimeError(f"oracle_sgemm_sampled failed with code {rc}")
     return ref, absb
+
+
+def gemm_ref(A, B, transa=False, transb=False, alpha=1.0, beta=0.0, C0=None, nthreads=None):
+    """General form: returns (ref, absb) of alpha * op(A) @ op(B) + beta * C0.
+
+    A and B are the stored float32 operands: op(A) is A (M x K) or, with
+    transa, A.T for A stored K x M; likewise B (K x N, or N x K with transb).
+    C0 (M x N, float32) is read only when beta != 0.
+    """
+    A = _as_f32_2d(A, "A")
+    B = _as_f32_2d(B, "B")
+    opa = np.ascontiguousarray(A.T) if transa else A
+    opb = np.ascontiguousarray(B.T) if transb else B
+    M, K = opa.shape
+    K2, N = opb.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    alpha = float(np.float32(alpha))
+    beta = float(np.float32(beta))
+    if alpha != 0.0 and K > 0:
+        ab, ab_abs = sgemm_ref(opa, opb, nthreads)
+        ref = alpha * ab
+        absb = abs(alpha) * ab_abs
+    else:
+        ref = np.zeros((M, N), dtype=np.float64)
+        absb = np.zeros((M, N), dtype=np.float64)
+    if beta != 0.0:
+        if C0 is None:
+            raise ValueError("beta != 0 needs C0")
+        c0 = np.asarray(C0, dtype=np.float64)
+        if c0.shape != (M, N):
+            raise ValueError("C0 has the wrong shape")
+        ref = ref + beta * c0
+        absb = absb + np.abs(beta * c0)
+    return ref, absb
+
+
+def gemm_ref_batched(A, B, transa=False, transb=False, alpha=1.0, beta=0.0, C0=None,
+                     nthreads=None):
+    """gemm_ref per batch entry of 3-D stacks (a stack of one broadcasts)."""
+    A = np.asarray(A)
+    B = np.asarray(B)
+    if A.ndim != 3 or B.ndim != 3:
+        raise ValueError("A and B must be 3-D stacks")
+    batch = max(A.shape[0], B.shape[0])
+    if A.shape[0] not in (1, batch) or B.shape[0] not in (1, batch):
+        raise ValueError("batch sizes differ")
+    refs, absbs = [], []
+    for z in range(batch):
+        a = A[z if A.shape[0] > 1 else 0]
+        b = B[z if B.shape[0] > 1 else 0]
+        c0 = None if C0 is None else C0[z]
+        r, s = gemm_ref(a, b, transa, transb, alpha, beta, c0, nthreads)
+        refs.append(r)
+        absbs.append(s)
+    if not refs:
+        return np.zeros((0, 0, 0)), np.zeros((0, 0, 0))
+    return np.stack(refs), np.stack(absbs)
 
 
 def compare(C, ref, absb, tol=TOL):

@@ -111,19 +111,97 @@ def test_empty_output_is_a_noop(lib):
     assert _call(5, 0, 7, A=0, B=0, C=0) == 0
 
 
+def _ex(cfg, M=4, N=4, K=4, ta=0, tb=0, ws=0, ws_bytes=0):
+    lda = (M if ta else K)
+    ldb = (K if tb else N)
+    return sg.sgemm_f32_ex(ta, tb, M, N, K, 1.0, P, lda, 0, 2 * P, ldb, 0, 0.0, 3 * P, N, 0, 1,
+                           ws, ws_bytes, 0, cfg)
+
+
 def test_ex_rejects_bad_forced_variant(lib):
     cfg = sg.binding.SgemmCfg()
     cfg.id = sg.sgemm_f32_num_variants()
-    assert sg.sgemm_f32_ex(4, 4, 4, P, 4, 2 * P, 4, 3 * P, 4, 0, cfg) == HIP_ERROR_INVALID_VALUE
+    assert _ex(cfg) == HIP_ERROR_INVALID_VALUE
     cfg.id = 0
     cfg.group_m = -1  # negative group height
-    assert sg.sgemm_f32_ex(4, 4, 4, P, 4, 2 * P, 4, 3 * P, 4, 0, cfg) == HIP_ERROR_INVALID_VALUE
+    assert _ex(cfg) == HIP_ERROR_INVALID_VALUE
+    cfg.group_m = 8
+    cfg.id = 7        # the vector-FMA comparison has no transposed-operand kernels
+    assert sg.sgemm_f32_variant_ops(7) == 1
+    assert _ex(cfg, ta=1) == HIP_ERROR_INVALID_VALUE
+    cfg.id = 0
+    cfg.splits = 4    # a split needs a workspace
+    assert _ex(cfg, K=1024) == HIP_ERROR_INVALID_VALUE
 
 
 def test_ex_rejects_limits(lib):
     # lda beyond the 32-bit in-slice offset limit
     assert sg.sgemm_f32(4, 4, 4, P, 1 << 22, 2 * P, 4, 3 * P, 4, 0) == HIP_ERROR_INVALID_VALUE
     assert sg.sgemm_f32(4, 4, 4, P, 4, 2 * P, 1 << 25, 3 * P, 4, 0) == HIP_ERROR_INVALID_VALUE
+    # the limits follow the layout: a transposed A is index-contiguous
+    cfg = sg.binding.SgemmCfg()
+    lib_ = sg.load()
+    out = sg.binding.SgemmCfg()
+    assert lib_.sgemm_f32_plan(1, 0, 4, 4, 4, (1 << 22), 4, 4, 1, 256, 0, ctypes.byref(out)) == 0
+    assert lib_.sgemm_f32_plan(0, 0, 4, 4, 4, (1 << 22), 4, 4, 1, 256, 0, ctypes.byref(out)) \
+        == HIP_ERROR_INVALID_VALUE
+    assert lib_.sgemm_f32_plan(0, 1, 4, 4, 4, 4, (1 << 22), 4, 1, 256, 0, ctypes.byref(out)) \
+        == HIP_ERROR_INVALID_VALUE
+    del cfg
+
+
+def _gen(ta=0, tb=0, M=4, N=4, K=4, A=P, lda=None, sa=0, B=2 * P, ldb=None, sb=0,
+         C=3 * P, ldc=None, sc=0, batch=1, ws=0, ws_bytes=0, alpha=1.0, beta=0.0):
+    lda = max(M if ta else K, 1) if lda is None else lda
+    ldb = max(K if tb else N, 1) if ldb is None else ldb
+    ldc = max(N, 1) if ldc is None else ldc
+    return sg.sgemm_f32_strided_batched(ta, tb, M, N, K, alpha, A, lda, sa, B, ldb, sb, beta,
+                                        C, ldc, sc, batch, ws, ws_bytes, 0)
+
+
+GEN_BAD = [
+    dict(ta=2),                                  # not a layout
+    dict(tb=-1),
+    dict(ta=1, M=8, K=4, lda=7),                 # transposed A: lda >= M
+    dict(tb=1, N=4, K=8, ldb=7),                 # transposed B: ldb >= K
+    dict(batch=-1),
+    dict(batch=2, sa=-4, sc=64),                 # negative stride
+    dict(batch=2, sc=8),                         # C entries overlap (need 16)
+    dict(batch=3, sc=16, C=2 * P + 64, sb=16),   # C's span overlaps B's span
+    dict(ws=4 * P + 4, ws_bytes=1024),           # workspace not 16-byte aligned
+    dict(ws=0, ws_bytes=0, C=0),                 # null C
+    dict(ws=3 * P, ws_bytes=64),                 # workspace overlaps C
+    dict(ws=P, ws_bytes=64),                     # workspace overlaps A
+]
+
+
+@pytest.mark.parametrize("args", GEN_BAD)
+def test_general_invalid_arguments_rejected(lib, args):
+    assert _gen(**args) == HIP_ERROR_INVALID_VALUE
+
+
+def test_general_noops(lib):
+    # batch 0, M 0 or N 0: nothing to do, pointers never looked at
+    assert _gen(batch=0, A=0, B=0, C=0) == 0
+    assert _gen(M=0, A=0, B=0, C=0) == 0
+    # K == 0 (or alpha == 0) with beta == 1 leaves C as it is: no launch
+    assert _gen(K=0, A=0, B=0, beta=1.0) == 0
+    assert _gen(alpha=0.0, beta=1.0) == 0
+
+
+def test_variant_layouts(lib):
+    """Every variant has the plain layout; the direct-load tiles also carry
+    the transposed ones (the 96-row wave tiles only a transposed B)."""
+    n = sg.sgemm_f32_num_variants()
+    masks = [sg.sgemm_f32_variant_ops(i) for i in range(n)]
+    assert all(m & 1 for m in masks)
+    assert sum(1 for m in masks if m == 0xF) >= 2
+    assert sg.sgemm_f32_variant_ops(n) == -1
+    for ta in (0, 1):
+        for tb in (0, 1):
+            p = sg.sgemm_f32_plan(1000, 900, 800, 1000 if ta else 800, 800 if tb else 900, 900,
+                                  256, ta, tb)
+            assert masks[p.id] & (1 << (ta + 2 * tb))
 
 
 SHAPES = [(512, 512, 512), (2048, 2048, 2048), (3072, 3072, 3072), (8192, 8192, 4096),
@@ -134,13 +212,29 @@ SHAPES = [(512, 512, 512), (2048, 2048, 2048), (3072, 3072, 3072), (8192, 8192, 
 @pytest.mark.parametrize("M,N,K", SHAPES)
 def test_plan_geometry(lib, M, N, K):
     for cus in (256, 80):
-        p = sg.sgemm_f32_plan(M, N, K, max(K, 1), N, N, cus)
-        assert p.kernel == sg.binding.SGEMM_KERNEL_MFMA
-        assert p.tiles_m == metrics.ceil_div(M, p.bm)
-        assert p.tiles_n == metrics.ceil_div(N, p.bn)
-        assert p.grid == p.tiles_m * p.tiles_n
-        assert p.threads == 64 * p.waves_m * p.waves_n
-        assert p.group_m > 0 and p.xcd_remap == 1
+        for ws in (0, 1 << 40):
+            p = sg.sgemm_f32_plan(M, N, K, max(K, 1), N, N, cus, workspace_bytes=ws)
+            assert p.kernel == sg.binding.SGEMM_KERNEL_MFMA
+            assert p.tiles_m == metrics.ceil_div(M, p.bm)
+            assert p.tiles_n == metrics.ceil_div(N, p.bn)
+            assert p.grid == p.tiles_m * p.tiles_n * p.splits
+            assert p.threads == 64 * p.waves_m * p.waves_n
+            assert p.group_m > 0 and p.xcd_remap == 1
+            if ws == 0:
+                assert p.splits == 1 and p.workspace_bytes == 0
+            _check_split(p, M, N, K, 1)
+
+
+def _check_split(p, M, N, K, batch):
+    """A split's K ranges tile [0, K) in multiples of 64, and its workspace
+    holds one partial result (rows padded to 4 floats) per split and entry."""
+    assert p.splits >= 1
+    if p.splits == 1:
+        assert p.workspace_bytes == 0 and p.k_chunk >= max(K, 1)
+        return
+    assert p.k_chunk % 64 == 0
+    assert (p.splits - 1) * p.k_chunk < K <= p.splits * p.k_chunk
+    assert p.workspace_bytes == batch * p.splits * M * ((N + 3) // 4 * 4) * 4
 
 
 def test_selector_prefers_full_waves(lib):
@@ -154,8 +248,40 @@ def test_selector_prefers_full_waves(lib):
     assert p.grid * p.bm * p.bn == 8192 * 8192
 
 
+def test_selector_splits_k_for_few_tiles(lib):
+    """With a workspace, a long-K product with few output tiles is split
+    across workgroups (one 128 x 128 output is a single tile otherwise); a
+    grid that already fills the chip is not."""
+    p = sg.sgemm_f32_plan(128, 128, 32768, 32768, 128, 128, 256, workspace_bytes=1 << 30)
+    assert p.splits >= 16
+    _check_split(p, 128, 128, 32768, 1)
+    p = sg.sgemm_f32_plan(8192, 8192, 8192, 8192, 8192, 8192, 256, workspace_bytes=1 << 40)
+    assert p.splits == 1
+    # the workspace limit is respected
+    p = sg.sgemm_f32_plan(128, 128, 32768, 32768, 128, 128, 256, workspace_bytes=4 * 128 * 128 * 4)
+    assert p.splits <= 4 and p.workspace_bytes <= 4 * 128 * 128 * 4
+    # batches fill the chip by themselves
+    p = sg.sgemm_f32_plan(128, 128, 4096, 4096, 128, 128, 256, batch=512,
+                          workspace_bytes=1 << 40)
+    assert p.splits == 1 and p.grid == 512
+
+
+def test_cfg_geometry_of_forced_splits(lib):
+    for want, K in [(2, 1000), (3, 1000), (7, 4099), (64, 32768), (100, 32768), (8, 64), (4, 65)]:
+        cfg = sg.SgemmCfg()
+        cfg.id, cfg.splits, cfg.group_m, cfg.xcd_remap = 1, want, 8, 1
+        g = sg.sgemm_f32_cfg_geometry(cfg, 0, 0, 300, 200, K, K, 200, 200, 3)
+        assert g.id == 1 and g.group_m == 8 and g.xcd_remap == 1
+        assert g.splits <= max(min(want, 64), 1)
+        _check_split(g, 300, 200, K, 3)
+        assert g.grid == g.tiles_m * g.tiles_n * g.splits * 3
+
+
 def test_plan_rejects_invalid(lib):
     out = sg.binding.SgemmCfg()
-    assert lib.sgemm_f32_plan(-1, 4, 4, 4, 4, 4, 256, ctypes.byref(out)) == HIP_ERROR_INVALID_VALUE
-    assert lib.sgemm_f32_plan(4, 4, 8, 4, 4, 4, 256, ctypes.byref(out)) == HIP_ERROR_INVALID_VALUE
-    assert lib.sgemm_f32_plan(4, 4, 4, 4, 4, 4, 256, None) == HIP_ERROR_INVALID_VALUE
+    plan = lib.sgemm_f32_plan
+    assert plan(0, 0, -1, 4, 4, 4, 4, 4, 1, 256, 0, ctypes.byref(out)) == HIP_ERROR_INVALID_VALUE
+    assert plan(0, 0, 4, 4, 8, 4, 4, 4, 1, 256, 0, ctypes.byref(out)) == HIP_ERROR_INVALID_VALUE
+    assert plan(0, 0, 4, 4, 4, 4, 4, 4, 1, 256, 0, None) == HIP_ERROR_INVALID_VALUE
+    assert plan(3, 0, 4, 4, 4, 4, 4, 4, 1, 256, 0, ctypes.byref(out)) == HIP_ERROR_INVALID_VALUE
+    assert plan(0, 0, 4, 4, 4, 4, 4, 4, -1, 256, 0, ctypes.byref(out)) == HIP_ERROR_INVALID_VALUE

@@ -1,0 +1,265 @@
+"""GPU parity for the BLAS-style paths: transposed operands, alpha/beta,
+K split across workgroups with a fixed-order reduction, and strided batches.
+Every result is compared element by element with the CPU reference's general
+form (oracle.gemm_ref / gemm_ref_batched) on seeded inputs."""
+import numpy as np
+import pytest
+
+import oracle
+import fp32_gemm_sgemm_amd as sg
+from fp32_gemm_sgemm_amd import inputs
+from gpu_cases import (check_general, forced, forced_split, note, place, run_general,
+                       stored)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+LAYOUTS = [(0, 0), (1, 0), (0, 1), (1, 1)]
+
+
+def variants_for(ta, tb, selectable_only=False):
+    out = []
+    for vid in range(sg.sgemm_f32_num_variants()):
+        if sg.sgemm_f32_variant_ops(vid) & (1 << (ta + 2 * tb)):
+            out.append(vid)
+    return out
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+@pytest.mark.parametrize("M,N,K", [(300, 200, 100), (257, 513, 129), (64, 96, 33), (1, 1, 1),
+                                   (520, 390, 700)])
+def test_transposed_layouts_default(ta, tb, M, N, K):
+    note(f"layout ta={ta} tb={tb} {M}x{N}x{K}")
+    A, B = inputs.make_operands(M, N, K, seed=70 + ta + 2 * tb)
+    As, Bs = stored(A, ta), stored(B, tb)
+    check_general(run_general(As, Bs, ta, tb), As, Bs, ta, tb)
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_transposed_layouts_every_variant(ta, tb):
+    """Each variant compiled for the layout, on a shape spanning several
+    tiles with ragged edges in M, N and K; aligned (direct loads) and with
+    padded, odd row strides and a 4-byte shifted start (register fetch)."""
+    M, N, K = 517, 389, 261
+    A, B = inputs.make_operands(M, N, K, seed=80 + ta + 2 * tb)
+    As, Bs = stored(A, ta), stored(B, tb)
+    for vid in variants_for(ta, tb):
+        for pad, shift in [((0, 0, 0), (0, 0, 0)), ((4, 8, 0), (0, 0, 0)),
+                           ((3, 1, 5), (1, 1, 1))]:
+            note(f"layout ta={ta} tb={tb} variant {vid} pad={pad} shift={shift}")
+            C = run_general(As, Bs, ta, tb, cfg=forced(vid), pad=pad, shift=shift)
+            check_general(C, As, Bs, ta, tb)
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_transposed_exact_cases(ta, tb):
+    """Closed forms through the transposed paths: a stored permutation
+    matrix used transposed gathers rows (or columns) by the inverse
+    permutation, exactly."""
+    n = 131
+    P, perm = inputs.permutation(n, seed=90)
+    _, X = inputs.make_operands(n, 77, n, seed=91)
+    note(f"permutation ta={ta} tb={tb}")
+    if tb == 0:
+        # op(A) = P or P^T; B = X (stored transposed when ta... only A varies)
+        C = run_general(P, stored(X, 0), ta, 0)
+        want = X[np.argsort(perm)] if ta else X[perm]
+        assert np.array_equal(C, want)
+    else:
+        Y = np.ascontiguousarray(X.T)                 # 77 x n
+        C = run_general(stored(Y, ta), P, ta, 1)
+        want = Y[:, perm]
+        assert np.array_equal(C, want)
+
+
+@pytest.mark.parametrize("alpha,beta", [(1.5, -0.75), (-2.0, 0.0), (0.0, 0.5), (0.0, 0.0),
+                                        (1.0, 1.0), (0.25, 2.0)])
+def test_alpha_beta(alpha, beta):
+    M, N, K = 333, 222, 150
+    A, B = inputs.make_operands(M, N, K, seed=100)
+    C0 = inputs.make_operands(M, N, 1, seed=101)[0][:, :1] * np.linspace(-1, 1, N, dtype=np.float32)
+    C0 = np.ascontiguousarray(C0.astype(np.float32))
+    for vid in (None, 1, 7, 9, 11, 12, 13):
+        note(f"alpha={alpha} beta={beta} variant {vid}")
+        cfg = None if vid is None else forced(vid)
+        C = run_general(A, B, 0, 0, alpha, beta, C0, cfg=cfg)
+        check_general(C, A, B, 0, 0, alpha, beta, C0)
+        if alpha == 0.0:
+            assert np.array_equal(C, (np.float32(beta) * C0).astype(np.float32))
+
+
+def test_beta_zero_ignores_nan_and_k_zero_scales():
+    M, N = 100, 60
+    A, B = inputs.make_operands(M, N, 40, seed=102)
+    note("beta 0 over NaN C")
+    nan = np.full((M, N), np.nan, np.float32)
+    C = run_general(A, B, 0, 0, 1.0, 0.0, nan)
+    check_general(C, A, B, 0, 0)
+    note("K = 0 with beta")
+    C0 = inputs.make_operands(M, N, 1, seed=103)[0][:, :1] * np.ones((1, N), np.float32)
+    Z, Zb = np.zeros((M, 0), np.float32), np.zeros((0, N), np.float32)
+    C = run_general(Z, Zb, 0, 0, 3.0, -0.5, np.ascontiguousarray(C0))
+    assert np.array_equal(C, (np.float32(-0.5) * C0).astype(np.float32))
+
+
+SPLIT_VARIANTS = [1, 7, 9, 11, 12, 13]
+
+
+@pytest.mark.parametrize("K", [1000, 1001, 130])
+def test_split_k_forced(K):
+    """Every kernel family with forced K splits (ragged last split, K not a
+    multiple of 4), reduced in fixed order: within the bound, and bitwise the
+    same on a second run."""
+    M, N = 300, 203
+    A, B = inputs.make_operands(M, N, K, seed=110 + K)
+    for vid in SPLIT_VARIANTS:
+        for splits in (2, 3, 8):
+            note(f"split-K variant {vid} splits {splits} K={K}")
+            cfg = forced_split(vid, splits)
+            C1 = run_general(A, B, 0, 0, cfg=cfg)
+            check_general(C1, A, B, 0, 0)
+            C2 = run_general(A, B, 0, 0, cfg=cfg)
+            assert np.array_equal(C1, C2)
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_split_k_with_layouts_and_scalars(ta, tb):
+    M, N, K = 190, 170, 1500
+    A, B = inputs.make_operands(M, N, K, seed=120 + ta + 2 * tb)
+    As, Bs = stored(A, ta), stored(B, tb)
+    C0 = np.ascontiguousarray(inputs.make_operands(M, N, 1, seed=121)[0][:, :1] *
+                              np.ones((1, N), np.float32))
+    for vid in (11, 12):
+        note(f"split-K layout ta={ta} tb={tb} variant {vid}")
+        C = run_general(As, Bs, ta, tb, -1.25, 0.5, C0, cfg=forced_split(vid, 5))
+        check_general(C, As, Bs, ta, tb, -1.25, 0.5, C0)
+
+
+def test_split_k_long_k_single_tile_auto():
+    """128 x 128 x 32768 (one output tile): with a workspace the selector
+    splits K; the result is checked in full and is reproducible."""
+    M, N, K = 128, 128, 32768
+    A, B = inputs.make_operands(M, N, K, seed=47)
+    Ad, Bd = place(A), place(B)
+    Cd = torch.empty((M, N), device="cuda")
+    ws_bytes = sg.sgemm_f32_workspace_size(0, 0, M, N, K, K, N, N, 1)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    q = sg.sgemm_f32_query(0, 0, M, N, K, Ad.data_ptr(), K, 0, Bd.data_ptr(), N, 0,
+                           Cd.data_ptr(), N, 0, 1, ws.data_ptr(), ws_bytes)
+    note(f"auto split 128x128x32768: variant {q.id} splits {q.splits} ws {ws_bytes}")
+    assert q.splits > 1 and q.workspace_bytes == ws_bytes
+    code = sg.sgemm_f32_gemm(0, 0, M, N, K, 1.0, Ad.data_ptr(), K, Bd.data_ptr(), N, 0.0,
+                             Cd.data_ptr(), N, ws.data_ptr(), ws_bytes,
+                             torch.cuda.current_stream().cuda_stream)
+    assert code == 0
+    torch.cuda.synchronize()
+    C1 = Cd.cpu().numpy()
+    check_general(C1, A, B, 0, 0)
+    sg.sgemm_f32_gemm(0, 0, M, N, K, 1.0, Ad.data_ptr(), K, Bd.data_ptr(), N, 0.0,
+                      Cd.data_ptr(), N, ws.data_ptr(), ws_bytes,
+                      torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert np.array_equal(C1, Cd.cpu().numpy())
+
+
+def test_small_config_with_workspace():
+    """512^3 (the small configuration) through the workspace entry point."""
+    A, B = inputs.make_operands(512, 512, 512, seed=0)
+    note("512^3 with workspace")
+    C = run_general(A, B, 0, 0)
+    check_general(C, A, B, 0, 0)
+
+
+def _batched_stack(batch, rows, cols, seed, gap):
+    """A (batch, rows, cols) device view whose entries are rows*cols + gap
+    floats apart, and the host copy."""
+    rng = np.random.default_rng(seed)
+    host = rng.uniform(-1, 1, (batch, rows, cols)).astype(np.float32)
+    stride = rows * cols + gap
+    buf = torch.zeros(max(batch * stride, 1), dtype=torch.float32, device="cuda")
+    view = torch.as_strided(buf, (batch, rows, cols), (stride, cols, 1))
+    view.copy_(torch.from_numpy(host))
+    return view, host
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_strided_batched(ta, tb):
+    batch, M, N, K = 5, 70, 90, 130
+    Ar = (K, M) if ta else (M, K)
+    Br = (N, K) if tb else (K, N)
+    A, Ah = _batched_stack(batch, *Ar, seed=130, gap=37)
+    B, Bh = _batched_stack(batch, *Br, seed=131, gap=0)
+    C0h = np.random.default_rng(132).uniform(-1, 1, (batch, M, N)).astype(np.float32)
+    C = torch.zeros((batch, M, N + 3), device="cuda")[:, :, :N]
+    C.copy_(torch.from_numpy(C0h))
+    note(f"strided batched ta={ta} tb={tb}")
+    sg.sgemm_batched(A, B, out=C, transa=ta, transb=tb, alpha=0.5, beta=-1.0)
+    torch.cuda.synchronize()
+    ref, absb = oracle.gemm_ref_batched(Ah, Bh, ta, tb, 0.5, -1.0, C0h)
+    rep = oracle.compare(C.cpu().numpy(), ref, absb)
+    assert rep["n_bad"] == 0, rep
+
+
+def test_strided_batched_broadcast_and_split():
+    """Stride 0 reuses one B for every entry; a forced split over a batch."""
+    batch, M, N, K = 7, 100, 64, 900
+    A, Ah = _batched_stack(batch, M, K, seed=140, gap=5)
+    B, Bh = _batched_stack(1, K, N, seed=141, gap=0)
+    for cfg in (None, forced_split(12, 3), forced_split(1, 4)):
+        note(f"batched broadcast cfg={None if cfg is None else (cfg.id, cfg.splits)}")
+        C = sg.sgemm_batched(A, B, cfg=cfg)
+        torch.cuda.synchronize()
+        ref, absb = oracle.gemm_ref_batched(Ah, Bh)
+        rep = oracle.compare(C.cpu().numpy(), ref, absb)
+        assert rep["n_bad"] == 0, rep
+
+
+def test_batched_many_small_entries():
+    batch, M, N, K = 3000, 8, 12, 20
+    A, Ah = _batched_stack(batch, M, K, seed=150, gap=0)
+    B, Bh = _batched_stack(batch, K, N, seed=151, gap=0)
+    note("3000 small entries")
+    C = sg.sgemm_batched(A, B)
+    torch.cuda.synchronize()
+    ref, absb = oracle.gemm_ref_batched(Ah, Bh)
+    rep = oracle.compare(C.cpu().numpy(), ref, absb)
+    assert rep["n_bad"] == 0, rep
+
+
+def test_batch_beyond_one_launch():
+    """More entries than one reduction launch's second grid dimension holds
+    (65535) and, for the GEMM, more workgroups than one dispatch holds
+    (2^32 work-items): the host splits the launches.  A and B are broadcast
+    (stride 0), so every entry must equal the one reference."""
+    M, N, K = 4, 4, 128
+    A, B = inputs.make_operands(M, N, K, seed=160)
+    Ad, Bd = place(A), place(B)
+    ref, absb = oracle.gemm_ref(A, B)
+    for batch, cfg in [(70000, forced_split(1, 2)), (8_500_000, forced(0))]:
+        note(f"batch {batch} cfg ({cfg.id}, {cfg.splits})")
+        C = torch.empty((batch, M, N), device="cuda")
+        ws_bytes = sg.sgemm_f32_cfg_geometry(cfg, 0, 0, M, N, K, K, N, N, batch).workspace_bytes
+        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+        code = sg.sgemm_f32_ex(0, 0, M, N, K, 1.0, Ad.data_ptr(), K, 0, Bd.data_ptr(), N, 0,
+                               0.0, C.data_ptr(), N, M * N, batch, ws.data_ptr(), ws_bytes,
+                               torch.cuda.current_stream().cuda_stream, cfg)
+        assert code == 0
+        torch.cuda.synchronize()
+        Ch = C.cpu().numpy()
+        rep = oracle.compare(Ch[0], ref, absb)
+        assert rep["n_bad"] == 0, rep
+        assert np.all(Ch == Ch[0][None])
+        del C, ws
+        torch.cuda.empty_cache()
+
+
+def test_batch_zero_and_empty():
+    A = torch.zeros((0, 4, 4), device="cuda")
+    B = torch.zeros((0, 4, 4), device="cuda")
+    note("batch 0")
+    C = sg.sgemm_batched(A, B)
+    torch.cuda.synchronize()
+    assert C.shape == (0, 4, 4)

@@ -294,3 +294,102 @@ def test_pins_accept_oracle_and_reject_mutants():
     assert _pins_pass(lambda A, B: oracle.sgemm_ref(A, B))
     for m in _mutants():
         assert not _pins_pass(m), m.__name__
+
+
+# ---- the general form: op(), alpha, beta, batches ------------------------------------
+# Pinned by closed forms that a dropped or doubled transpose, a scalar applied
+# to the wrong term or a batch entry taken from the wrong place would break.
+
+def test_general_transposed_permutations():
+    """op(A) = P^T for a stored permutation P gives the inverse row
+    permutation of B; op(B) = P^T gives a column gather of A (exact)."""
+    P, perm = inputs.permutation(37, seed=61)
+    _, B = _rand(37, 23, 37, seed=62)
+    ref, _ = oracle.gemm_ref(P, B, transa=True)
+    assert np.array_equal(ref, B[np.argsort(perm)].astype(np.float64))
+    ref, _ = oracle.gemm_ref(P, B, transa=False)
+    assert np.array_equal(ref, B[perm].astype(np.float64))
+    A, _ = _rand(19, 37, 37, seed=63)
+    ref, _ = oracle.gemm_ref(A, P, transb=True)
+    assert np.array_equal(ref, A[:, perm].astype(np.float64))
+    ref, _ = oracle.gemm_ref(A, P, transb=False)
+    assert np.array_equal(ref, A[:, np.argsort(perm)].astype(np.float64))
+
+
+@pytest.mark.parametrize("ta,tb", [(False, False), (True, False), (False, True), (True, True)])
+def test_general_transposes_of_stored_transposes(ta, tb):
+    """Storing an operand transposed and asking for its transpose is the
+    plain product, on non-square shapes (a missed transpose changes the
+    shapes or the values)."""
+    A, B = _rand(21, 13, 17, seed=64)
+    As = np.ascontiguousarray(A.T) if ta else A
+    Bs = np.ascontiguousarray(B.T) if tb else B
+    ref, absb = oracle.gemm_ref(As, Bs, ta, tb)
+    want = np.array([[math.fsum(float(A[i, k]) * float(B[k, j]) for k in range(17))
+                      for j in range(13)] for i in range(21)])
+    assert np.all(np.abs(ref - want) <= _sum_bound(17, absb))
+    assert ref.shape == (21, 13)
+
+
+def test_general_alpha_beta_closed_forms():
+    A, B = _rand(12, 9, 7, seed=65)
+    C0 = inputs.make_operands(12, 9, 1, seed=66)[0][:, :1] * np.ones((1, 9), np.float32)
+    ref1, absb1 = oracle.gemm_ref(A, B)
+    # a power-of-two alpha scales exactly
+    ref, absb = oracle.gemm_ref(A, B, alpha=-0.5)
+    assert np.array_equal(ref, -0.5 * ref1) and np.array_equal(absb, 0.5 * absb1)
+    # alpha = 0: beta * C0 exactly, A and B not used (NaN operands are ignored)
+    nanA = np.full_like(A, np.nan)
+    ref, absb = oracle.gemm_ref(nanA, B, alpha=0.0, beta=-2.0, C0=C0)
+    assert np.array_equal(ref, -2.0 * C0.astype(np.float64))
+    assert np.array_equal(absb, 2.0 * np.abs(C0.astype(np.float64)))
+    # beta = 0: C0 not used (NaN is ignored)
+    ref, _ = oracle.gemm_ref(A, B, beta=0.0, C0=np.full((12, 9), np.nan, np.float32))
+    assert np.array_equal(ref, ref1)
+    # K = 0: beta * C0
+    Z, Zb = np.zeros((12, 0), np.float32), np.zeros((0, 9), np.float32)
+    ref, _ = oracle.gemm_ref(Z, Zb, alpha=3.0, beta=0.25, C0=C0)
+    assert np.array_equal(ref, 0.25 * C0.astype(np.float64))
+    # identity: alpha * I x B + beta * C0 with small integers is exact
+    rng = np.random.default_rng(67)
+    Bi = inputs.small_integers(rng, (12, 9))
+    Ci = inputs.small_integers(rng, (12, 9))
+    ref, _ = oracle.gemm_ref(inputs.identity(12), Bi, alpha=3.0, beta=-1.0, C0=Ci)
+    assert np.array_equal(ref, 3.0 * Bi.astype(np.float64) - Ci.astype(np.float64))
+
+
+def test_general_batched_entries_and_broadcast():
+    rng = np.random.default_rng(68)
+    A = rng.uniform(-1, 1, (3, 5, 4)).astype(np.float32)
+    B = rng.uniform(-1, 1, (1, 4, 6)).astype(np.float32)    # broadcast
+    ref, absb = oracle.gemm_ref_batched(A, B)
+    assert ref.shape == (3, 5, 6)
+    for z in range(3):
+        r, s = oracle.gemm_ref(A[z], B[0])
+        assert np.array_equal(ref[z], r) and np.array_equal(absb[z], s)
+    # entries are independent: permuting A's stack permutes the results
+    ref2, _ = oracle.gemm_ref_batched(A[::-1].copy(), B)
+    assert np.array_equal(ref2, ref[::-1])
+    with pytest.raises(ValueError):
+        oracle.gemm_ref_batched(A, np.zeros((2, 4, 6), np.float32))
+
+
+def _general_mutants():
+    def transpose_ignored(A, B, ta, tb):
+        a = A if not ta else A.reshape(A.shape[1], A.shape[0])
+        b = B if not tb else B.reshape(B.shape[1], B.shape[0])
+        return oracle.gemm_ref(np.ascontiguousarray(a), np.ascontiguousarray(b))
+
+    def transposes_swapped(A, B, ta, tb):
+        return oracle.gemm_ref(A, B, tb, ta) if A.shape[0] == B.shape[1] else (None, None)
+
+    return [transpose_ignored, transposes_swapped]
+
+
+def test_general_pins_reject_mutants():
+    P, perm = inputs.permutation(37, seed=61)
+    _, B = _rand(37, 37, 37, seed=62)
+    want = B[np.argsort(perm)].astype(np.float64)
+    for m in _general_mutants():
+        ref, _ = m(P, B, True, False)
+        assert ref is None or not np.array_equal(ref, want), m.__name__

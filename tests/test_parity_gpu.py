@@ -303,10 +303,11 @@ def test_query_and_nondefault_stream():
     A, B = inputs.make_operands(640, 480, 320, seed=48)
     Ad, Bd = to_device(A), to_device(B)
     Cd = torch.empty((640, 480), device="cuda")
-    q = sg.sgemm_f32_query(640, 480, 320, Ad.data_ptr(), 320, Bd.data_ptr(), 480, Cd.data_ptr(), 480)
+    q = sg.sgemm_f32_query(0, 0, 640, 480, 320, Ad.data_ptr(), 320, 0, Bd.data_ptr(), 480, 0,
+                           Cd.data_ptr(), 480, 0)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     p = sg.sgemm_f32_plan(640, 480, 320, 320, 480, 480, cus)
-    assert (q.id, q.grid, q.group_m, q.xcd_remap) == (p.id, p.grid, p.group_m, p.xcd_remap)
+    assert (q.id, q.grid, q.group_m, q.xcd_remap, q.splits) == (p.id, p.grid, p.group_m, p.xcd_remap, 1)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
