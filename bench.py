@@ -25,6 +25,12 @@ One JSON line is printed.  Besides the driver's fields it holds:
                 sample of the same product (whole rows of C, about
                 --cpu-seconds of work), in TFLOP/s, with the threads used; the
                 sampled rows are also compared with the GPU result.
+  extras        the library's other paths, each timed the same way after a
+                time-based warm-up (--extra-warm-ms): the small 512^3
+                configuration and the one-tile 128 x 128 x 32768 product with
+                and without a workspace (K split across workgroups), the
+                transposed-operand layouts at 8192^3 and 3072^3, and
+                strided batches of attention-like products.
 """
 import argparse
 import hashlib
@@ -100,6 +106,109 @@ def time_workload(torch, sg, w, steps, warmup, cfg=None):
     }
 
 
+def time_call(torch, fn, steps, warm_ms):
+    """Mean ms per call of fn() over `steps` calls timed with HIP events on the
+    current stream, after at least warm_ms of warm-up calls."""
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    one = max(e0.elapsed_time(e1), 1e-3)
+    for _ in range(max(3, int(warm_ms / one))):
+        fn()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def extras(torch, sg, steps, warm_ms, cus, peak):
+    """Throughput of the split-K, transposed-layout and batched paths."""
+    from fp32_gemm_sgemm_amd import inputs
+    out = []
+    stream = torch.cuda.current_stream()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1234)
+
+    def operand(shape):
+        return torch.rand(shape, device="cuda", generator=gen) * 2 - 1
+
+    def chk(code):
+        if code != 0:
+            raise RuntimeError(f"libsgemm call failed with hipError_t {code}")
+
+    def record(name, flops, ms, plan, **kw):
+        tf = flops / (ms * 1e-3) / 1e12
+        out.append(dict(name=name, value=round(tf, 3), unit="TFLOP/s", ms=round(ms, 5),
+                        frac_of_fp32_matrix_peak=round(tf / peak, 4), variant=plan.id,
+                        tile=f"{plan.bm}x{plan.bn}x{plan.bk}", splits=plan.splits, **kw))
+
+    # K split across workgroups: the small configuration and one tile with long K
+    w = inputs.WORKLOADS["sgemm_512x512x512_uniform_seed0"]
+    A_np, B_np = inputs.workload_operands(w)
+    for name, (A, B) in [("512x512x512 (seed 0)", (torch.from_numpy(A_np).cuda(),
+                                                     torch.from_numpy(B_np).cuda())),
+                         ("128x128x32768", (operand((128, 32768)), operand((32768, 128))))]:
+        M, K = A.shape
+        N = B.shape[1]
+        C = torch.empty((M, N), device="cuda")
+        wsb = sg.sgemm_f32_workspace_size(0, 0, M, N, K, K, N, N, 1)
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+        h = stream.cuda_stream
+        plan_ws = sg.sgemm_f32_plan(M, N, K, K, N, N, cus, 0, 0, 1, wsb)
+        plan_no = sg.sgemm_f32_plan(M, N, K, K, N, N, cus)
+        ms_no = time_call(torch, lambda: chk(sg.sgemm_f32(M, N, K, A.data_ptr(), K, B.data_ptr(), N,
+                                                      C.data_ptr(), N, h)), steps, warm_ms)
+        ms_ws = time_call(torch, lambda: chk(sg.sgemm_f32_gemm(0, 0, M, N, K, 1.0, A.data_ptr(), K,
+                                                           B.data_ptr(), N, 0.0, C.data_ptr(), N,
+                                                           ws.data_ptr(), wsb, h)), steps, warm_ms)
+        flops = 2.0 * M * N * K
+        record(f"{name} sgemm_f32 (no workspace)", flops, ms_no, plan_no)
+        record(f"{name} with workspace", flops, ms_ws, plan_ws, workspace_bytes=wsb,
+               speedup=round(ms_no / ms_ws, 3))
+        del A, B, C, ws
+
+    # transposed operands (loaded as stored)
+    for n in (8192, 3072):
+        for ta, tb in ((1, 0), (0, 1), (1, 1)):
+            A = operand((n, n))
+            B = operand((n, n))
+            C = torch.empty((n, n), device="cuda")
+            plan = sg.sgemm_f32_plan(n, n, n, n, n, n, cus, ta, tb)
+            h = stream.cuda_stream
+            ms = time_call(torch, lambda: chk(sg.sgemm_f32_gemm(ta, tb, n, n, n, 1.0, A.data_ptr(), n,
+                                                            B.data_ptr(), n, 0.0, C.data_ptr(), n,
+                                                            0, 0, h)), steps, warm_ms)
+            lay = ("T" if ta else "N") + ("T" if tb else "N")
+            record(f"{n}^3 {lay}", 2.0 * n ** 3, ms, plan)
+            del A, B, C
+    torch.cuda.empty_cache()
+
+    # strided batches: per-head products of attention (sequence 1024, head 128)
+    for name, batch, M, N, K, ta, tb in [("64 x QK^T 1024x1024x128 NT", 64, 1024, 1024, 128, 0, 1),
+                                         ("64 x PV 1024x128x1024 NN", 64, 1024, 128, 1024, 0, 0)]:
+        A = operand((batch,) + ((K, M) if ta else (M, K)))
+        B = operand((batch,) + ((N, K) if tb else (K, N)))
+        C = torch.empty((batch, M, N), device="cuda")
+        lda, ldb = A.shape[2], B.shape[2]
+        wsb = sg.sgemm_f32_workspace_size(ta, tb, M, N, K, lda, ldb, N, batch)
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+        plan = sg.sgemm_f32_plan(M, N, K, lda, ldb, N, cus, ta, tb, batch, wsb)
+        h = stream.cuda_stream
+        ms = time_call(torch, lambda: chk(sg.sgemm_f32_strided_batched(
+            ta, tb, M, N, K, 1.0, A.data_ptr(), lda, A.stride(0), B.data_ptr(), ldb, B.stride(0),
+            0.0, C.data_ptr(), N, C.stride(0), batch, ws.data_ptr(), wsb, h)), steps, warm_ms)
+        record(name, 2.0 * batch * M * N * K, ms, plan, batch=batch)
+        del A, B, C, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w, A_np, B_np, C_gpu, seconds):
     """The CPU reference on whole rows of the same product, about `seconds` of
     work; its rows are also checked against the GPU result."""
@@ -142,6 +251,9 @@ def main(argv=None):
     ap.add_argument("--variant", type=int, default=-1, help="force a compiled variant id")
     ap.add_argument("--group-m", type=int, default=8)
     ap.add_argument("--xcd-remap", type=int, default=1)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the split-K, transposed-layout and batched measurements")
+    ap.add_argument("--extra-warm-ms", type=float, default=150.0)
     ap.add_argument("--no-probe", action="store_true",
                     help="skip the MFMA-peak probe (the measured matrix-core ceiling)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -245,6 +357,9 @@ def main(argv=None):
             "warmup": warm2,
         }
         del r2
+
+    if not args.no_extras:
+        result["extras"] = extras(torch, sg, args.steps, args.extra_warm_ms, cus, peak)
 
     if not args.no_probe:
         from fp32_gemm_sgemm_amd import probes

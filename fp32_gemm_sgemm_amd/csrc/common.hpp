@@ -112,6 +112,8 @@ template <int W>
 __device__ __forceinline__ void store_row(float *p, int col, int N, const float (&v)[W],
                                           float alpha, float beta)
 {
+    // (no 3-wide vector: 3-element vector stores may be widened to 4)
+    static_assert(W == 1 || W == 2 || W == 4, "1, 2 or 4 adjacent results");
     if constexpr (W > 1) {
         if (col + W - 1 < N) {
             typedef float vec_t __attribute__((ext_vector_type(W), aligned(4)));

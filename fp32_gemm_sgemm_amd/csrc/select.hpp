@@ -32,6 +32,8 @@ struct Variant {
     const void *fn[4];  // kernel per operand layout, index transa + 2*transb (null: none)
     int eff_permille;   // measured steady-state fraction of the FP32 matrix peak
                         // (x1000) on full tiles; 0 = never chosen by the selector
+    int eff_unaligned_permille;  // the same when rows are not 16-byte aligned
+                                 // (every slice fetched through registers)
 };
 
 // One call as the planner sees it.
@@ -157,18 +159,20 @@ constexpr double kCuFlopPerNs = 157.3e3 / 256.0;
 // Fixed cost of one tile (prologue fetch, pipeline fill, epilogue stores).
 constexpr double kTileFixedNs = 2500.0;
 // The reduction pass: start-up of the second launch, and the rate at which
-// it streams partials (mostly from L2 and MALL) and writes C.
+// it streams the partials and writes C (measured 3-5 us and about 5 TB/s).
 constexpr double kReduceFixedNs = 3000.0;
-constexpr double kReduceBytesPerNs = 3000.0;
+constexpr double kReduceBytesPerNs = 5000.0;
 
-inline double estimate_ns(const Variant &v, const Problem &p, int splits, int k_chunk, int cus)
+inline double estimate_ns(const Variant &v, const Problem &p, int splits, int k_chunk, int cus,
+                          bool aligned)
 {
     const long long tiles = ceil_div_ll(p.M, v.bm) * ceil_div_ll(p.N, v.bn) * splits * (long long)p.batch;
     const long long rounds = ceil_div_ll(tiles, cus);
     const int kc = splits > 1 ? k_chunk : p.K;
     long long slices = ceil_div_ll(kc, v.bk);
     if (v.stages == 0 && v.stage_at >= 0) slices += slices & 1;  // register pipeline takes pairs
-    const double slice_ns = 2.0 * v.bm * v.bn * v.bk / (kCuFlopPerNs * v.eff_permille / 1000.0);
+    const int eff = aligned ? v.eff_permille : v.eff_unaligned_permille;
+    const double slice_ns = 2.0 * v.bm * v.bn * v.bk / (kCuFlopPerNs * eff / 1000.0);
     double t = (double)rounds * (kTileFixedNs + (double)slices * slice_ns);
     if (splits > 1)
         t += kReduceFixedNs +
@@ -199,7 +203,9 @@ inline Choice select_plan(const Variant *vs, int n, const Problem &p, int cus, b
     for (int pass = 0; pass < 2 && best.id < 0; ++pass) {
         for (int i = 0; i < n; ++i) {
             const Variant &v = vs[i];
-            if (v.kernel != SGEMM_KERNEL_MFMA || v.eff_permille <= 0 || !v.fn[op]) continue;
+            if (v.kernel != SGEMM_KERNEL_MFMA || v.eff_permille <= 0 || v.eff_unaligned_permille <= 0 ||
+                !v.fn[op])
+                continue;
             if (pass == 0 && v.stages > 0 && !direct_ok) continue;
             int last = 0;
             for (int want : kSplitCandidates) {
@@ -210,7 +216,7 @@ inline Choice select_plan(const Variant *vs, int n, const Problem &p, int cus, b
                 if (split_workspace_bytes(p, splits) > workspace_bytes) break;
                 const long long grid = ceil_div_ll(p.M, v.bm) * ceil_div_ll(p.N, v.bn) * splits * (long long)p.batch;
                 if (grid > INT_MAX) break;
-                const double t = estimate_ns(v, p, splits, k_chunk, cus);
+                const double t = estimate_ns(v, p, splits, k_chunk, cus, direct_ok);
                 if (best.id < 0 || t < best_t) {
                     best = {i, splits};
                     best_t = t;

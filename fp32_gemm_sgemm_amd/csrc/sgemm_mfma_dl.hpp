@@ -45,9 +45,17 @@ template <int BK> __device__ __forceinline__ int chunk_swizzle(int r)
     else return (r ^ ((r >> 3) & 1)) & 7;
 }
 
+// Three adjacent floats with 4-byte alignment (the compiler picks the LDS
+// read instructions that this alignment allows).
+struct DlF3 {
+    float x[3];
+    __device__ __forceinline__ float operator[](int i) const { return x[i]; }
+};
+
 template <int W> struct DlVec;
 template <> struct DlVec<1> { typedef float T; };
 template <> struct DlVec<2> { typedef f32x2 T; };
+template <> struct DlVec<3> { typedef DlF3 T; };
 template <> struct DlVec<4> { typedef f32x4 T; };
 
 // Fragment vector of an index-contiguous operand (unused, and a plain float,
@@ -82,7 +90,7 @@ struct DlOperand {
     static constexpr int LOADS = E * BK / 4 / (NW * 64);  // per thread per slice
     static constexpr int FLOATS = E * BK;
     static_assert(WT % 32 == 0 && W >= 1, "wave tiles must be multiples of 32");
-    static_assert(KC || W == 1 || W == 2 || W == 4, "index-contiguous fragments are 1, 2 or 4 wide");
+    static_assert(KC || (W >= 1 && W <= 4), "index-contiguous fragments are 1 to 4 wide");
     static_assert(LOADS * NW * 64 * 4 == E * BK, "slices must split into whole 1 KB blocks per wave");
 
     // Fetch assignment of load j: byte offset from the slice's base (the
