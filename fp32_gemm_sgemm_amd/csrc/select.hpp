@@ -31,9 +31,11 @@ struct Variant {
     int lds_bytes;
     const void *fn[4];  // kernel per operand layout, index transa + 2*transb (null: none)
     int eff_permille;   // measured steady-state fraction of the FP32 matrix peak
-                        // (x1000) on full tiles; 0 = never chosen by the selector
-    int eff_unaligned_permille;  // the same when rows are not 16-byte aligned
-                                 // (every slice fetched through registers)
+                        // (x1000) over rounds of full tiles; 0 = never chosen by the selector
+    int eff_one_permille;        // the same when the grid has at most one workgroup
+                                 // per CU (no co-resident workgroups to hide latency)
+    int eff_unaligned_permille;  // the same as eff_permille when rows are not
+                                 // 16-byte aligned (every slice fetched through registers)
 };
 
 // One call as the planner sees it.
@@ -171,7 +173,8 @@ inline double estimate_ns(const Variant &v, const Problem &p, int splits, int k_
     const int kc = splits > 1 ? k_chunk : p.K;
     long long slices = ceil_div_ll(kc, v.bk);
     if (v.stages == 0 && v.stage_at >= 0) slices += slices & 1;  // register pipeline takes pairs
-    const int eff = aligned ? v.eff_permille : v.eff_unaligned_permille;
+    double eff = aligned ? v.eff_permille : v.eff_unaligned_permille;
+    if (tiles <= cus) eff = eff * v.eff_one_permille / v.eff_permille;
     const double slice_ns = 2.0 * v.bm * v.bn * v.bk / (kCuFlopPerNs * eff / 1000.0);
     double t = (double)rounds * (kTileFixedNs + (double)slices * slice_ns);
     if (splits > 1)
@@ -203,8 +206,8 @@ inline Choice select_plan(const Variant *vs, int n, const Problem &p, int cus, b
     for (int pass = 0; pass < 2 && best.id < 0; ++pass) {
         for (int i = 0; i < n; ++i) {
             const Variant &v = vs[i];
-            if (v.kernel != SGEMM_KERNEL_MFMA || v.eff_permille <= 0 || v.eff_unaligned_permille <= 0 ||
-                !v.fn[op])
+            if (v.kernel != SGEMM_KERNEL_MFMA || v.eff_permille <= 0 || v.eff_one_permille <= 0 ||
+                v.eff_unaligned_permille <= 0 || !v.fn[op])
                 continue;
             if (pass == 0 && v.stages > 0 && !direct_ok) continue;
             int last = 0;

@@ -27,7 +27,7 @@ using sgemm::Problem;
 using sgemm::Variant;
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGE_AT>
-Variant mfma_variant(int eff_permille, int eff_unaligned_permille)
+Variant mfma_variant(int eff_permille, int eff_one_permille, int eff_unaligned_permille)
 {
     typedef sgemm::MfmaTraits<BM, BN, BK, WM, WN, STAGE_AT> T;
     return Variant{SGEMM_KERNEL_MFMA, BM, BN, BK, WM, WN, STAGE_AT, 0,
@@ -35,17 +35,18 @@ Variant mfma_variant(int eff_permille, int eff_unaligned_permille)
                    {reinterpret_cast<const void *>(
                         &sgemm::sgemm_mfma_kernel<BM, BN, BK, WM, WN, STAGE_AT>),
                     nullptr, nullptr, nullptr},
-                   eff_permille, eff_unaligned_permille};
+                   eff_permille, eff_one_permille, eff_unaligned_permille};
 }
 
 // OPS: bit (transa + 2*transb) set for each operand layout to compile.
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int OPS>
-Variant dl_variant(int eff_permille, int eff_unaligned_permille)
+Variant dl_variant(int eff_permille, int eff_one_permille, int eff_unaligned_permille)
 {
     typedef sgemm::DlTraits<BM, BN, BK, WM, WN, STAGES, false, false> T;
     Variant v{SGEMM_KERNEL_MFMA, BM, BN, BK, WM, WN, -1, STAGES,
               T::NT, (int)(T::LDS_FLOATS * sizeof(float)),
-              {nullptr, nullptr, nullptr, nullptr}, eff_permille, eff_unaligned_permille};
+              {nullptr, nullptr, nullptr, nullptr}, eff_permille, eff_one_permille,
+              eff_unaligned_permille};
     v.fn[0] = reinterpret_cast<const void *>(
         &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, false, false>);
     if constexpr ((OPS & 2) != 0)
@@ -67,35 +68,39 @@ Variant valu_variant()
                    T::NT, (int)(T::LDS_FLOATS * sizeof(float)),
                    {reinterpret_cast<const void *>(&sgemm::sgemm_valu_kernel),
                     nullptr, nullptr, nullptr},
-                   0, 0};
+                   0, 0, 0};
 }
 
 constexpr int kAllOps = 0xf;
 
 // The compiled variants.  Indices are part of the ABI of sgemm_f32_ex.  The
-// two last arguments are the fractions of the FP32 matrix peak (x1000) the
-// variant sustains per round of full tiles on MI355X, which the selector's
-// cost model uses: with 16-byte aligned rows (measured at 8192^3 for the
-// 256 x 256 and 128 x 128 tiles, at 3072^3, one 192 x 192 tile per CU, for
-// the 192 x 192 tiles) and with unaligned rows (measured at 4099^3; 0.85 of
-// the aligned figure where not measured).  0 keeps a variant out of
-// automatic selection (comparison kernels, dominated tiles).
+// three last arguments are fractions of the FP32 matrix peak (x1000) the
+// variant sustains on MI355X, which the selector's cost model uses: over
+// rounds of full tiles with 16-byte aligned rows (measured at 8192^3; at
+// 3072^3, one tile per CU, for the 192 x 192 tiles), with at most one
+// workgroup per CU (measured at 2048^3 and 1024 x 1024 x 8192 split 4 ways),
+// and with unaligned rows (measured at 4099^3; 0.85 of the aligned figure
+// where not measured).  0 keeps a variant out of automatic selection
+// (comparison kernels, dominated tiles).
 const Variant kVariants[] = {
-    mfma_variant<256, 256, 16, 4, 2, 0>(894, 760),      // 0: 8 waves of 64x128
-    mfma_variant<128, 128, 16, 2, 2, 0>(861, 781),      // 1: 4 waves of 64x64
-    mfma_variant<128, 128, 32, 2, 2, 1>(0, 0),          // 2: 4 waves of 64x64, BK 32
-    mfma_variant<128, 256, 16, 2, 2, 0>(0, 0),          // 3: 4 waves of 64x128
-    mfma_variant<256, 128, 16, 4, 1, 0>(0, 0),          // 4: 4 waves of 64x128
-    mfma_variant<256, 256, 16, 4, 2, -1>(0, 0),         // 5: plain order (comparison)
-    mfma_variant<128, 128, 16, 2, 2, -1>(0, 0),         // 6: plain order (comparison)
-    valu_variant(),                                     // 7: vector-FMA comparison
-    mfma_variant<192, 192, 16, 2, 6, 0>(0, 0),          // 8: 12 waves of 96x32
-    mfma_variant<192, 192, 32, 2, 6, 1>(869, 730),      // 9: 12 waves of 96x32, BK 32
-    dl_variant<256, 256, 16, 4, 2, 4, 1>(0, 0),         // 10: direct loads, 4 stages
-    dl_variant<256, 256, 32, 4, 2, 2, kAllOps>(912, 737),  // 11: direct loads, 2 stages of BK 32
-    dl_variant<128, 128, 32, 2, 2, 3, kAllOps>(775, 466),  // 12: direct loads
-    dl_variant<192, 192, 32, 2, 6, 3, kAllOps>(854, 708),  // 13: direct loads
-    dl_variant<256, 256, 16, 4, 2, 3, 1>(0, 0),         // 14: direct loads, 3 stages
+    mfma_variant<256, 256, 16, 4, 2, 0>(894, 894, 760),    // 0: 8 waves of 64x128
+    mfma_variant<128, 128, 16, 2, 2, 0>(886, 760, 781),    // 1: 4 waves of 64x64
+    mfma_variant<128, 128, 32, 2, 2, 1>(0, 0, 0),          // 2: 4 waves of 64x64, BK 32
+    mfma_variant<128, 256, 16, 2, 2, 0>(0, 0, 0),          // 3: 4 waves of 64x128
+    mfma_variant<256, 128, 16, 4, 1, 0>(0, 0, 0),          // 4: 4 waves of 64x128
+    mfma_variant<256, 256, 16, 4, 2, -1>(0, 0, 0),         // 5: plain order (comparison)
+    mfma_variant<128, 128, 16, 2, 2, -1>(0, 0, 0),         // 6: plain order (comparison)
+    valu_variant(),                                        // 7: vector-FMA comparison
+    mfma_variant<192, 192, 16, 2, 6, 0>(0, 0, 0),          // 8: 12 waves of 96x32
+    mfma_variant<192, 192, 32, 2, 6, 1>(869, 869, 730),    // 9: 12 waves of 96x32, BK 32
+    dl_variant<256, 256, 16, 4, 2, 4, 1>(0, 0, 0),         // 10: direct loads, 4 stages
+    dl_variant<256, 256, 32, 4, 2, 2, kAllOps>(920, 911, 737),  // 11: direct loads, 2 stages of BK 32
+    dl_variant<128, 128, 32, 2, 2, 3, kAllOps>(782, 754, 466),  // 12: direct loads
+    dl_variant<192, 192, 32, 2, 6, 3, kAllOps>(872, 872, 708),  // 13: direct loads
+    dl_variant<256, 256, 16, 4, 2, 3, 1>(0, 0, 0),         // 14: direct loads, 3 stages
+    dl_variant<128, 128, 32, 2, 4, 3, kAllOps>(820, 790, 521),  // 15: direct loads, 8 waves of 64x32
+    mfma_variant<128, 128, 16, 2, 4, 0>(839, 820, 764),    // 16: 8 waves of 64x32
+    mfma_variant<128, 128, 32, 2, 4, 1>(857, 787, 790),    // 17: 8 waves of 64x32, BK 32
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
