@@ -25,6 +25,10 @@ One JSON line is printed.  Besides the driver's fields it holds:
                 sample of the same product (whole rows of C, about
                 --cpu-seconds of work), in TFLOP/s, with the threads used; the
                 sampled rows are also compared with the GPU result.
+  configs       every configuration of the measured workload set through
+                sgemm_f32 (the plain C ABI, no workspace): 512^3, 2048^3 (and
+                its identity-A run), 3072^3, 8192x8192x4096, 4096x4096x8192,
+                the ragged 4099^3 and 8192^3, each after a time-based warm-up.
   extras        the library's other paths, each timed the same way after a
                 time-based warm-up (--extra-warm-ms): the small 512^3
                 configuration and the one-tile 128 x 128 x 32768 product with
@@ -125,6 +129,48 @@ def time_call(torch, fn, steps, warm_ms):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
+
+
+CONFIG_WORKLOADS = [
+    "sgemm_512x512x512_uniform_seed0",
+    "sgemm_2048x2048x2048_uniform_seed1",
+    "sgemm_2048x2048x2048_identityA_seed1",
+    "sgemm_3072x3072x3072_normal_seed2",
+    "sgemm_8192x8192x4096_uniform_seed3",
+    "sgemm_4096x4096x8192_uniform_seed3",
+    "sgemm_4099x4099x4099_uniform_seed3",
+    "sgemm_8192x8192x8192_uniform_seed4",
+]
+
+
+def configs(torch, sg, steps, warm_ms, cus, peak):
+    """TFLOP/s of each workload configuration through sgemm_f32."""
+    from fp32_gemm_sgemm_amd import inputs
+    out = []
+    stream = torch.cuda.current_stream()
+    for name in CONFIG_WORKLOADS:
+        w = inputs.WORKLOADS[name]
+        A_np, B_np = inputs.workload_operands(w)
+        A = torch.from_numpy(A_np).to("cuda")
+        B = torch.from_numpy(B_np).to("cuda")
+        del A_np, B_np
+        C = torch.empty((w.M, w.N), device="cuda")
+        h = stream.cuda_stream
+
+        def call():
+            code = sg.sgemm_f32(w.M, w.N, w.K, A.data_ptr(), w.K, B.data_ptr(), w.N,
+                                C.data_ptr(), w.N, h)
+            if code != 0:
+                raise RuntimeError(f"sgemm_f32 failed with hipError_t {code}")
+        ms = time_call(torch, call, steps, warm_ms)
+        plan = sg.sgemm_f32_plan(w.M, w.N, w.K, w.K, w.N, w.N, cus)
+        tf = w.flops / (ms * 1e-3) / 1e12
+        out.append(dict(workload=name, value=round(tf, 3), unit="TFLOP/s", ms=round(ms, 5),
+                        frac_of_fp32_matrix_peak=round(tf / peak, 4), variant=plan.id,
+                        tile=f"{plan.bm}x{plan.bn}x{plan.bk}"))
+        del A, B, C
+    torch.cuda.empty_cache()
+    return out
 
 
 def extras(torch, sg, steps, warm_ms, cus, peak):
@@ -251,6 +297,8 @@ def main(argv=None):
     ap.add_argument("--variant", type=int, default=-1, help="force a compiled variant id")
     ap.add_argument("--group-m", type=int, default=8)
     ap.add_argument("--xcd-remap", type=int, default=1)
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip timing every workload configuration")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the split-K, transposed-layout and batched measurements")
     ap.add_argument("--extra-warm-ms", type=float, default=150.0)
@@ -358,6 +406,8 @@ def main(argv=None):
         }
         del r2
 
+    if not args.no_configs:
+        result["configs"] = configs(torch, sg, args.steps, args.extra_warm_ms, cus, peak)
     if not args.no_extras:
         result["extras"] = extras(torch, sg, args.steps, args.extra_warm_ms, cus, peak)
 

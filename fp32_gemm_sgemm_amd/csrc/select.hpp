@@ -27,6 +27,7 @@ struct Variant {
     int waves_m, waves_n;
     int stage_at;      // register-staged kernel: LDS write after this k group
     int stages;        // direct-load kernel: LDS stages (0 = register-staged kernel)
+    int dword;         // direct-load kernel with 4-byte loads (for rows not 16-byte aligned)
     int threads;
     int lds_bytes;
     const void *fn[4];  // kernel per operand layout, index transa + 2*transb (null: none)
@@ -165,17 +166,18 @@ constexpr double kTileFixedNs = 2500.0;
 constexpr double kReduceFixedNs = 3000.0;
 constexpr double kReduceBytesPerNs = 5000.0;
 
+// eff: the variant's fraction of peak (x1000) for this call's alignment.
 inline double estimate_ns(const Variant &v, const Problem &p, int splits, int k_chunk, int cus,
-                          bool aligned)
+                          int eff)
 {
     const long long tiles = ceil_div_ll(p.M, v.bm) * ceil_div_ll(p.N, v.bn) * splits * (long long)p.batch;
     const long long rounds = ceil_div_ll(tiles, cus);
     const int kc = splits > 1 ? k_chunk : p.K;
     long long slices = ceil_div_ll(kc, v.bk);
     if (v.stages == 0 && v.stage_at >= 0) slices += slices & 1;  // register pipeline takes pairs
-    double eff = aligned ? v.eff_permille : v.eff_unaligned_permille;
-    if (tiles <= cus) eff = eff * v.eff_one_permille / v.eff_permille;
-    const double slice_ns = 2.0 * v.bm * v.bn * v.bk / (kCuFlopPerNs * eff / 1000.0);
+    double e = eff;
+    if (tiles <= cus) e = e * v.eff_one_permille / v.eff_permille;
+    const double slice_ns = 2.0 * v.bm * v.bn * v.bk / (kCuFlopPerNs * e / 1000.0);
     double t = (double)rounds * (kTileFixedNs + (double)slices * slice_ns);
     if (splits > 1)
         t += kReduceFixedNs +
@@ -191,14 +193,28 @@ struct Choice {
 // Candidate split counts tried by the selector.
 constexpr int kSplitCandidates[] = {1, 2, 3, 4, 5, 6, 8, 10, 12, 16, 20, 24, 32, 48, 64};
 
+// The efficiency (x1000) variant v is expected to reach on this call, or 0 if
+// it does not apply.  aligned16: rows start 16-byte aligned; lds_ok: the
+// leading dimensions allow direct-load offsets.  Strict (first pass): 16-byte
+// direct-load variants only on aligned rows, 4-byte ones only on unaligned
+// rows; otherwise (second pass) any variant, fetching through registers where
+// direct loads do not apply.
+inline int variant_eff(const Variant &v, bool aligned16, bool lds_ok, bool strict)
+{
+    if (v.stages == 0) return aligned16 ? v.eff_permille : v.eff_unaligned_permille;
+    if (v.dword) {
+        if (strict && (aligned16 || !lds_ok)) return 0;
+        return v.eff_unaligned_permille;
+    }
+    if (strict && !(aligned16 && lds_ok)) return 0;
+    return aligned16 && lds_ok ? v.eff_permille : v.eff_unaligned_permille;
+}
+
 // The fastest (variant, split count) by the cost model among the variants
 // compiled for the operand layout whose workspace fits in `workspace_bytes`.
-// direct_ok: the operands allow direct global -> LDS loads; otherwise a
-// direct-load variant would fetch every slice through registers and is used
-// only when nothing else is compiled for the layout.  Returns id -1 if no
-// variant serves the layout.
-inline Choice select_plan(const Variant *vs, int n, const Problem &p, int cus, bool direct_ok,
-                          long long workspace_bytes)
+// Returns id -1 if no variant serves the layout.
+inline Choice select_plan(const Variant *vs, int n, const Problem &p, int cus, bool aligned16,
+                          bool lds_ok, long long workspace_bytes)
 {
     const int op = op_index(p);
     Choice best = {-1, 1};
@@ -209,7 +225,8 @@ inline Choice select_plan(const Variant *vs, int n, const Problem &p, int cus, b
             if (v.kernel != SGEMM_KERNEL_MFMA || v.eff_permille <= 0 || v.eff_one_permille <= 0 ||
                 v.eff_unaligned_permille <= 0 || !v.fn[op])
                 continue;
-            if (pass == 0 && v.stages > 0 && !direct_ok) continue;
+            const int eff = variant_eff(v, aligned16, lds_ok, pass == 0);
+            if (eff <= 0) continue;
             int last = 0;
             for (int want : kSplitCandidates) {
                 int splits, k_chunk;
@@ -219,7 +236,7 @@ inline Choice select_plan(const Variant *vs, int n, const Problem &p, int cus, b
                 if (split_workspace_bytes(p, splits) > workspace_bytes) break;
                 const long long grid = ceil_div_ll(p.M, v.bm) * ceil_div_ll(p.N, v.bn) * splits * (long long)p.batch;
                 if (grid > INT_MAX) break;
-                const double t = estimate_ns(v, p, splits, k_chunk, cus, direct_ok);
+                const double t = estimate_ns(v, p, splits, k_chunk, cus, eff);
                 if (best.id < 0 || t < best_t) {
                     best = {i, splits};
                     best_t = t;

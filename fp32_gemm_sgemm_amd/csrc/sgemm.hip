@@ -30,7 +30,7 @@ template <int BM, int BN, int BK, int WM, int WN, int STAGE_AT>
 Variant mfma_variant(int eff_permille, int eff_one_permille, int eff_unaligned_permille)
 {
     typedef sgemm::MfmaTraits<BM, BN, BK, WM, WN, STAGE_AT> T;
-    return Variant{SGEMM_KERNEL_MFMA, BM, BN, BK, WM, WN, STAGE_AT, 0,
+    return Variant{SGEMM_KERNEL_MFMA, BM, BN, BK, WM, WN, STAGE_AT, 0, 0,
                    T::NT, (int)(T::LDS_FLOATS * sizeof(float)),
                    {reinterpret_cast<const void *>(
                         &sgemm::sgemm_mfma_kernel<BM, BN, BK, WM, WN, STAGE_AT>),
@@ -38,33 +38,34 @@ Variant mfma_variant(int eff_permille, int eff_one_permille, int eff_unaligned_p
                    eff_permille, eff_one_permille, eff_unaligned_permille};
 }
 
-// OPS: bit (transa + 2*transb) set for each operand layout to compile.
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, int OPS>
+// OPS: bit (transa + 2*transb) set for each operand layout to compile.  DW:
+// 4-byte direct loads (rows need only be 4-byte aligned).
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int OPS, bool DW = false>
 Variant dl_variant(int eff_permille, int eff_one_permille, int eff_unaligned_permille)
 {
-    typedef sgemm::DlTraits<BM, BN, BK, WM, WN, STAGES, false, false> T;
-    Variant v{SGEMM_KERNEL_MFMA, BM, BN, BK, WM, WN, -1, STAGES,
+    typedef sgemm::DlTraits<BM, BN, BK, WM, WN, STAGES, false, false, DW> T;
+    Variant v{SGEMM_KERNEL_MFMA, BM, BN, BK, WM, WN, -1, STAGES, DW ? 1 : 0,
               T::NT, (int)(T::LDS_FLOATS * sizeof(float)),
               {nullptr, nullptr, nullptr, nullptr}, eff_permille, eff_one_permille,
               eff_unaligned_permille};
     v.fn[0] = reinterpret_cast<const void *>(
-        &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, false, false>);
+        &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, false, false, DW>);
     if constexpr ((OPS & 2) != 0)
         v.fn[1] = reinterpret_cast<const void *>(
-            &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, true, false>);
+            &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, true, false, DW>);
     if constexpr ((OPS & 4) != 0)
         v.fn[2] = reinterpret_cast<const void *>(
-            &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, false, true>);
+            &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, false, true, DW>);
     if constexpr ((OPS & 8) != 0)
         v.fn[3] = reinterpret_cast<const void *>(
-            &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, true, true>);
+            &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, true, true, DW>);
     return v;
 }
 
 Variant valu_variant()
 {
     typedef sgemm::ValuTraits T;
-    return Variant{SGEMM_KERNEL_VALU, T::BM, T::BN, T::BK, 1, 1, -1, 0,
+    return Variant{SGEMM_KERNEL_VALU, T::BM, T::BN, T::BK, 1, 1, -1, 0, 0,
                    T::NT, (int)(T::LDS_FLOATS * sizeof(float)),
                    {reinterpret_cast<const void *>(&sgemm::sgemm_valu_kernel),
                     nullptr, nullptr, nullptr},
@@ -80,8 +81,9 @@ constexpr int kAllOps = 0xf;
 // 3072^3, one tile per CU, for the 192 x 192 tiles), with at most one
 // workgroup per CU (measured at 2048^3 and 1024 x 1024 x 8192 split 4 ways),
 // and with unaligned rows (measured at 4099^3; 0.85 of the aligned figure
-// where not measured).  0 keeps a variant out of automatic selection
-// (comparison kernels, dominated tiles).
+// where not measured).  The 4-byte direct-load variant serves only rows that
+// are not 16-byte aligned (measured at 4099^3 and 2051^3).  0 keeps a variant
+// out of automatic selection (comparison kernels, dominated tiles).
 const Variant kVariants[] = {
     mfma_variant<256, 256, 16, 4, 2, 0>(894, 894, 760),    // 0: 8 waves of 64x128
     mfma_variant<128, 128, 16, 2, 2, 0>(886, 760, 781),    // 1: 4 waves of 64x64
@@ -101,6 +103,7 @@ const Variant kVariants[] = {
     dl_variant<128, 128, 32, 2, 4, 3, kAllOps>(820, 790, 521),  // 15: direct loads, 8 waves of 64x32
     mfma_variant<128, 128, 16, 2, 4, 0>(839, 820, 764),    // 16: 8 waves of 64x32
     mfma_variant<128, 128, 32, 2, 4, 1>(857, 787, 790),    // 17: 8 waves of 64x32, BK 32
+    dl_variant<192, 192, 32, 2, 6, 3, kAllOps, true>(852, 840, 852),  // 18: 4-byte direct loads
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -189,14 +192,20 @@ hipError_t validate(const Call &c)
     return hipSuccess;
 }
 
-// Direct global -> LDS loads need every batch entry's rows to start 16-byte
-// aligned (a null pointer stands for an aligned start: used by plan).
-bool direct_loads_ok(const Call &c)
+// Rows start 16-byte aligned in every batch entry (a null pointer stands for
+// an aligned start: used by plan).  16-byte direct global -> LDS loads need
+// this and the leading-dimension limits of sgemm::direct_lds_ok; 4-byte ones
+// need only the limits.
+bool rows_aligned16(const Call &c)
 {
     const uintptr_t a = (uintptr_t)c.A, b = (uintptr_t)c.B;
-    const bool al = ((a | b) & 15u) == 0 && c.p.lda % 4 == 0 && c.p.ldb % 4 == 0 &&
-                    (c.p.batch <= 1 || (c.sa % 4 == 0 && c.sb % 4 == 0));
-    return al && sgemm::direct_lds_ok(c.p);
+    return ((a | b) & 15u) == 0 && c.p.lda % 4 == 0 && c.p.ldb % 4 == 0 &&
+           (c.p.batch <= 1 || (c.sa % 4 == 0 && c.sb % 4 == 0));
+}
+
+bool direct_loads_ok(const Variant &v, const Call &c)
+{
+    return sgemm::direct_lds_ok(c.p) && (v.dword || rows_aligned16(c));
 }
 
 // Workgroups per launch: the dispatch packet counts work-items in 32 bits.
@@ -222,7 +231,7 @@ hipError_t launch_gemm(const Variant &v, const sgemm_cfg &cfg, const Call &c, hi
     g.tiles_n = cfg.tiles_n;
     g.group_m = cfg.group_m;
     g.xcd_remap = cfg.xcd_remap;
-    g.direct = direct_loads_ok(c) ? 1 : 0;
+    g.direct = direct_loads_ok(v, c) ? 1 : 0;
     const long long ldp = sgemm::partial_ld(p.N);
     if (cfg.splits > 1) {
         // partials: [batch][split][M][ldp] in the workspace
@@ -289,7 +298,7 @@ int plan_for(const Call &c, int cus, sgemm_cfg *out)
     if (!out || !sgemm::sizes_ok(c.p)) return hipErrorInvalidValue;
     const long long ws = c.ws_bytes > (size_t)LLONG_MAX ? LLONG_MAX : (long long)c.ws_bytes;
     const Choice ch = sgemm::select_plan(kVariants, kNumVariants, c.p, cus > 0 ? cus : 256,
-                                         direct_loads_ok(c), ws);
+                                         rows_aligned16(c), sgemm::direct_lds_ok(c.p), ws);
     if (ch.id < 0) return hipErrorInvalidValue;
     return sgemm::finish_cfg(kVariants[ch.id], ch.id, c.p, ch.splits, out) ? hipSuccess
                                                                            : hipErrorInvalidValue;

@@ -1,33 +1,34 @@
 // Single-precision GEMM on CDNA4 matrix cores with direct global -> LDS loads
-// (gfx950 buffer_load_dwordx4 ... lds): the AMD counterpart of the multi-stage
-// asynchronous-copy pipeline of "4.1 CUDA GEMM operator performance
-// optimization", section 10.  Fetched slices land in LDS without passing
-// through registers, so there are no staging registers and no LDS write
-// instructions, and STAGES slices can be in flight.
+// (gfx950 buffer_load_dword[x4] ... lds): the AMD counterpart of the
+// multi-stage asynchronous-copy pipeline of "4.1 CUDA GEMM operator
+// performance optimization", section 10.  Fetched slices land in LDS without
+// passing through registers, so there are no staging registers and no LDS
+// write instructions, and STAGES slices can be in flight.
 //
-// The MFMA part (wave tiles of 32x32 blocks, k permutation, column
-// interleave, fragment ping-pong) is the one of sgemm_mfma.hpp.  What differs is the LDS layout and the fetch:
+// The MFMA part (wave tiles of 32x32 blocks, k permutation, fragment
+// ping-pong) is the one of sgemm_mfma.hpp.  What differs is the LDS layout
+// and the fetch:
 //
-//  * A direct load writes a wave's 64 lanes x 16 bytes to 1 KB of contiguous
-//    LDS (lane l at offset 16*l, checked on the device), so the A slice is
-//    stored without padding: BM rows of BK floats.  To keep the fragment
-//    reads (32 consecutive rows, one 16-byte chunk each) free of bank
-//    conflicts, chunk p of row r is stored at chunk position p ^ f(r), and a
-//    lane fetching position q of its 1 KB block loads the global chunk that
-//    belongs there.  f uses only row bits 0-3, so it is the same for every
-//    32-row block:  BK = 16: f(r) = ((r >> 1) ^ (r >> 2)) & 3;
-//                   BK = 32: f(r) = (r ^ ((r >> 3) & 1)) & 7.
-//    Either makes the 16-byte chunks read by any 8 consecutive lanes fall in
-//    distinct 128-byte bank rows' slots, and those of any 16 consecutive lanes
-//    in distinct slots of 256 bytes.
-//  * B keeps its row-major layout: a 1 KB block is part of one B row.
-//  * Loads go through buffer resources ending at the matrices' last
-//    elements; rows past M (A) or K (B) read as zero, and a chunk wholly past
-//    K (A) or N (B) gets an offset beyond every resource (also zero).  A
-//    slice that holds a partial chunk (K or N not a multiple of 4 at the
-//    edge) is fetched instead through registers (dword loads and a select)
-//    and written to the same swizzled positions.  Operands whose rows are
-//    not 16-byte aligned use the register fetch for every slice.
+//  * A direct load writes a wave's 64 lanes x EL floats to contiguous LDS
+//    (lane l at offset 4*EL*l, checked on the device for EL = 4 and EL = 1),
+//    so operand tiles are stored without padding.  EL = 4 (16-byte loads)
+//    needs rows that start 16-byte aligned; DW kernels use EL = 1 (4-byte
+//    loads), which any row allows, with four times the load instructions.
+//  * Each operand is k-contiguous (A, or a transposed B) or index-contiguous
+//    (B, or a transposed A) and keeps that storage in LDS (DlOperand below).
+//    In a k-contiguous tile, 16-byte chunk p of row r is stored at chunk
+//    position p ^ f(r), which keeps the fragment reads (32 consecutive rows,
+//    one 16-byte chunk each) free of bank conflicts; a lane loads the global
+//    data that belongs at its LDS position.  f uses only row bits 0-3:
+//    BK = 16: f(r) = ((r >> 1) ^ (r >> 2)) & 3;
+//    BK = 32: f(r) = (r ^ ((r >> 3) & 1)) & 7.
+//  * Loads go through buffer resources ending at the operands' last
+//    elements; rows past the end read as zero, and data wholly past K, M or N
+//    gets an offset beyond every resource (also zero).  With 16-byte loads,
+//    a slice that holds a chunk only partly inside the data is fetched
+//    instead through registers (dword loads and a select) into the same
+//    positions, and so is every slice when the rows are not 16-byte aligned
+//    (DW kernels exist for that case).
 //
 // Pipeline, per slice kt: wait for this thread's fetch of slice kt, barrier
 // (every wave's fetch of kt has landed and every wave has finished slice
@@ -83,37 +84,41 @@ __device__ __forceinline__ float dl_elem(const V &v, int b)
 //  XC ("index contiguous": B, or a transposed A): the operand's rows run
 //     along X.  LDS holds BK rows of E floats; a fragment read is one W-wide
 //     read per k: the W blocks' values at one k.
-template <int E, int BK, int WT, int NW, bool KC>
+template <int E, int BK, int WT, int NW, bool KC, bool DW>
 struct DlOperand {
     static constexpr int W = WT / 32;
-    static constexpr int CPR = KC ? BK / 4 : E / 4;    // 16-byte chunks per LDS row
-    static constexpr int LOADS = E * BK / 4 / (NW * 64);  // per thread per slice
+    static constexpr int ELEMS = DW ? 1 : 4;            // floats per lane per load
+    static constexpr int LOADS = E * BK / ELEMS / (NW * 64);  // per thread per slice
     static constexpr int FLOATS = E * BK;
     static_assert(WT % 32 == 0 && W >= 1, "wave tiles must be multiples of 32");
     static_assert(KC || (W >= 1 && W <= 4), "index-contiguous fragments are 1 to 4 wide");
-    static_assert(LOADS * NW * 64 * 4 == E * BK, "slices must split into whole 1 KB blocks per wave");
+    static_assert(LOADS * NW * 64 * ELEMS == E * BK, "slices must split into whole wave loads");
 
     // Fetch assignment of load j: byte offset from the slice's base (the
-    // tile's first index at the slice's first k) and the chunk's first
-    // column along the contiguous dimension (k for KC, the index for XC).
+    // tile's first index at the slice's first k) and the first column of the
+    // lane's data along the contiguous dimension (k for KC, the index for
+    // XC).  The lane's data lands at LDS float (j*NW + wave)*64*ELEMS +
+    // lane*ELEMS of the operand's region.
     __device__ __forceinline__ static void assign(int j, int wave, int lane, int ld,
                                                   uint32_t &off, int &col)
     {
-        const int q = (j * NW + wave) * 64 + lane;
-        const int row = q / CPR;
-        int c = q % CPR;
+        const int q = ((j * NW + wave) * 64 + lane) * ELEMS;  // LDS float position
+        const int rl = KC ? BK : E;                            // floats per LDS row
+        const int row = q / rl;
+        int c = q % rl;
         int r = row;
         if constexpr (KC) {
-            c ^= chunk_swizzle<BK>(row);
+            c = 4 * ((c / 4) ^ chunk_swizzle<BK>(row)) + c % 4;
             const int in = row % WT;
             r = row - in + W * (in % 32) + in / 32;
         }
-        col = 4 * c;
-        off = 4u * ((uint32_t)r * (uint32_t)ld + 4u * (uint32_t)c);
+        col = c;
+        off = 4u * ((uint32_t)r * (uint32_t)ld + (uint32_t)c);
     }
 };
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, bool TA, bool TB>
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, bool TA, bool TB,
+          bool DW = false>
 struct DlTraits {
     static constexpr int NW = WAVES_M * WAVES_N;
     static constexpr int NT = NW * 64;
@@ -121,8 +126,8 @@ struct DlTraits {
     static constexpr int WTN = BN / WAVES_N;
     static constexpr int RM = WTM / 32;
     static constexpr int NB = WTN / 32;
-    typedef DlOperand<BM, BK, WTM, NW, !TA> OpA;
-    typedef DlOperand<BN, BK, WTN, NW, TB> OpB;
+    typedef DlOperand<BM, BK, WTM, NW, !TA, DW> OpA;
+    typedef DlOperand<BN, BK, WTN, NW, TB, DW> OpB;
     static constexpr int A_FLOATS = BM * BK;
     static constexpr int STAGE_FLOATS = BM * BK + BK * BN;
     static constexpr int LDS_FLOATS = STAGES * STAGE_FLOATS;
@@ -136,17 +141,18 @@ struct DlTraits {
 // (resources are clamped below it when direct loads are used).
 constexpr uint32_t kOobOffset = 0x80000000u;
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, bool TA, bool TB>
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, bool TA, bool TB, bool DW>
 __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64)
 sgemm_mfma_dl_kernel(GemmArgs g)
 {
-    typedef DlTraits<BM, BN, BK, WAVES_M, WAVES_N, STAGES, TA, TB> T;
+    typedef DlTraits<BM, BN, BK, WAVES_M, WAVES_N, STAGES, TA, TB, DW> T;
     typedef typename T::OpA OpA;
     typedef typename T::OpB OpB;
     constexpr int NW = T::NW, WTM = T::WTM, WTN = T::WTN, RM = T::RM, NB = T::NB;
     constexpr int A_LOADS = OpA::LOADS, B_LOADS = OpB::LOADS;
     constexpr int STAGE_FLOATS = T::STAGE_FLOATS, A_FLOATS = T::A_FLOATS;
     constexpr int G = BK / 8;
+    constexpr int EL = DW ? 1 : 4;  // floats per lane per load
 
     __shared__ __attribute__((aligned(1024))) float smem[T::LDS_FLOATS];
 
@@ -174,8 +180,8 @@ sgemm_mfma_dl_kernel(GemmArgs g)
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     // ---- fetch assignment ------------------------------------------------------
-    // Load j of this thread fills 16 bytes at LDS chunk (j*NW + wave)*64 + lane
-    // of the operand's region of a stage.
+    // Load j of this thread fills EL floats at LDS float (j*NW + wave)*64*EL +
+    // lane*EL of the operand's region of a stage.
     uint32_t a_off[A_LOADS], b_off[B_LOADS];
     int a_col[A_LOADS], b_col[B_LOADS];
 #pragma unroll
@@ -202,45 +208,56 @@ sgemm_mfma_dl_kernel(GemmArgs g)
                                   : 4 * ((int64_t)(K - 1 - k0) * ldb + (N - n0));
         const int a_lim = TA ? M - m0 : K - k0;
         const int b_lim = TB ? K - k0 : N - n0;
-        const bool partial = ((a_lim & 3) && a_lim < (TA ? BM : BK)) ||
-                             ((b_lim & 3) && b_lim < (TB ? BK : BN));
+        // (16-byte loads: a slice holding a chunk that is only partly inside
+        // the data goes through registers; 4-byte loads are masked one by one)
+        const bool partial = !DW && (((a_lim & 3) && a_lim < (TA ? BM : BK)) ||
+                                     ((b_lim & 3) && b_lim < (TB ? BK : BN)));
         if (g.direct && !partial) {
             const auto ar = make_rsrc(abase, abytes < (int64_t)kOobOffset ? abytes : (int64_t)kOobOffset);
             const auto br = make_rsrc(bbase, bbytes < (int64_t)kOobOffset ? bbytes : (int64_t)kOobOffset);
+            // (the load size must be a literal: one call per size)
 #pragma unroll
-            for (int j = 0; j < A_LOADS; ++j)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    ar, (lds_void *)(smem + s * STAGE_FLOATS + (j * NW + wave) * 256), 16,
-                    (int)(a_col[j] < a_lim ? a_off[j] : kOobOffset), 0, 0, 0);
+            for (int j = 0; j < A_LOADS; ++j) {
+                const int off = (int)(a_col[j] < a_lim ? a_off[j] : kOobOffset);
+                float *dst = smem + s * STAGE_FLOATS + (j * NW + wave) * 64 * EL;
+                if constexpr (DW) __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void *)dst, 4, off, 0, 0, 0);
+                else __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void *)dst, 16, off, 0, 0, 0);
+            }
 #pragma unroll
-            for (int j = 0; j < B_LOADS; ++j)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    br, (lds_void *)(smem + s * STAGE_FLOATS + A_FLOATS + (j * NW + wave) * 256), 16,
-                    (int)(b_col[j] < b_lim ? b_off[j] : kOobOffset), 0, 0, 0);
+            for (int j = 0; j < B_LOADS; ++j) {
+                const int off = (int)(b_col[j] < b_lim ? b_off[j] : kOobOffset);
+                float *dst = smem + s * STAGE_FLOATS + A_FLOATS + (j * NW + wave) * 64 * EL;
+                if constexpr (DW) __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_void *)dst, 4, off, 0, 0, 0);
+                else __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_void *)dst, 16, off, 0, 0, 0);
+            }
         } else {
             const auto ar = make_rsrc(abase, abytes);
             const auto br = make_rsrc(bbase, bbytes);
-            f32x4 va[A_LOADS], vb[B_LOADS];
+            float va[A_LOADS][EL], vb[B_LOADS][EL];
 #pragma unroll
             for (int j = 0; j < A_LOADS; ++j)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
+                for (int e = 0; e < EL; ++e) {
                     const float x = buffer_load_f32(ar, a_off[j] + 4u * e);
                     va[j][e] = (a_col[j] + e < a_lim) ? x : 0.0f;
                 }
 #pragma unroll
             for (int j = 0; j < B_LOADS; ++j)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
+                for (int e = 0; e < EL; ++e) {
                     const float x = buffer_load_f32(br, b_off[j] + 4u * e);
                     vb[j][e] = (b_col[j] + e < b_lim) ? x : 0.0f;
                 }
+            auto put = [&](float *dst, const float (&v)[EL]) {
+                if constexpr (EL == 4) *reinterpret_cast<f32x4 *>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+                else *dst = v[0];
+            };
 #pragma unroll
             for (int j = 0; j < A_LOADS; ++j)
-                *reinterpret_cast<f32x4 *>(smem + s * STAGE_FLOATS + ((j * NW + wave) * 64 + lane) * 4) = va[j];
+                put(smem + s * STAGE_FLOATS + ((j * NW + wave) * 64 + lane) * EL, va[j]);
 #pragma unroll
             for (int j = 0; j < B_LOADS; ++j)
-                *reinterpret_cast<f32x4 *>(smem + s * STAGE_FLOATS + A_FLOATS + ((j * NW + wave) * 64 + lane) * 4) = vb[j];
+                put(smem + s * STAGE_FLOATS + A_FLOATS + ((j * NW + wave) * 64 + lane) * EL, vb[j]);
         }
     };
 

@@ -248,6 +248,16 @@ def test_selector_prefers_full_waves(lib):
     assert p.grid * p.bm * p.bn == 8192 * 8192
 
 
+def test_selector_unaligned_rows(lib):
+    """Rows that are not 16-byte aligned (ld = 4099) cannot take 16-byte
+    direct loads; the 192 x 192 tile with 4-byte direct loads serves them
+    (one launch, no workspace needed), for plain and transposed A."""
+    for ta in (0, 1):
+        p = sg.sgemm_f32_plan(4099, 4099, 4099, 4099, 4099, 4099, 256, ta, 0, 1, 0)
+        assert (p.bm, p.bn, p.splits) == (192, 192, 1)
+        assert sg.sgemm_f32_variant_ops(p.id) & (1 << ta)
+
+
 def test_selector_splits_k_for_few_tiles(lib):
     """With a workspace, a long-K product with few output tiles is split
     across workgroups (one 128 x 128 output is a single tile otherwise); a
