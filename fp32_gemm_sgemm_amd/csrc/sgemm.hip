@@ -81,8 +81,9 @@ constexpr int kAllOps = 0xf;
 // 3072^3, one tile per CU, for the 192 x 192 tiles), with at most one
 // workgroup per CU (measured at 2048^3 and 1024 x 1024 x 8192 split 4 ways),
 // and with unaligned rows (measured at 4099^3; 0.85 of the aligned figure
-// where not measured).  The 4-byte direct-load variant serves only rows that
-// are not 16-byte aligned (measured at 4099^3 and 2051^3).  0 keeps a variant
+// where not measured; 64 x 64 tiles measured at 512^3, 1024^3 and 2048^3).
+// The 4-byte direct-load variants serve only rows that are not 16-byte
+// aligned (measured at 4099^3 and 2051^3).  0 keeps a variant
 // out of automatic selection (comparison kernels, dominated tiles).
 const Variant kVariants[] = {
     mfma_variant<256, 256, 16, 4, 2, 0>(894, 894, 760),    // 0: 8 waves of 64x128
@@ -104,6 +105,9 @@ const Variant kVariants[] = {
     mfma_variant<128, 128, 16, 2, 4, 0>(839, 820, 764),    // 16: 8 waves of 64x32
     mfma_variant<128, 128, 32, 2, 4, 1>(857, 787, 790),    // 17: 8 waves of 64x32, BK 32
     dl_variant<192, 192, 32, 2, 6, 3, kAllOps, true>(852, 840, 852),  // 18: 4-byte direct loads
+    mfma_variant<64, 64, 32, 2, 2, 1>(788, 615, 693),      // 19: 4 waves of 32x32
+    dl_variant<64, 64, 32, 2, 2, 2, kAllOps>(828, 567, 497),  // 20: direct loads, 4 waves of 32x32
+    dl_variant<64, 64, 32, 2, 2, 2, kAllOps, true>(780, 497, 780),  // 21: 4-byte direct loads
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
