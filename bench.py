@@ -383,7 +383,7 @@ def main(argv=None):
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": read_traffic(),
+            "traffic": read_traffic() if w.name == HEADLINE else None,
             "compulsory_bytes": metrics.compulsory_bytes(w.M, w.N, w.K),
             "kernel_source_sha256_16": kernel_source_hash(),
         },
