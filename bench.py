@@ -29,6 +29,8 @@ One JSON line is printed.  Besides the driver's fields it holds:
                 sgemm_f32 (the plain C ABI, no workspace): 512^3, 2048^3 (and
                 its identity-A run), 3072^3, 8192x8192x4096, 4096x4096x8192,
                 the ragged 4099^3 and 8192^3, each after a time-based warm-up.
+  vendor        context only: torch.matmul in float32 (the ROCm BLAS libraries,
+                TF32 disabled) timed the same way at 8192^3 and 3072^3.
   extras        the library's other paths, each timed the same way after a
                 time-based warm-up (--extra-warm-ms): the small 512^3
                 configuration and the one-tile 128 x 128 x 32768 product with
@@ -255,6 +257,23 @@ def extras(torch, sg, steps, warm_ms, cus, peak):
     return out
 
 
+def vendor(torch, steps, warm_ms, peak):
+    """torch.matmul (rocBLAS / hipBLASLt) in float32 on the same shapes, for context."""
+    out = []
+    torch.backends.cuda.matmul.allow_tf32 = False
+    for n in (8192, 3072):
+        A = torch.rand((n, n), device="cuda") * 2 - 1
+        B = torch.rand((n, n), device="cuda") * 2 - 1
+        C = torch.empty((n, n), device="cuda")
+        ms = time_call(torch, lambda: torch.matmul(A, B, out=C), steps, warm_ms)
+        tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+        out.append(dict(shape=f"{n}^3", value=round(tf, 3), unit="TFLOP/s", ms=round(ms, 5),
+                        frac_of_fp32_matrix_peak=round(tf / peak, 4)))
+        del A, B, C
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w, A_np, B_np, C_gpu, seconds):
     """The CPU reference on whole rows of the same product, about `seconds` of
     work; its rows are also checked against the GPU result."""
@@ -299,6 +318,8 @@ def main(argv=None):
     ap.add_argument("--xcd-remap", type=int, default=1)
     ap.add_argument("--no-configs", action="store_true",
                     help="skip timing every workload configuration")
+    ap.add_argument("--no-vendor", action="store_true",
+                    help="skip the torch.matmul context measurement")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the split-K, transposed-layout and batched measurements")
     ap.add_argument("--extra-warm-ms", type=float, default=150.0)
@@ -410,6 +431,8 @@ def main(argv=None):
         result["configs"] = configs(torch, sg, args.steps, args.extra_warm_ms, cus, peak)
     if not args.no_extras:
         result["extras"] = extras(torch, sg, args.steps, args.extra_warm_ms, cus, peak)
+    if not args.no_vendor:
+        result["vendor"] = vendor(torch, args.steps, args.extra_warm_ms, peak)
 
     if not args.no_probe:
         from fp32_gemm_sgemm_amd import probes

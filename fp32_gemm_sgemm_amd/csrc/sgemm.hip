@@ -40,7 +40,8 @@ Variant mfma_variant(int eff_permille, int eff_one_permille, int eff_unaligned_p
 
 // OPS: bit (transa + 2*transb) set for each operand layout to compile.  DW:
 // 4-byte direct loads (rows need only be 4-byte aligned).
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, int OPS, bool DW = false>
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int OPS, bool DW = false,
+          int PIPE = 0>
 Variant dl_variant(int eff_permille, int eff_one_permille, int eff_unaligned_permille)
 {
     typedef sgemm::DlTraits<BM, BN, BK, WM, WN, STAGES, false, false, DW> T;
@@ -49,16 +50,16 @@ Variant dl_variant(int eff_permille, int eff_one_permille, int eff_unaligned_per
               {nullptr, nullptr, nullptr, nullptr}, eff_permille, eff_one_permille,
               eff_unaligned_permille};
     v.fn[0] = reinterpret_cast<const void *>(
-        &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, false, false, DW>);
+        &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, false, false, DW, PIPE>);
     if constexpr ((OPS & 2) != 0)
         v.fn[1] = reinterpret_cast<const void *>(
-            &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, true, false, DW>);
+            &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, true, false, DW, PIPE>);
     if constexpr ((OPS & 4) != 0)
         v.fn[2] = reinterpret_cast<const void *>(
-            &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, false, true, DW>);
+            &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, false, true, DW, PIPE>);
     if constexpr ((OPS & 8) != 0)
         v.fn[3] = reinterpret_cast<const void *>(
-            &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, true, true, DW>);
+            &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, true, true, DW, PIPE>);
     return v;
 }
 
@@ -73,6 +74,8 @@ Variant valu_variant()
 }
 
 constexpr int kAllOps = 0xf;
+// Direct-load main loop: cross-slice pipeline (2) with accumulators in AGPRs (4).
+constexpr int kCrossSliceAgpr = 6;
 
 // The compiled variants.  Indices are part of the ABI of sgemm_f32_ex.  The
 // three last arguments are fractions of the FP32 matrix peak (x1000) the
@@ -97,16 +100,16 @@ const Variant kVariants[] = {
     mfma_variant<192, 192, 16, 2, 6, 0>(0, 0, 0),          // 8: 12 waves of 96x32
     mfma_variant<192, 192, 32, 2, 6, 1>(869, 869, 730),    // 9: 12 waves of 96x32, BK 32
     dl_variant<256, 256, 16, 4, 2, 4, 1>(0, 0, 0),         // 10: direct loads, 4 stages
-    dl_variant<256, 256, 32, 4, 2, 2, kAllOps>(920, 911, 737),  // 11: direct loads, 2 stages of BK 32
-    dl_variant<128, 128, 32, 2, 2, 3, kAllOps>(782, 754, 466),  // 12: direct loads
-    dl_variant<192, 192, 32, 2, 6, 3, kAllOps>(872, 872, 708),  // 13: direct loads
+    dl_variant<256, 256, 32, 4, 2, 2, kAllOps, false, kCrossSliceAgpr>(928, 918, 660),  // 11: direct loads, 2 stages of BK 32
+    dl_variant<128, 128, 32, 2, 2, 3, kAllOps>(782, 754, 397),  // 12: direct loads
+    dl_variant<192, 192, 32, 2, 6, 3, kAllOps>(872, 872, 615),  // 13: direct loads
     dl_variant<256, 256, 16, 4, 2, 3, 1>(0, 0, 0),         // 14: direct loads, 3 stages
-    dl_variant<128, 128, 32, 2, 4, 3, kAllOps>(820, 790, 521),  // 15: direct loads, 8 waves of 64x32
+    dl_variant<128, 128, 32, 2, 4, 3, kAllOps>(820, 790, 492),  // 15: direct loads, 8 waves of 64x32
     mfma_variant<128, 128, 16, 2, 4, 0>(839, 820, 764),    // 16: 8 waves of 64x32
     mfma_variant<128, 128, 32, 2, 4, 1>(857, 787, 790),    // 17: 8 waves of 64x32, BK 32
     dl_variant<192, 192, 32, 2, 6, 3, kAllOps, true>(852, 840, 852),  // 18: 4-byte direct loads
     mfma_variant<64, 64, 32, 2, 2, 1>(788, 615, 693),      // 19: 4 waves of 32x32
-    dl_variant<64, 64, 32, 2, 2, 2, kAllOps>(828, 567, 497),  // 20: direct loads, 4 waves of 32x32
+    dl_variant<64, 64, 32, 2, 2, 2, kAllOps, false, kCrossSliceAgpr>(848, 581, 508),  // 20: direct loads, 4 waves of 32x32
     dl_variant<64, 64, 32, 2, 2, 2, kAllOps, true>(780, 497, 780),  // 21: 4-byte direct loads
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));

@@ -30,10 +30,17 @@
 //    positions, and so is every slice when the rows are not 16-byte aligned
 //    (DW kernels exist for that case).
 //
-// Pipeline, per slice kt: wait for this thread's fetch of slice kt, barrier
-// (every wave's fetch of kt has landed and every wave has finished slice
-// kt-1), issue the fetch of slice kt+STAGES-1 into the buffer slice kt-1
-// used, multiply slice kt.  One barrier per slice.
+// Pipelines (PIPE), one barrier per slice either way:
+//  * plain (PIPE & 3 == 0), per slice kt: wait for this thread's fetch of
+//    slice kt, barrier (every wave's fetch of kt has landed and every wave has
+//    finished slice kt-1), issue the fetch of slice kt+STAGES-1 into the
+//    buffer slice kt-1 used, multiply slice kt.
+//  * cross-slice (PIPE & 3 == 2): the fetch of slice kt+STAGES-1 is
+//    interleaved with the MFMAs of slice kt's first k group, the barrier sits
+//    before the last k group, and the next slice's first fragments are read
+//    in the shadow of that group's MFMAs, so no LDS latency and no burst of
+//    load instructions stands between two slices' MFMAs.
+//  PIPE & 4 keeps the accumulators in AGPRs.
 #pragma once
 
 #include "common.hpp"
@@ -141,7 +148,8 @@ struct DlTraits {
 // (resources are clamped below it when direct loads are used).
 constexpr uint32_t kOobOffset = 0x80000000u;
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, bool TA, bool TB, bool DW>
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, bool TA, bool TB, bool DW,
+          int PIPE = 0>
 __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64)
 sgemm_mfma_dl_kernel(GemmArgs g)
 {
@@ -156,9 +164,10 @@ sgemm_mfma_dl_kernel(GemmArgs g)
 
     __shared__ __attribute__((aligned(1024))) float smem[T::LDS_FLOATS];
 
-    // (No AGPR hint here: with no staging registers the accumulators fit in
-    // ArchVGPRs, and with the hint the allocator rotates them through copies
-    // at the loop back-edge.)
+    // PIPE bit 2: an (empty) AGPR clobber makes the register allocator keep
+    // the accumulators in AGPRs.  It pays with the cross-slice loop; with the
+    // plain loop the allocator rotated them through copies at the back-edge.
+    if constexpr ((PIPE & 4) != 0) asm volatile("" ::: "a0");
 
     const Work w = map_work(g);
     locate<TA, TB>(g, w);
@@ -198,7 +207,9 @@ sgemm_mfma_dl_kernel(GemmArgs g)
     // index at k0), the resource extent up to the operand's last element, and
     // the limit of the contiguous column (k for KC, the index for XC) below
     // which a chunk holds data.
-    auto fetch = [&](int kt, int s) {
+    // Loads [lo, hi) of the slice's A_LOADS + B_LOADS (A first); a slice that
+    // goes through registers is fetched whole by the call with lo == 0.
+    auto fetch = [&](int kt, int s, int lo, int hi) {
         const int k0 = kt * BK;
         const float *abase = TA ? A + (int64_t)k0 * lda + m0 : A + (int64_t)m0 * lda + k0;
         const float *bbase = TB ? B + (int64_t)n0 * ldb + k0 : B + (int64_t)k0 * ldb + n0;
@@ -218,6 +229,7 @@ sgemm_mfma_dl_kernel(GemmArgs g)
             // (the load size must be a literal: one call per size)
 #pragma unroll
             for (int j = 0; j < A_LOADS; ++j) {
+                if (j < lo || j >= hi) continue;
                 const int off = (int)(a_col[j] < a_lim ? a_off[j] : kOobOffset);
                 float *dst = smem + s * STAGE_FLOATS + (j * NW + wave) * 64 * EL;
                 if constexpr (DW) __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void *)dst, 4, off, 0, 0, 0);
@@ -225,39 +237,43 @@ sgemm_mfma_dl_kernel(GemmArgs g)
             }
 #pragma unroll
             for (int j = 0; j < B_LOADS; ++j) {
+                if (A_LOADS + j < lo || A_LOADS + j >= hi) continue;
                 const int off = (int)(b_col[j] < b_lim ? b_off[j] : kOobOffset);
                 float *dst = smem + s * STAGE_FLOATS + A_FLOATS + (j * NW + wave) * 64 * EL;
                 if constexpr (DW) __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_void *)dst, 4, off, 0, 0, 0);
                 else __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_void *)dst, 16, off, 0, 0, 0);
             }
-        } else {
+        } else if (lo == 0) {
+            // One load's data at a time (loaded, masked, written to LDS), so
+            // this rarely used path needs few staging registers.
             const auto ar = make_rsrc(abase, abytes);
             const auto br = make_rsrc(bbase, bbytes);
-            float va[A_LOADS][EL], vb[B_LOADS][EL];
-#pragma unroll
-            for (int j = 0; j < A_LOADS; ++j)
-#pragma unroll
-                for (int e = 0; e < EL; ++e) {
-                    const float x = buffer_load_f32(ar, a_off[j] + 4u * e);
-                    va[j][e] = (a_col[j] + e < a_lim) ? x : 0.0f;
-                }
-#pragma unroll
-            for (int j = 0; j < B_LOADS; ++j)
-#pragma unroll
-                for (int e = 0; e < EL; ++e) {
-                    const float x = buffer_load_f32(br, b_off[j] + 4u * e);
-                    vb[j][e] = (b_col[j] + e < b_lim) ? x : 0.0f;
-                }
             auto put = [&](float *dst, const float (&v)[EL]) {
                 if constexpr (EL == 4) *reinterpret_cast<f32x4 *>(dst) = f32x4{v[0], v[1], v[2], v[3]};
                 else *dst = v[0];
             };
 #pragma unroll
-            for (int j = 0; j < A_LOADS; ++j)
-                put(smem + s * STAGE_FLOATS + ((j * NW + wave) * 64 + lane) * EL, va[j]);
+            for (int j = 0; j < A_LOADS; ++j) {
+                float v[EL];
 #pragma unroll
-            for (int j = 0; j < B_LOADS; ++j)
-                put(smem + s * STAGE_FLOATS + A_FLOATS + ((j * NW + wave) * 64 + lane) * EL, vb[j]);
+                for (int e = 0; e < EL; ++e) {
+                    const float x = buffer_load_f32(ar, a_off[j] + 4u * e);
+                    v[e] = (a_col[j] + e < a_lim) ? x : 0.0f;
+                }
+                put(smem + s * STAGE_FLOATS + ((j * NW + wave) * 64 + lane) * EL, v);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int j = 0; j < B_LOADS; ++j) {
+                float v[EL];
+#pragma unroll
+                for (int e = 0; e < EL; ++e) {
+                    const float x = buffer_load_f32(br, b_off[j] + 4u * e);
+                    v[e] = (b_col[j] + e < b_lim) ? x : 0.0f;
+                }
+                put(smem + s * STAGE_FLOATS + A_FLOATS + ((j * NW + wave) * 64 + lane) * EL, v);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     };
 
@@ -338,9 +354,78 @@ sgemm_mfma_dl_kernel(GemmArgs g)
     constexpr int WAIT_ALL = (7 << 4);  // vmcnt(0) lgkmcnt(0)
     constexpr int WAIT_LATER_LGKM0 = WAIT_LATER & ~(15 << 8);
     const int nk = (K + BK - 1) / BK;
+    constexpr int LOADS_ALL = A_LOADS + B_LOADS;
+    if constexpr ((PIPE & 3) == 2) {
+        // Cross-slice pipeline.  Slice kt: the loads of slice kt+STAGES-1 are
+        // issued among the MFMAs of k group 0; before the last k group each
+        // thread waits for its own loads of slice kt+1 and its LDS reads of
+        // slice kt, one barrier follows (every wave's slice kt+1 has landed and
+        // every wave has read all of slice kt, whose stage the next slice's
+        // loads may then overwrite), and the fragments of slice kt+1's first k
+        // group are read in the shadow of the last group's MFMAs.
+        static_assert(G % 2 == 0, "fragment buffers alternate per k group");
+        Frag f[2];
+        if (nk > 0) {
+#pragma unroll
+            for (int s = 0; s < STAGES - 1; ++s)
+                if (s < nk) fetch(s, s, 0, LOADS_ALL);
+            if (STAGES - 2 < nk) __builtin_amdgcn_s_waitcnt(WAIT_LATER_LGKM0);
+            else __builtin_amdgcn_s_waitcnt(WAIT_ALL);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            read_frag(0, 0, f[0]);
+        }
+        for (int kt = 0; kt < nk; ++kt) {
+            const int s = kt % STAGES;
+            const int s1 = (kt + 1) % STAGES;
+            const bool next = kt + 1 < nk;
+            const bool more = kt + STAGES - 1 < nk;
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (gi + 1 < G) {
+                    read_frag(s, gi + 1, f[(gi + 1) & 1]);
+                    if (gi == 0 && more) fetch(kt + STAGES - 1, (kt + STAGES - 1) % STAGES, 0, LOADS_ALL);
+                    mfma_frag(f[gi & 1]);
+                    // fragment reads (and in group 0 the loads) among the MFMAs
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                    }
+                    if (gi == 0) {
+#pragma unroll
+                        for (int i = 0; i < LOADS_ALL; ++i) {
+                            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                        }
+                    }
+                } else {
+                    // own loads of slice kt+1 landed (the later slices' may still
+                    // be in flight) and own reads of slice kt done, barrier, then
+                    // the next slice's first fragments
+                    if (kt + STAGES - 1 < nk) __builtin_amdgcn_s_waitcnt(WAIT_LATER_LGKM0);
+                    else __builtin_amdgcn_s_waitcnt(WAIT_ALL);
+                    asm volatile("" ::: "memory");
+                    __builtin_amdgcn_s_barrier();
+                    asm volatile("" ::: "memory");
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (next) read_frag(s1, 0, f[G & 1]);
+                    mfma_frag(f[gi & 1]);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
-        if (s < nk) fetch(s, s);
+        if (s < nk) fetch(s, s, 0, LOADS_ALL);
     for (int kt = 0; kt < nk; ++kt) {
         const int s = kt % STAGES;
         // this thread's fetch of slice kt has landed once at most the later
@@ -351,16 +436,22 @@ sgemm_mfma_dl_kernel(GemmArgs g)
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
-        if (kt + STAGES - 1 < nk) fetch(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+        const bool more = kt + STAGES - 1 < nk;
+        const int kn = kt + STAGES - 1, sn = (kt + STAGES - 1) % STAGES;
+        // PIPE 1: the next slice's loads are issued a share per k group, between
+        // the fragment reads and the MFMAs, instead of all before the first read.
+        if ((PIPE & 3) == 0 && more) fetch(kn, sn, 0, LOADS_ALL);
         Frag f[2];
         read_frag(s, 0, f[0]);
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) {
             if (gi + 1 < G) read_frag(s, gi + 1, f[(gi + 1) & 1]);
+            if ((PIPE & 3) == 1 && more) fetch(kn, sn, gi * LOADS_ALL / G, (gi + 1) * LOADS_ALL / G);
             __builtin_amdgcn_sched_barrier(0);
             mfma_frag(f[gi & 1]);
             __builtin_amdgcn_sched_barrier(0);
         }
+    }
     }
 
     // ---- epilogue ----------------------------------------------------------------------
