@@ -55,11 +55,22 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sgemm_8192x8192x8192_traffic.txt"
 KERNEL_SOURCES = ["sgemm_mfma.hpp", "sgemm_mfma_dl.hpp", "common.hpp"]
 
 
+def kernel_code(text):
+    """Kernel source with // comments and blank lines removed: what the
+    counters depend on (editing a comment does not change the kernel)."""
+    lines = []
+    for line in text.splitlines():
+        code = line.split("//", 1)[0].rstrip()
+        if code.strip():
+            lines.append(code)
+    return "\n".join(lines)
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "fp32_gemm_sgemm_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "fp32_gemm_sgemm_amd", "csrc", name)) as f:
+            h.update(kernel_code(f.read()).encode())
     return h.hexdigest()[:16]
 
 
