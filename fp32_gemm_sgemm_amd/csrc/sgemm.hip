@@ -102,12 +102,12 @@ const Variant kVariants[] = {
     dl_variant<256, 256, 16, 4, 2, 4, 1>(0, 0, 0),         // 10: direct loads, 4 stages
     dl_variant<256, 256, 32, 4, 2, 2, kAllOps, false, kCrossSliceAgpr>(928, 918, 660),  // 11: direct loads, 2 stages of BK 32
     dl_variant<128, 128, 32, 2, 2, 3, kAllOps>(782, 754, 397),  // 12: direct loads
-    dl_variant<192, 192, 32, 2, 6, 3, kAllOps>(872, 872, 615),  // 13: direct loads
+    dl_variant<192, 192, 32, 2, 6, 2, kAllOps, false, kCrossSliceAgpr>(896, 884, 626),  // 13: direct loads
     dl_variant<256, 256, 16, 4, 2, 3, 1>(0, 0, 0),         // 14: direct loads, 3 stages
-    dl_variant<128, 128, 32, 2, 4, 3, kAllOps>(820, 790, 492),  // 15: direct loads, 8 waves of 64x32
-    mfma_variant<128, 128, 16, 2, 4, 0>(839, 820, 764),    // 16: 8 waves of 64x32
+    dl_variant<128, 128, 32, 2, 4, 2, kAllOps, false, kCrossSliceAgpr>(900, 825, 579),  // 15: direct loads, 8 waves of 64x32
+    mfma_variant<128, 128, 16, 2, 4, 0>(839, 817, 764),    // 16: 8 waves of 64x32
     mfma_variant<128, 128, 32, 2, 4, 1>(857, 787, 790),    // 17: 8 waves of 64x32, BK 32
-    dl_variant<192, 192, 32, 2, 6, 3, kAllOps, true>(852, 840, 852),  // 18: 4-byte direct loads
+    dl_variant<192, 192, 32, 2, 6, 2, kAllOps, true, kCrossSliceAgpr>(861, 851, 861),  // 18: 4-byte direct loads
     mfma_variant<64, 64, 32, 2, 2, 1>(788, 615, 693),      // 19: 4 waves of 32x32
     dl_variant<64, 64, 32, 2, 2, 2, kAllOps, false, kCrossSliceAgpr>(848, 581, 508),  // 20: direct loads, 4 waves of 32x32
     dl_variant<64, 64, 32, 2, 2, 2, kAllOps, true>(780, 497, 780),  // 21: 4-byte direct loads
