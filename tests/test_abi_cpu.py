@@ -295,3 +295,35 @@ def test_plan_rejects_invalid(lib):
     assert plan(0, 0, 4, 4, 4, 4, 4, 4, 1, 256, 0, None) == HIP_ERROR_INVALID_VALUE
     assert plan(3, 0, 4, 4, 4, 4, 4, 4, 1, 256, 0, ctypes.byref(out)) == HIP_ERROR_INVALID_VALUE
     assert plan(0, 0, 4, 4, 4, 4, 4, 4, -1, 256, 0, ctypes.byref(out)) == HIP_ERROR_INVALID_VALUE
+
+
+def test_plan_invariants_random(lib):
+    """Seeded random problems: every plan serves the layout, its grid covers
+    tiles x splits x batch, its K ranges tile [0, K) in multiples of 64, its
+    workspace is what the split needs and never more than offered, and a
+    forced configuration completed by sgemm_f32_cfg_geometry agrees with the
+    selector's own choice."""
+    import numpy as np
+    rng = np.random.default_rng(2024)
+    for _ in range(400):
+        M, N, K = (int(x) for x in rng.integers(1, 9000, size=3))
+        if rng.random() < 0.3:
+            M, N = (int(x) for x in rng.integers(1, 300, size=2))
+        ta, tb = (int(x) for x in rng.integers(0, 2, size=2))
+        batch = int(rng.choice([1, 1, 1, 2, 7, 64]))
+        lda = (M if ta else K) + int(rng.integers(0, 5))
+        ldb = (K if tb else N) + int(rng.integers(0, 5))
+        ldc = N + int(rng.integers(0, 5))
+        ws = int(rng.choice([0, 1 << 20, 1 << 26, 1 << 40]))
+        cus = int(rng.choice([256, 304, 80]))
+        p = sg.sgemm_f32_plan(M, N, K, lda, ldb, ldc, cus, ta, tb, batch, ws)
+        assert sg.sgemm_f32_variant_ops(p.id) & (1 << (ta + 2 * tb))
+        assert p.tiles_m == metrics.ceil_div(M, p.bm) and p.tiles_n == metrics.ceil_div(N, p.bn)
+        assert p.grid == p.tiles_m * p.tiles_n * p.splits * batch
+        assert p.workspace_bytes <= ws
+        _check_split(p, M, N, K, batch)
+        cfg = sg.SgemmCfg()
+        cfg.id, cfg.splits, cfg.group_m, cfg.xcd_remap = p.id, p.splits, p.group_m, p.xcd_remap
+        g = sg.sgemm_f32_cfg_geometry(cfg, ta, tb, M, N, K, lda, ldb, ldc, batch)
+        assert (g.splits, g.k_chunk, g.grid, g.workspace_bytes) == \
+            (p.splits, p.k_chunk, p.grid, p.workspace_bytes)

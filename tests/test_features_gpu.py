@@ -309,3 +309,47 @@ def test_hip_graph_capture_and_replay():
             torch.cuda.synchronize()
             assert np.array_equal(Cd.cpu().numpy(), ref.cpu().numpy()), f"replay {rep}"
         del graph
+
+
+def test_random_configurations():
+    """40 seeded random problems mixing every feature: layout, alpha/beta,
+    batch with gaps between entries, a forced variant compiled for the layout
+    (or the selector), a forced K split, padded row strides and 4-byte
+    shifted starts; each compared in full with the general reference."""
+    rng = np.random.default_rng(31337)
+    nvar = sg.sgemm_f32_num_variants()
+    for case in range(40):
+        M, N, K = (int(x) for x in rng.integers(1, 260, size=3))
+        ta, tb = (int(x) for x in rng.integers(0, 2, size=2))
+        batch = int(rng.choice([1, 1, 2, 3]))
+        alpha = float(rng.choice([1.0, -0.75, 0.0, 2.5]))
+        beta = float(rng.choice([0.0, 0.0, 1.0, -0.5]))
+        pads = [int(x) for x in rng.integers(0, 6, size=3)]
+        shift = [int(x) for x in rng.integers(0, 2, size=3)]
+        ops = [v for v in range(nvar) if sg.sgemm_f32_variant_ops(v) & (1 << (ta + 2 * tb))]
+        vid = None if rng.random() < 0.3 else int(rng.choice(ops))
+        splits = int(rng.choice([1, 1, 2, 3, 8]))
+        note(f"random case {case}: {M}x{N}x{K} ta={ta} tb={tb} batch={batch} alpha={alpha} "
+             f"beta={beta} variant={vid} splits={splits} pads={pads} shift={shift}")
+        Ar, Br = ((K, M) if ta else (M, K)), ((N, K) if tb else (K, N))
+        Ah = rng.uniform(-1, 1, (batch,) + Ar).astype(np.float32)
+        Bh = rng.uniform(-1, 1, (batch,) + Br).astype(np.float32)
+        C0 = rng.uniform(-1, 1, (batch, M, N)).astype(np.float32)
+
+        def stack(host, pad, sh):
+            b, r, c = host.shape
+            ld = c + pad
+            stride = r * ld + 3 * pad
+            buf = torch.zeros(sh + b * stride + 4, dtype=torch.float32, device="cuda")
+            view = torch.as_strided(buf, (b, r, c), (stride, ld, 1), storage_offset=sh)
+            view.copy_(torch.from_numpy(host))
+            return view
+        A, B, C = stack(Ah, pads[0], shift[0]), stack(Bh, pads[1], shift[1]), stack(C0, pads[2], shift[2])
+        cfg = None
+        if vid is not None:
+            cfg = forced_split(vid, splits)
+        sg.sgemm_batched(A, B, out=C, transa=ta, transb=tb, alpha=alpha, beta=beta, cfg=cfg)
+        torch.cuda.synchronize()
+        ref, absb = oracle.gemm_ref_batched(Ah, Bh, ta, tb, alpha, beta, C0)
+        rep = oracle.compare(C.cpu().numpy(), ref, absb)
+        assert rep["n_bad"] == 0, (case, rep)
