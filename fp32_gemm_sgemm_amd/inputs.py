@@ -146,3 +146,25 @@ def small_integers(rng: np.random.Generator, shape, lo: int = -2, hi: int = 2) -
 
 def ones(shape) -> np.ndarray:
     return np.ones(shape, dtype=np.float32)
+
+
+def small_integers_device(shape, seed: int, lo: int = -3, hi: int = 3, device="cuda"):
+    """i.i.d. integers in [lo, hi] as a float32 device tensor, drawn on the
+    device by torch's seeded generator (for operands too large to draw and
+    upload from the host; the checks copy back only the rows and columns they
+    need)."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    return torch.randint(lo, hi + 1, tuple(shape), generator=gen, device=device,
+                         dtype=torch.float32)
+
+
+def grid_sample(n: int, seed: int, k: int = 40) -> np.ndarray:
+    """Sorted distinct indices in [0, n): the first, middle and last, and k
+    seeded uniform picks."""
+    if n <= 0:
+        return np.zeros(0, dtype=np.int64)
+    rng = np.random.default_rng(200_000 + seed)
+    picks = {0, n // 2, n - 1} | set(rng.integers(0, n, size=k).tolist())
+    return np.array(sorted(picks), dtype=np.int64)
