@@ -60,6 +60,12 @@ struct DlF3 {
     __device__ __forceinline__ float operator[](int i) const { return x[i]; }
 };
 
+// Offset given to chunks that must read as zero: beyond every resource
+// (resources are clamped below it when direct loads are used).
+constexpr uint32_t kOobOffset = 0x80000000u;
+
+template <bool B> struct DlTag { static constexpr bool value = B; };
+
 template <int W> struct DlVec;
 template <> struct DlVec<1> { typedef float T; };
 template <> struct DlVec<2> { typedef f32x2 T; };
@@ -109,18 +115,40 @@ struct DlOperand {
     __device__ __forceinline__ static void assign(int j, int wave, int lane, int ld,
                                                   uint32_t &off, int &col)
     {
+        int r, c;
+        source(j, wave, lane, r, c);
+        col = c;
+        off = 4u * ((uint32_t)r * (uint32_t)ld + (uint32_t)c);
+    }
+
+    // Load j's offset for a slice that lies wholly inside K, in a tile whose
+    // edge along the operand's own index (M for A, N for B) is at `lim`:
+    // data of indices at or past it gets kOobOffset.  Such offsets stay fixed
+    // for the whole tile, so a run of full slices needs no per-slice checks.
+    __device__ __forceinline__ static uint32_t full_slice_off(int j, int wave, int lane, int ld,
+                                                             int lim)
+    {
+        int r, c;
+        source(j, wave, lane, r, c);
+        const int idx = KC ? r : c;
+        return idx < lim ? 4u * ((uint32_t)r * (uint32_t)ld + (uint32_t)c) : kOobOffset;
+    }
+
+  private:
+    // The global row r and column c (of the operand as stored, relative to the
+    // slice's base) whose EL floats load j of this lane brings in.
+    __device__ __forceinline__ static void source(int j, int wave, int lane, int &r, int &c)
+    {
         const int q = ((j * NW + wave) * 64 + lane) * ELEMS;  // LDS float position
         const int rl = KC ? BK : E;                            // floats per LDS row
         const int row = q / rl;
-        int c = q % rl;
-        int r = row;
+        c = q % rl;
+        r = row;
         if constexpr (KC) {
             c = 4 * ((c / 4) ^ chunk_swizzle<BK>(row)) + c % 4;
             const int in = row % WT;
             r = row - in + W * (in % 32) + in / 32;
         }
-        col = c;
-        off = 4u * ((uint32_t)r * (uint32_t)ld + (uint32_t)c);
     }
 };
 
@@ -144,9 +172,6 @@ struct DlTraits {
     static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS budget of one CU");
 };
 
-// Offset given to chunks that must read as zero: beyond every resource
-// (resources are clamped below it when direct loads are used).
-constexpr uint32_t kOobOffset = 0x80000000u;
 
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, bool TA, bool TB, bool DW,
           int PIPE = 0>
@@ -277,6 +302,29 @@ sgemm_mfma_dl_kernel(GemmArgs g)
         }
     };
 
+    // Fetch of a slice wholly inside K in a tile that takes direct loads
+    // throughout, with the tile's fixed offsets (full_slice_off): one
+    // resource per operand, no checks, nothing that needs a branch.
+    auto fetch_full = [&](int kt, int s, const uint32_t (&af)[A_LOADS], const uint32_t (&bf)[B_LOADS]) {
+        const int k0 = kt * BK;
+        const float *abase = TA ? A + (int64_t)k0 * lda + m0 : A + (int64_t)m0 * lda + k0;
+        const float *bbase = TB ? B + (int64_t)n0 * ldb + k0 : B + (int64_t)k0 * ldb + n0;
+        const auto ar = make_rsrc(abase, (int64_t)kOobOffset);
+        const auto br = make_rsrc(bbase, (int64_t)kOobOffset);
+#pragma unroll
+        for (int j = 0; j < A_LOADS; ++j) {
+            float *dst = smem + s * STAGE_FLOATS + (j * NW + wave) * 64 * EL;
+            if constexpr (DW) __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void *)dst, 4, (int)af[j], 0, 0, 0);
+            else __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void *)dst, 16, (int)af[j], 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < B_LOADS; ++j) {
+            float *dst = smem + s * STAGE_FLOATS + A_FLOATS + (j * NW + wave) * 64 * EL;
+            if constexpr (DW) __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_void *)dst, 4, (int)bf[j], 0, 0, 0);
+            else __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_void *)dst, 16, (int)bf[j], 0, 0, 0);
+        }
+    };
+
     // ---- fragments -----------------------------------------------------------------
     // MFMA step t (0..3) of k group g takes k = 8g + t from lanes 0-31 and
     // k = 8g + 4 + t from lanes 32-63 (h = lane >> 5).
@@ -376,17 +424,25 @@ sgemm_mfma_dl_kernel(GemmArgs g)
             asm volatile("" ::: "memory");
             read_frag(0, 0, f[0]);
         }
-        for (int kt = 0; kt < nk; ++kt) {
+        uint32_t af[A_LOADS], bf[B_LOADS];
+        // One slice kt.  FULL: the slice fetched here (kt+STAGES-1) lies wholly
+        // inside K and the tile takes direct loads, so the fetch has no branch
+        // and its loads can sit among the MFMAs.
+        auto slice = [&](int kt, auto full) {
+            constexpr bool FULL = decltype(full)::value;
             const int s = kt % STAGES;
             const int s1 = (kt + 1) % STAGES;
-            const bool next = kt + 1 < nk;
-            const bool more = kt + STAGES - 1 < nk;
+            const bool next = FULL || kt + 1 < nk;
+            const bool more = FULL || kt + STAGES - 1 < nk;
 #pragma unroll
             for (int gi = 0; gi < G; ++gi) {
                 __builtin_amdgcn_sched_barrier(0);
                 if (gi + 1 < G) {
                     read_frag(s, gi + 1, f[(gi + 1) & 1]);
-                    if (gi == 0 && more) fetch(kt + STAGES - 1, (kt + STAGES - 1) % STAGES, 0, LOADS_ALL);
+                    if (gi == 0) {
+                        if constexpr (FULL) fetch_full(kt + STAGES - 1, (kt + STAGES - 1) % STAGES, af, bf);
+                        else if (more) fetch(kt + STAGES - 1, (kt + STAGES - 1) % STAGES, 0, LOADS_ALL);
+                    }
                     mfma_frag(f[gi & 1]);
                     // fragment reads (and in group 0 the loads) among the MFMAs
 #pragma unroll
@@ -405,7 +461,7 @@ sgemm_mfma_dl_kernel(GemmArgs g)
                     // own loads of slice kt+1 landed (the later slices' may still
                     // be in flight) and own reads of slice kt done, barrier, then
                     // the next slice's first fragments
-                    if (kt + STAGES - 1 < nk) __builtin_amdgcn_s_waitcnt(WAIT_LATER_LGKM0);
+                    if (more) __builtin_amdgcn_s_waitcnt(WAIT_LATER_LGKM0);
                     else __builtin_amdgcn_s_waitcnt(WAIT_ALL);
                     asm volatile("" ::: "memory");
                     __builtin_amdgcn_s_barrier();
@@ -421,7 +477,22 @@ sgemm_mfma_dl_kernel(GemmArgs g)
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
+        };
+        int kt = 0;
+        // Tiles whose every slice goes by direct loads (no chunk only partly
+        // inside M or N) run the slices that fetch a full slice without checks.
+        const int m_lim = M - m0, n_lim = N - n0;
+        const bool edge_chunks = !DW && ((TA && (m_lim & 3) && m_lim < BM) ||
+                                         (!TB && (n_lim & 3) && n_lim < BN));
+        if (g.direct && !edge_chunks) {
+#pragma unroll
+            for (int j = 0; j < A_LOADS; ++j) af[j] = OpA::full_slice_off(j, wave, lane, lda, m_lim);
+#pragma unroll
+            for (int j = 0; j < B_LOADS; ++j) bf[j] = OpB::full_slice_off(j, wave, lane, ldb, n_lim);
+            const int kend = K / BK - (STAGES - 1);
+            for (; kt < kend; ++kt) slice(kt, DlTag<true>());
         }
+        for (; kt < nk; ++kt) slice(kt, DlTag<false>());
     } else {
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
