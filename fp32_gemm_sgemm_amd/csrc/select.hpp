@@ -161,9 +161,11 @@ inline bool finish_cfg(const Variant &v, int id, const Problem &p, int want, sge
 constexpr double kCuFlopPerNs = 157.3e3 / 256.0;
 // Fixed cost of one tile (prologue fetch, pipeline fill, epilogue stores).
 constexpr double kTileFixedNs = 2500.0;
-// The reduction pass: start-up of the second launch, and the rate at which
-// it streams the partials and writes C (measured 3-5 us and about 5 TB/s).
-constexpr double kReduceFixedNs = 3000.0;
+// The reduction pass: the second launch and the wait for the first one to
+// drain (a split product measured 7-10 us above its main kernel's model at
+// 512^3 and 128 x 128 x 32768), and the rate at which it streams the
+// partials and writes C (about 5 TB/s).
+constexpr double kReduceFixedNs = 7500.0;
 constexpr double kReduceBytesPerNs = 5000.0;
 
 // eff: the variant's fraction of peak (x1000) for this call's alignment.

@@ -79,18 +79,17 @@ constexpr int kCrossSliceAgpr = 6;
 
 // The compiled variants.  Indices are part of the ABI of sgemm_f32_ex.  The
 // three last arguments are fractions of the FP32 matrix peak (x1000) the
-// variant sustains on MI355X, which the selector's cost model uses: over
-// rounds of full tiles with 16-byte aligned rows (measured at 8192^3; at
-// 3072^3, one tile per CU, for the 192 x 192 tiles), with at most one
-// workgroup per CU (measured at 2048^3 and 1024 x 1024 x 8192 split 4 ways),
-// and with unaligned rows (measured at 4099^3; 0.85 of the aligned figure
-// where not measured; 64 x 64 tiles measured at 512^3, 1024^3 and 2048^3).
+// variant sustains on MI355X, which the selector's cost model uses.  Each is
+// the model inverted on one measured shape, K = 4096 throughout (BM x BN the
+// variant's tile): over four rounds of full tiles with 16-byte aligned rows
+// (32 BM x 32 BN), over one round, one workgroup per CU (16 BM x 16 BN), and
+// with rows that are not 16-byte aligned (32 BM - 5 x 32 BN - 5, K = 4099).
 // The 4-byte direct-load variants serve only rows that are not 16-byte
-// aligned (measured at 4099^3 and 2051^3).  0 keeps a variant
-// out of automatic selection (comparison kernels, dominated tiles).
+// aligned.  0 keeps a variant out of automatic selection (comparison
+// kernels, dominated tiles).
 const Variant kVariants[] = {
-    mfma_variant<256, 256, 16, 4, 2, 0>(894, 894, 760),    // 0: 8 waves of 64x128
-    mfma_variant<128, 128, 16, 2, 2, 0>(886, 760, 781),    // 1: 4 waves of 64x64
+    mfma_variant<256, 256, 16, 4, 2, 0>(897, 889, 700),    // 0: 8 waves of 64x128
+    mfma_variant<128, 128, 16, 2, 2, 0>(860, 767, 595),    // 1: 4 waves of 64x64
     mfma_variant<128, 128, 32, 2, 2, 1>(0, 0, 0),          // 2: 4 waves of 64x64, BK 32
     mfma_variant<128, 256, 16, 2, 2, 0>(0, 0, 0),          // 3: 4 waves of 64x128
     mfma_variant<256, 128, 16, 4, 1, 0>(0, 0, 0),          // 4: 4 waves of 64x128
@@ -98,19 +97,19 @@ const Variant kVariants[] = {
     mfma_variant<128, 128, 16, 2, 2, -1>(0, 0, 0),         // 6: plain order (comparison)
     valu_variant(),                                        // 7: vector-FMA comparison
     mfma_variant<192, 192, 16, 2, 6, 0>(0, 0, 0),          // 8: 12 waves of 96x32
-    mfma_variant<192, 192, 32, 2, 6, 1>(869, 869, 730),    // 9: 12 waves of 96x32, BK 32
+    mfma_variant<192, 192, 32, 2, 6, 1>(893, 883, 718),    // 9: 12 waves of 96x32, BK 32
     dl_variant<256, 256, 16, 4, 2, 4, 1>(0, 0, 0),         // 10: direct loads, 4 stages
-    dl_variant<256, 256, 32, 4, 2, 2, kAllOps, false, kCrossSliceAgpr>(928, 918, 660),  // 11: direct loads, 2 stages of BK 32
-    dl_variant<128, 128, 32, 2, 2, 3, kAllOps>(782, 754, 397),  // 12: direct loads
-    dl_variant<192, 192, 32, 2, 6, 2, kAllOps, false, kCrossSliceAgpr>(896, 884, 626),  // 13: direct loads
+    dl_variant<256, 256, 32, 4, 2, 2, kAllOps, false, kCrossSliceAgpr>(966, 959, 660),  // 11: direct loads, 2 stages of BK 32
+    dl_variant<128, 128, 32, 2, 2, 3, kAllOps>(778, 770, 404),  // 12: direct loads
+    dl_variant<192, 192, 32, 2, 6, 2, kAllOps, false, kCrossSliceAgpr>(954, 947, 611),  // 13: direct loads
     dl_variant<256, 256, 16, 4, 2, 3, 1>(0, 0, 0),         // 14: direct loads, 3 stages
-    dl_variant<128, 128, 32, 2, 4, 2, kAllOps, false, kCrossSliceAgpr>(900, 825, 579),  // 15: direct loads, 8 waves of 64x32
-    mfma_variant<128, 128, 16, 2, 4, 0>(839, 817, 764),    // 16: 8 waves of 64x32
-    mfma_variant<128, 128, 32, 2, 4, 1>(857, 787, 790),    // 17: 8 waves of 64x32, BK 32
-    dl_variant<192, 192, 32, 2, 6, 2, kAllOps, true, kCrossSliceAgpr>(861, 851, 861),  // 18: 4-byte direct loads
-    mfma_variant<64, 64, 32, 2, 2, 1>(788, 615, 693),      // 19: 4 waves of 32x32
-    dl_variant<64, 64, 32, 2, 2, 2, kAllOps, false, kCrossSliceAgpr>(848, 581, 508),  // 20: direct loads, 4 waves of 32x32
-    dl_variant<64, 64, 32, 2, 2, 2, kAllOps, true>(780, 497, 780),  // 21: 4-byte direct loads
+    dl_variant<128, 128, 32, 2, 4, 2, kAllOps, false, kCrossSliceAgpr>(950, 919, 669),  // 15: direct loads, 8 waves of 64x32
+    mfma_variant<128, 128, 16, 2, 4, 0>(831, 828, 678),    // 16: 8 waves of 64x32
+    mfma_variant<128, 128, 32, 2, 4, 1>(821, 800, 752),    // 17: 8 waves of 64x32, BK 32
+    dl_variant<192, 192, 32, 2, 6, 2, kAllOps, true, kCrossSliceAgpr>(948, 940, 945),  // 18: 4-byte direct loads
+    mfma_variant<64, 64, 32, 2, 2, 1>(779, 605, 597),      // 19: 4 waves of 32x32
+    dl_variant<64, 64, 32, 2, 2, 2, kAllOps, false, kCrossSliceAgpr>(943, 651, 507),  // 20: direct loads, 4 waves of 32x32
+    dl_variant<64, 64, 32, 2, 2, 2, kAllOps, true>(780, 526, 774),  // 21: 4-byte direct loads
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 

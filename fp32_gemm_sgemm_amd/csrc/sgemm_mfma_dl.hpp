@@ -39,7 +39,11 @@
 //    interleaved with the MFMAs of slice kt's first k group, the barrier sits
 //    before the last k group, and the next slice's first fragments are read
 //    in the shadow of that group's MFMAs, so no LDS latency and no burst of
-//    load instructions stands between two slices' MFMAs.
+//    load instructions stands between two slices' MFMAs.  In a tile whose
+//    every slice takes direct loads, the slices that fetch a slice wholly
+//    inside K run a second copy of the loop body with load offsets fixed for
+//    the tile and no checks, so no branch separates the loads from the MFMAs
+//    they are scheduled among; the last slices keep the general fetch.
 //  PIPE & 4 keeps the accumulators in AGPRs.
 #pragma once
 
