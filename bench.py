@@ -10,7 +10,8 @@ workload, M = N = K = 8192, row-major, A and B i.i.d. U[-1, 1] drawn with seed
 untimed warm-up steps are followed by exactly K timed steps, bracketed by
 device synchronisation, with HIP events recorded on the launch stream around
 each step.  TFLOP/s = 2*M*N*K / t ("4.1 CUDA GEMM operator performance
-optimization", section 1.3).  A second workload, 3072^3 with N(0, 1) inputs
+optimization", section 1.3).  By default the operands stay cached between
+steps (warm); --cold writes 512 MiB between steps, outside the step's events.  A second workload, 3072^3 with N(0, 1) inputs
 (seed 2), is timed the same way and reported under "secondary"; its launches
 are only ~0.45 ms, so it is warmed for at least --secondary-warm-ms of GPU
 time (the chip takes about 0.1 s of sustained load to reach its full clock;
@@ -23,8 +24,9 @@ One JSON line is printed.  Besides the driver's fields it holds:
                 under profiles/, or null if the kernel sources changed since.
   cpu_baseline  the CPU reference (oracle/) timed on this host on a bounded
                 sample of the same product (whole rows of C, about
-                --cpu-seconds of work), in TFLOP/s, with the threads used; the
-                sampled rows are also compared with the GPU result.
+                --cpu-seconds of work), in TFLOP/s, with the threads used, and
+                on one thread over a smaller sample; the sampled rows are also
+                compared with the GPU result.
   configs       every configuration of the measured workload set through
                 sgemm_f32 (the plain C ABI, no workspace): 512^3, 2048^3 (and
                 its identity-A run), 3072^3, 8192x8192x4096, 4096x4096x8192,
@@ -93,13 +95,20 @@ def read_traffic():
         return None
 
 
-def time_workload(torch, sg, w, steps, warmup, cfg=None):
+# Bytes written between timed steps with --cold: twice the 256 MB last-level
+# cache (MALL), so no operand byte stays cached from the previous step.
+COLD_FLUSH_BYTES = 512 << 20
+
+
+def time_workload(torch, sg, w, steps, warmup, cfg=None, cold=False):
     from fp32_gemm_sgemm_amd import inputs
     A_np, B_np = inputs.workload_operands(w)
     A = torch.from_numpy(A_np).to("cuda")
     B = torch.from_numpy(B_np).to("cuda")
     C = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
+    flush = torch.empty(COLD_FLUSH_BYTES // 4, dtype=torch.float32, device="cuda") \
+        if cold else None
     for _ in range(warmup):
         sg.sgemm(A, B, out=C, stream=stream, cfg=cfg)
     torch.cuda.synchronize()
@@ -108,11 +117,14 @@ def time_workload(torch, sg, w, steps, warmup, cfg=None):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
+        if flush is not None:
+            flush.fill_(float(i))  # outside the step's events
         starts[i].record(stream)
         sg.sgemm(A, B, out=C, stream=stream, cfg=cfg)
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t0
+    del flush
     per_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
     region_ms = starts[0].elapsed_time(ends[-1])
     return {
@@ -305,10 +317,20 @@ def cpu_baseline(w, A_np, B_np, C_gpu, seconds):
         max_err = max(max_err, rep["max_norm_err"])
         rows = r1
     flops = 2.0 * rows * w.N * w.K
+    # the same reference on one thread, over whole rows for about a sixth as long
+    rows1, spent1 = 0, 0.0
+    while rows1 < w.M and (spent1 < seconds / 6 or rows1 == 0):
+        t0 = time.perf_counter()
+        oracle.sgemm_ref(A_np[rows1:rows1 + 1], B_np, nthreads=1)
+        spent1 += time.perf_counter() - t0
+        rows1 += 1
+    flops1 = 2.0 * rows1 * w.N * w.K
     return {
         "value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": nt, "kind": "oracle",
         "sample": f"rows 0..{rows - 1} of C ({rows} x {w.N} outputs, K = {w.K}, "
                   f"{flops / 1e9:.1f} GFLOP) in {spent:.1f} s",
+        "single_thread": {"value": flops1 / spent1 / 1e12, "unit": "TFLOP/s",
+                          "sample": f"rows 0..{rows1 - 1} in {spent1:.1f} s"},
         "check": {"n": rows * w.N, "n_bad": n_bad, "max_norm_err": max_err,
                   "tol": oracle.TOL},
     }
@@ -336,6 +358,9 @@ def main(argv=None):
     ap.add_argument("--extra-warm-ms", type=float, default=150.0)
     ap.add_argument("--no-probe", action="store_true",
                     help="skip the MFMA-peak probe (the measured matrix-core ceiling)")
+    ap.add_argument("--cold", action="store_true",
+                    help="write 512 MiB between timed steps (no operand left in L2 or MALL); "
+                         "the value is then the mean of the per-step event times")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="before timing, run one plain device copy of this many MiB, a "
                          "known-size kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -376,9 +401,10 @@ def main(argv=None):
         del src, dst
 
     w = inputs.WORKLOADS[args.workload]
-    r = time_workload(torch, sg, w, args.steps, args.warmup, cfg)
+    r = time_workload(torch, sg, w, args.steps, args.warmup, cfg, cold=args.cold)
     flops = w.flops
-    ms_per_step = r["region_ms"] / args.steps
+    # (with --cold the region also holds the cache flushes between steps)
+    ms_per_step = r["mean_ms"] if args.cold else r["region_ms"] / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (r["mean_ms"] * 1e-3) / 1e12
     peak = metrics.MI355X_FP32_MATRIX_PEAK_TFLOPS
@@ -406,6 +432,7 @@ def main(argv=None):
             "waves": f"{plan.waves_m}x{plan.waves_n}",
             "kernel": "mfma_f32_32x32x2" if plan.kernel == 0 else "valu_fma",
             "parallelism": "single GPU",
+            "cache": "cold" if args.cold else "warm",
         },
         "frac_of_fp32_matrix_peak": round(value / peak, 4),
         "timing_ms": {k: round(r[k], 4) for k in ("mean_ms", "median_ms", "min_ms", "p90_ms")},
