@@ -109,7 +109,7 @@ const Variant kVariants[] = {
     dl_variant<192, 192, 32, 2, 6, 2, kAllOps, true, kCrossSliceAgpr>(948, 940, 945),  // 18: 4-byte direct loads
     mfma_variant<64, 64, 32, 2, 2, 1>(779, 605, 597),      // 19: 4 waves of 32x32
     dl_variant<64, 64, 32, 2, 2, 2, kAllOps, false, kCrossSliceAgpr>(943, 651, 507),  // 20: direct loads, 4 waves of 32x32
-    dl_variant<64, 64, 32, 2, 2, 2, kAllOps, true>(780, 526, 774),  // 21: 4-byte direct loads
+    dl_variant<64, 64, 32, 2, 2, 2, kAllOps, true, kCrossSliceAgpr>(854, 640, 902),  // 21: 4-byte direct loads
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
