@@ -103,7 +103,7 @@ const Variant kVariants[] = {
     dl_variant<128, 128, 32, 2, 2, 3, kAllOps>(778, 770, 404),  // 12: direct loads
     dl_variant<192, 192, 32, 2, 6, 2, kAllOps, false, kCrossSliceAgpr>(954, 947, 611),  // 13: direct loads
     dl_variant<256, 256, 16, 4, 2, 3, 1>(0, 0, 0),         // 14: direct loads, 3 stages
-    dl_variant<128, 128, 32, 2, 4, 2, kAllOps, false, kCrossSliceAgpr>(950, 919, 669),  // 15: direct loads, 8 waves of 64x32
+    dl_variant<128, 128, 32, 4, 2, 2, kAllOps, false, kCrossSliceAgpr>(955, 931, 661),  // 15: direct loads, 8 waves of 32x64
     mfma_variant<128, 128, 16, 2, 4, 0>(831, 828, 678),    // 16: 8 waves of 64x32
     mfma_variant<128, 128, 32, 2, 4, 1>(821, 800, 752),    // 17: 8 waves of 64x32, BK 32
     dl_variant<192, 192, 32, 2, 6, 2, kAllOps, true, kCrossSliceAgpr>(948, 940, 945),  // 18: 4-byte direct loads
