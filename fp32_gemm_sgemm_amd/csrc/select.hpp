@@ -36,7 +36,9 @@ struct Variant {
     int eff_one_permille;        // the same when the grid has at most one workgroup
                                  // per CU (no co-resident workgroups to hide latency)
     int eff_unaligned_permille;  // the same as eff_permille when rows are not
-                                 // 16-byte aligned (every slice fetched through registers)
+                                 // 16-byte aligned (4-byte direct loads for the variants
+                                 // that have them, every slice fetched through registers
+                                 // for the other direct-load ones)
 };
 
 // One call as the planner sees it.

@@ -400,7 +400,7 @@ int sgemm_f32_variant_ops(int id)
 
 const char *sgemm_f32_version(void)
 {
-    return "libsgemm 0.3.0 gfx950 fp32 (mfma_f32_32x32x2; NN/NT/TN/TT, alpha/beta, split-K, strided batch; "
+    return "libsgemm 0.4.0 gfx950 fp32 (mfma_f32_32x32x2; NN/NT/TN/TT, alpha/beta, split-K, strided batch; "
            "valu comparison)";
 }
 
