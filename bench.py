@@ -37,8 +37,9 @@ One JSON line is printed.  Besides the driver's fields it holds:
                 time-based warm-up (--extra-warm-ms): the small 512^3
                 configuration and the one-tile 128 x 128 x 32768 product with
                 and without a workspace (K split across workgroups), the
-                transposed-operand layouts at 8192^3 and 3072^3, and
-                strided batches of attention-like products.
+                transposed-operand layouts at 8192^3 and 3072^3, strided
+                batches of attention-like products, and the 1024 x 8192 x 8192
+                row band one GPU would run if 8192^3 were split over 8 GPUs.
 """
 import argparse
 import hashlib
@@ -276,6 +277,19 @@ def extras(torch, sg, steps, warm_ms, cus, peak):
             0.0, C.data_ptr(), N, C.stride(0), batch, ws.data_ptr(), wsb, h)), steps, warm_ms)
         record(name, 2.0 * batch * M * N * K, ms, plan, batch=batch)
         del A, B, C, ws
+    torch.cuda.empty_cache()
+
+    # one GPU's share of 8192^3 split by rows of C over 8 GPUs (a 1024-row band
+    # of A times all of B), the shape each GPU would run in a row-band sharding
+    M, N, K = 1024, 8192, 8192
+    A, B = operand((M, K)), operand((K, N))
+    C = torch.empty((M, N), device="cuda")
+    plan = sg.sgemm_f32_plan(M, N, K, K, N, N, cus)
+    h = stream.cuda_stream
+    ms = time_call(torch, lambda: chk(sg.sgemm_f32(M, N, K, A.data_ptr(), K, B.data_ptr(), N,
+                                                C.data_ptr(), N, h)), steps, warm_ms)
+    record("row-band shard 1024x8192x8192 (8192^3 over 8 GPUs)", 2.0 * M * N * K, ms, plan)
+    del A, B, C
     torch.cuda.empty_cache()
     return out
 
