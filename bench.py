@@ -40,6 +40,11 @@ One JSON line is printed.  Besides the driver's fields it holds:
                 transposed-operand layouts at 8192^3 and 3072^3, strided
                 batches of attention-like products, and the 1024 x 8192 x 8192
                 row band one GPU would run if 8192^3 were split over 8 GPUs.
+  mfma_probe    the sustained v_mfma_f32_32x32x2_f32 rate on register operands
+                (the matrix-core ceiling at the chip's actual clock), and the
+                headline's fraction of it.
+  valu_probe    the sustained non-packed v_fma_f32 rate on register operands
+                (the vector-ALU ceiling the comparison kernel is bound by).
 """
 import argparse
 import hashlib
@@ -371,7 +376,7 @@ def main(argv=None):
                     help="skip the split-K, transposed-layout and batched measurements")
     ap.add_argument("--extra-warm-ms", type=float, default=150.0)
     ap.add_argument("--no-probe", action="store_true",
-                    help="skip the MFMA-peak probe (the measured matrix-core ceiling)")
+                    help="skip the MFMA- and VALU-peak probes (the measured ceilings)")
     ap.add_argument("--cold", action="store_true",
                     help="write 512 MiB between timed steps (no operand left in L2 or MALL); "
                          "the value is then the mean of the per-step event times")
@@ -494,6 +499,13 @@ def main(argv=None):
             "frac_of_published_peak": round(ceil / peak, 4),
             "gemm_frac_of_probe": round(value / ceil, 4),
             "what": "sustained v_mfma_f32_32x32x2_f32 rate, register operands only",
+        }
+        vceil = probes.valu_peak_tflops()
+        result["valu_probe"] = {
+            "tflops": round(vceil, 3),
+            "frac_of_published_peak": round(vceil / peak, 4),
+            "what": "sustained non-packed v_fma_f32 rate, register operands only (the "
+                    "instruction of the vector-FMA comparison kernel)",
         }
 
     if not args.no_cpu_baseline:

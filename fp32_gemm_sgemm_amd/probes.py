@@ -20,17 +20,17 @@ def load():
         lib.sgemm_probe_mfma_peak.restype = ctypes.c_int
         lib.sgemm_probe_mfma_peak_flops.argtypes = [ctypes.c_int, ctypes.c_int]
         lib.sgemm_probe_mfma_peak_flops.restype = ctypes.c_double
+        lib.sgemm_probe_valu_peak.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                              ctypes.c_void_p]
+        lib.sgemm_probe_valu_peak.restype = ctypes.c_int
+        lib.sgemm_probe_valu_peak_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+        lib.sgemm_probe_valu_peak_flops.restype = ctypes.c_double
         _lib = lib
     return _lib
 
 
-def mfma_peak_tflops(workgroups_per_cu=2, iters=20000, reps=3):
-    """Sustained v_mfma_f32_32x32x2_f32 throughput of the whole chip, TFLOP/s
-    (best of `reps` launches after one warm-up)."""
+def _best_tflops(launch, flops, wgs, iters, reps):
     import torch
-    lib = load()
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    wgs = cus * workgroups_per_cu
     out = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     best = 0.0
@@ -38,14 +38,36 @@ def mfma_peak_tflops(workgroups_per_cu=2, iters=20000, reps=3):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        rc = lib.sgemm_probe_mfma_peak(wgs, iters, out.data_ptr(), stream.cuda_stream)
+        rc = launch(wgs, iters, out.data_ptr(), stream.cuda_stream)
         e1.record(stream)
         if rc != 0:
-            raise RuntimeError(f"sgemm_probe_mfma_peak failed with hipError_t {rc}")
+            raise RuntimeError(f"probe launch failed with hipError_t {rc}")
         torch.cuda.synchronize()
         if rep:
             t = e0.elapsed_time(e1) * 1e-3
-            best = max(best, lib.sgemm_probe_mfma_peak_flops(wgs, iters) / t / 1e12)
+            best = max(best, flops(wgs, iters) / t / 1e12)
     if not torch.isfinite(out).all():
         raise RuntimeError("probe produced non-finite values")
     return best
+
+
+def _cus():
+    import torch
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def mfma_peak_tflops(workgroups_per_cu=2, iters=20000, reps=3):
+    """Sustained v_mfma_f32_32x32x2_f32 throughput of the whole chip, TFLOP/s
+    (best of `reps` launches after one warm-up)."""
+    lib = load()
+    return _best_tflops(lib.sgemm_probe_mfma_peak, lib.sgemm_probe_mfma_peak_flops,
+                        _cus() * workgroups_per_cu, iters, reps)
+
+
+def valu_peak_tflops(workgroups_per_cu=16, iters=40000, reps=3):
+    """Sustained single-precision v_fma_f32 throughput of the whole chip
+    (non-packed, 16 independent chains per thread, 16 workgroups of 4 waves per CU), TFLOP/s
+    (best of `reps` launches after one warm-up)."""
+    lib = load()
+    return _best_tflops(lib.sgemm_probe_valu_peak, lib.sgemm_probe_valu_peak_flops,
+                        _cus() * workgroups_per_cu, iters, reps)
