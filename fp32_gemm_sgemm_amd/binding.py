@@ -32,7 +32,8 @@ class SgemmCfg(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "id", "kernel", "bm", "bn", "bk", "waves_m", "waves_n",
         "group_m", "xcd_remap", "splits", "k_chunk", "grid", "threads",
-        "lds_bytes", "tiles_m", "tiles_n")] + [("workspace_bytes", ctypes.c_longlong)]
+        "lds_bytes", "tiles_m", "tiles_n")] + [("workspace_bytes", ctypes.c_longlong)] + [
+        (n, ctypes.c_int) for n in ("strip_m", "strip_n")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

@@ -103,6 +103,20 @@ inline void split_k(int K, int want, int &splits, int &k_chunk)
     if (splits <= 1) k_chunk = K;
 }
 
+// Edge strips: at most this many rows (or columns) of C go to the strip
+// kernel instead of a row (or column) of tiles.
+constexpr int kStripMaxWidth = 4;
+
+// The block the tiled kernel computes when sm rows and sn columns of C go to
+// strips: the first M - sm rows and N - sn columns.
+inline Problem main_block(const Problem &p, int sm, int sn)
+{
+    Problem q = p;
+    q.M = p.M - sm;
+    q.N = p.N - sn;
+    return q;
+}
+
 // Row stride of the partial results (16-byte rows).
 inline long long partial_ld(int N) { return ((long long)N + 3) & ~3ll; }
 
@@ -131,17 +145,34 @@ inline void describe(const Variant &v, int id, sgemm_cfg *out)
     out->tiles_m = 0;
     out->tiles_n = 0;
     out->workspace_bytes = 0;
+    out->strip_m = 0;
+    out->strip_n = 0;
 }
 
 // Default tile order: groups of 8 tile rows and the XCD remap.
 constexpr int kDefaultGroupM = 8;
 constexpr int kDefaultXcdRemap = 1;
 
-// Fills the geometry of variant v with `want` K splits; false if the grid
-// does not fit in an int.
-inline bool finish_cfg(const Variant &v, int id, const Problem &p, int want, sgemm_cfg *out)
+// Whether sm rows and sn columns of C may go to strips.
+inline bool strips_ok(const Problem &p, int sm, int sn)
 {
+    return sm >= 0 && sn >= 0 && sm <= kStripMaxWidth && sn <= kStripMaxWidth && sm <= p.M &&
+           sn <= p.N;
+}
+
+// Fills the geometry of variant v with `want` K splits for the block left
+// after sm rows and sn columns go to strips (the tile counts, grid, split and
+// workspace describe that block; an empty block has grid 0); false if the
+// grid does not fit in an int or the strips are out of range.
+inline bool finish_cfg(const Variant &v, int id, const Problem &full, int want, int sm, int sn,
+                       sgemm_cfg *out)
+{
+    if (!strips_ok(full, sm, sn)) return false;
+    const Problem p = main_block(full, sm, sn);
     describe(v, id, out);
+    out->strip_m = sm;
+    out->strip_n = sn;
+    if (p.M == 0 || p.N == 0) want = 1;  // no tiled block: nothing to split
     int splits, k_chunk;
     split_k(p.K, want, splits, k_chunk);
     const long long tm = ceil_div_ll(p.M, v.bm), tn = ceil_div_ll(p.N, v.bn);
@@ -189,9 +220,26 @@ inline double estimate_ns(const Variant &v, const Problem &p, int splits, int k_
     return t;
 }
 
+// The strip kernel: one launch for both strips, bound by streaming the
+// operand each strip reads whole (op(B) for the row strip, the first M - sm
+// rows of op(A) for the column strip).
+constexpr double kStripFixedNs = 4000.0;
+constexpr double kStripBytesPerNs = 4000.0;
+
+inline double strip_ns(const Problem &p, int sm, int sn)
+{
+    const long long rows_left = p.M - sm;
+    const bool row_strip = sm > 0, col_strip = sn > 0 && rows_left > 0;
+    if (!row_strip && !col_strip) return 0.0;
+    const double elems = (row_strip ? (double)p.K * p.N : 0.0) +
+                         (col_strip ? (double)p.K * rows_left : 0.0);
+    return kStripFixedNs + 4.0 * elems * p.batch / kStripBytesPerNs;
+}
+
 struct Choice {
     int id;
     int splits;
+    int strip_m, strip_n;
 };
 
 // Candidate split counts tried by the selector.
@@ -214,14 +262,28 @@ inline int variant_eff(const Variant &v, bool aligned16, bool lds_ok, bool stric
     return aligned16 && lds_ok ? v.eff_permille : v.eff_unaligned_permille;
 }
 
-// The fastest (variant, split count) by the cost model among the variants
-// compiled for the operand layout whose workspace fits in `workspace_bytes`.
-// Returns id -1 if no variant serves the layout.
+// Strip widths worth trying along a dimension of size d with tile size b:
+// none, and the rows past the last full tile when there are at most
+// kStripMaxWidth of them (all of d when d itself is that small).
+inline int strip_candidates(int d, int b, int (&out)[2])
+{
+    out[0] = 0;
+    const int rem = d % b;
+    if (rem >= 1 && rem <= kStripMaxWidth) {
+        out[1] = rem;
+        return 2;
+    }
+    return 1;
+}
+
+// The fastest (variant, split count, strips) by the cost model among the
+// variants compiled for the operand layout whose workspace fits in
+// `workspace_bytes`.  Returns id -1 if no variant serves the layout.
 inline Choice select_plan(const Variant *vs, int n, const Problem &p, int cus, bool aligned16,
                           bool lds_ok, long long workspace_bytes)
 {
     const int op = op_index(p);
-    Choice best = {-1, 1};
+    Choice best = {-1, 1, 0, 0};
     double best_t = 0;
     for (int pass = 0; pass < 2 && best.id < 0; ++pass) {
         for (int i = 0; i < n; ++i) {
@@ -231,19 +293,36 @@ inline Choice select_plan(const Variant *vs, int n, const Problem &p, int cus, b
                 continue;
             const int eff = variant_eff(v, aligned16, lds_ok, pass == 0);
             if (eff <= 0) continue;
-            int last = 0;
-            for (int want : kSplitCandidates) {
-                int splits, k_chunk;
-                split_k(p.K, want, splits, k_chunk);
-                if (splits <= last) continue;
-                last = splits;
-                if (split_workspace_bytes(p, splits) > workspace_bytes) break;
-                const long long grid = ceil_div_ll(p.M, v.bm) * ceil_div_ll(p.N, v.bn) * splits * (long long)p.batch;
-                if (grid > INT_MAX) break;
-                const double t = estimate_ns(v, p, splits, k_chunk, cus, eff);
-                if (best.id < 0 || t < best_t) {
-                    best = {i, splits};
-                    best_t = t;
+            int sms[2], sns[2];
+            const int nsm = strip_candidates(p.M, v.bm, sms), nsn = strip_candidates(p.N, v.bn, sns);
+            for (int a = 0; a < nsm; ++a) {
+                for (int b = 0; b < nsn; ++b) {
+                    const Problem q = main_block(p, sms[a], sns[b]);
+                    const double ts = strip_ns(p, sms[a], sns[b]);
+                    if (q.M == 0 || q.N == 0) {
+                        // no tiled block: the strips are the whole product
+                        if (best.id < 0 || ts < best_t) {
+                            best = {i, 1, sms[a], sns[b]};
+                            best_t = ts;
+                        }
+                        continue;
+                    }
+                    int last = 0;
+                    for (int want : kSplitCandidates) {
+                        int splits, k_chunk;
+                        split_k(q.K, want, splits, k_chunk);
+                        if (splits <= last) continue;
+                        last = splits;
+                        if (split_workspace_bytes(q, splits) > workspace_bytes) break;
+                        const long long grid =
+                            ceil_div_ll(q.M, v.bm) * ceil_div_ll(q.N, v.bn) * splits * (long long)q.batch;
+                        if (grid > INT_MAX) break;
+                        const double t = estimate_ns(v, q, splits, k_chunk, cus, eff) + ts;
+                        if (best.id < 0 || t < best_t) {
+                            best = {i, splits, sms[a], sns[b]};
+                            best_t = t;
+                        }
+                    }
                 }
             }
         }

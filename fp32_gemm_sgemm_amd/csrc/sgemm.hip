@@ -16,6 +16,7 @@
 #include "sgemm_mfma.hpp"
 #include "sgemm_mfma_dl.hpp"
 #include "sgemm_reduce.hpp"
+#include "sgemm_strip.hpp"
 #include "sgemm_valu.hpp"
 #include "select.hpp"
 
@@ -110,6 +111,7 @@ const Variant kVariants[] = {
     mfma_variant<64, 64, 32, 2, 2, 1>(779, 605, 597),      // 19: 4 waves of 32x32
     dl_variant<64, 64, 32, 2, 2, 2, kAllOps, false, kCrossSliceAgpr>(943, 651, 507),  // 20: direct loads, 4 waves of 32x32
     dl_variant<64, 64, 32, 2, 2, 2, kAllOps, true, kCrossSliceAgpr>(854, 640, 902),  // 21: 4-byte direct loads
+    dl_variant<128, 128, 32, 4, 2, 2, kAllOps, true, kCrossSliceAgpr>(950, 925, 950),  // 22: 4-byte direct loads, 8 waves of 32x64
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -299,6 +301,102 @@ hipError_t launch_reduce(const Call &c, int splits, float alpha, hipStream_t str
     return hipSuccess;
 }
 
+// The edge strips of a plan (sgemm_strip.hpp): the last sm rows of C (all N
+// columns), and the last sn columns of the M - sm rows above them.  The row
+// strip streams op(B), which is k-contiguous when B is transposed; the column
+// strip streams op(A), k-contiguous when A is not.
+const void *strip_kernel(const Problem &p)
+{
+    static const void *const fns[4] = {
+        reinterpret_cast<const void *>(&sgemm::sgemm_strip_kernel<false, true>),   // NN
+        reinterpret_cast<const void *>(&sgemm::sgemm_strip_kernel<false, false>),  // TN
+        reinterpret_cast<const void *>(&sgemm::sgemm_strip_kernel<true, true>),    // NT
+        reinterpret_cast<const void *>(&sgemm::sgemm_strip_kernel<true, false>),   // TT
+    };
+    return fns[sgemm::op_index(p)];
+}
+
+hipError_t launch_strips(const Call &c, int sm, int sn, hipStream_t stream)
+{
+    const Problem &p = c.p;
+    const int m_main = p.M - sm, n_main = p.N - sn;
+    sgemm::StripArgs a = {};
+    a.K = p.K;
+    a.alpha = c.alpha;
+    a.beta = c.beta;
+    sgemm::Strip &rs = a.s[0], &cs = a.s[1];
+    if (sm > 0) {
+        // out(x, y) = C[m_main + y][x] = sum_k op(B)[k][x] * op(A)[m_main + y][k]
+        rs.big = c.B;
+        rs.ld_big = p.ldb;
+        rs.batch_big = c.sb;
+        if (p.transa) {
+            rs.small = c.A + m_main;
+            rs.s_y = 1;
+            rs.s_k = p.lda;
+        } else {
+            rs.small = c.A + (long long)m_main * p.lda;
+            rs.s_y = p.lda;
+            rs.s_k = 1;
+        }
+        rs.batch_small = c.sa;
+        rs.out = c.C + (long long)m_main * p.ldc;
+        rs.o_x = 1;
+        rs.o_y = p.ldc;
+        rs.batch_out = c.sc;
+        rs.X = p.N;
+        rs.r = sm;
+        const int w = p.transb ? sgemm::kStripKcWidth : sgemm::kStripXcWidth;
+        rs.wgs = (int)sgemm::ceil_div_ll(p.N, w);
+    }
+    if (sn > 0 && m_main > 0) {
+        // out(x, y) = C[x][n_main + y] = sum_k op(A)[x][k] * op(B)[k][n_main + y]
+        cs.big = c.A;
+        cs.ld_big = p.lda;
+        cs.batch_big = c.sa;
+        if (p.transb) {
+            cs.small = c.B + (long long)n_main * p.ldb;
+            cs.s_y = p.ldb;
+            cs.s_k = 1;
+        } else {
+            cs.small = c.B + n_main;
+            cs.s_y = 1;
+            cs.s_k = p.ldb;
+        }
+        cs.batch_small = c.sb;
+        cs.out = c.C + n_main;
+        cs.o_x = p.ldc;
+        cs.o_y = 1;
+        cs.batch_out = c.sc;
+        cs.X = m_main;
+        cs.r = sn;
+        const int w = p.transa ? sgemm::kStripXcWidth : sgemm::kStripKcWidth;
+        cs.wgs = (int)sgemm::ceil_div_ll(m_main, w);
+    }
+    const long long wgs = (long long)rs.wgs + cs.wgs;
+    if (wgs == 0) return hipSuccess;
+    if (wgs > INT_MAX) return hipErrorInvalidValue;
+    constexpr int kMaxY = 65535;
+    for (int z0 = 0; z0 < p.batch; z0 += kMaxY) {
+        const int nz = p.batch - z0 < kMaxY ? p.batch - z0 : kMaxY;
+        a.z0 = z0;
+        void *args[] = {&a};
+        hipError_t e = hipLaunchKernel(strip_kernel(p), dim3((unsigned)wgs, (unsigned)nz),
+                                       dim3(sgemm::kStripThreads), args, 0, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+// The part of a call the tiles compute: its first M - sm rows and N - sn
+// columns (same operands, strides and workspace).
+Call main_part(const Call &c, int sm, int sn)
+{
+    Call m = c;
+    m.p = sgemm::main_block(c.p, sm, sn);
+    return m;
+}
+
 int plan_for(const Call &c, int cus, sgemm_cfg *out)
 {
     if (!out || !sgemm::sizes_ok(c.p)) return hipErrorInvalidValue;
@@ -306,8 +404,9 @@ int plan_for(const Call &c, int cus, sgemm_cfg *out)
     const Choice ch = sgemm::select_plan(kVariants, kNumVariants, c.p, cus > 0 ? cus : 256,
                                          rows_aligned16(c), sgemm::direct_lds_ok(c.p), ws);
     if (ch.id < 0) return hipErrorInvalidValue;
-    return sgemm::finish_cfg(kVariants[ch.id], ch.id, c.p, ch.splits, out) ? hipSuccess
-                                                                           : hipErrorInvalidValue;
+    return sgemm::finish_cfg(kVariants[ch.id], ch.id, c.p, ch.splits, ch.strip_m, ch.strip_n, out)
+               ? hipSuccess
+               : hipErrorInvalidValue;
 }
 
 // A forced configuration completed for this call (see sgemm_f32_cfg_geometry).
@@ -318,7 +417,8 @@ int forced_cfg(const Problem &p, const sgemm_cfg *force, sgemm_cfg *cfg)
     const int id = force->id;
     if (!kVariants[id].fn[sgemm::op_index(p)]) return hipErrorInvalidValue;
     const int group_m = force->group_m, xcd = force->xcd_remap ? 1 : 0;
-    if (!sgemm::finish_cfg(kVariants[id], id, p, force->splits, cfg)) return hipErrorInvalidValue;
+    if (!sgemm::finish_cfg(kVariants[id], id, p, force->splits, force->strip_m, force->strip_n, cfg))
+        return hipErrorInvalidValue;
     cfg->group_m = group_m;
     cfg->xcd_remap = xcd;
     return hipSuccess;
@@ -352,9 +452,13 @@ int run(const Call &c, hipStream_t stream, const sgemm_cfg *force)
         if (r != hipSuccess) return r;
         id = cfg.id;
     }
-    e = launch_gemm(kVariants[id], cfg, c, stream);
-    if (e != hipSuccess || cfg.splits <= 1) return e;
-    return launch_reduce(c, cfg.splits, c.alpha, stream);
+    const Call m = main_part(c, cfg.strip_m, cfg.strip_n);
+    if (m.p.M > 0 && m.p.N > 0) {
+        e = launch_gemm(kVariants[id], cfg, m, stream);
+        if (e == hipSuccess && cfg.splits > 1) e = launch_reduce(m, cfg.splits, c.alpha, stream);
+        if (e != hipSuccess) return e;
+    }
+    return launch_strips(c, cfg.strip_m, cfg.strip_n, stream);
 }
 
 Call make_call(int transa, int transb, int M, int N, int K, float alpha,
@@ -400,8 +504,8 @@ int sgemm_f32_variant_ops(int id)
 
 const char *sgemm_f32_version(void)
 {
-    return "libsgemm 0.4.0 gfx950 fp32 (mfma_f32_32x32x2; NN/NT/TN/TT, alpha/beta, split-K, strided batch; "
-           "valu comparison)";
+    return "libsgemm 0.5.0 gfx950 fp32 (mfma_f32_32x32x2; NN/NT/TN/TT, alpha/beta, split-K, strided batch, "
+           "edge strips; valu comparison)";
 }
 
 int sgemm_f32_plan(int transa, int transb, int M, int N, int K, int lda, int ldb, int ldc, int batch,

@@ -1,0 +1,225 @@
+// Edge strips: the parts of a product that hold at most four rows or four
+// columns of C.
+//
+// A product whose M (or N) is a multiple of the tile height plus a few rows
+// spends a whole tile row on those few rows: 4099^2 outputs in 192^2 tiles are
+// 484 workgroups, 1.9 rounds of the chip's 256 compute units, where the
+// 4096^2 block alone is one round of 256^2 tiles (the tail effect of the DD2360
+// workbook "Applied GPU Programming", Module 17, and the wave quantisation of
+// "4.1 CUDA GEMM operator performance optimization", section 12.5).  The host
+// then runs the tiled kernel on the (M - sm) x (N - sn) block and this kernel
+// on the strips that remain:
+//
+//   row strip     rows M-sm .. M-1, columns 0 .. N-1        (sm <= 4)
+//   column strip  rows 0 .. M-sm-1, columns N-sn .. N-1     (sn <= 4)
+//
+// Each strip is a product out(x, y) = sum_k big(x, k) * small(y, k) with a
+// long index x (a column of C in the row strip, a row of C in the column
+// strip) and at most four values of y: its cost is streaming the big operand
+// (op(B) for the row strip, op(A) for the column strip) once, so it is bound by
+// memory bandwidth, and a matrix-core tile would pad its at most 4 rows to 32.
+// It runs on vector FMAs.
+//
+// A workgroup covers a block of x and all of K; its lanes and waves split K,
+// and their partial sums are added in a fixed order (a butterfly of lane
+// shuffles, then the waves in order through LDS), so a result is the same on
+// every run and no workspace is needed.  The small operand is staged through
+// LDS as [k][y] in chunks of K, zero for y past the strip and k past K.
+//
+// big is read in one of two storage orders:
+//   XC ("x contiguous"): big(x, k) = big[k * ld_big + x] (B in a row strip,
+//       a transposed A in a column strip).  Lanes run along x, 4 floats each;
+//       a workgroup covers 32 x, and its 64 K phases are 8 lane groups in
+//       each of 8 waves.
+//   KC ("k contiguous"): big(x, k) = big[x * ld_big + k] (a transposed B in a
+//       row strip, A in a column strip).  Lanes run along k, 4 floats each; a
+//       wave reads 4 rows, and a workgroup covers 16 rows in 4 row groups
+//       times 2 K phases.
+#pragma once
+
+#include "common.hpp"
+
+namespace sgemm {
+
+constexpr int kStripMax = 4;         // rows (or columns) of C one strip may hold
+constexpr int kStripThreads = 512;   // 8 waves
+constexpr int kStripKChunk = 2048;   // K values of the small operand staged at once
+constexpr int kStripXcWidth = 32;    // x per workgroup, XC order
+constexpr int kStripKcWidth = 16;    // x per workgroup, KC order
+
+struct Strip {
+    const float *big;     // XC: big(x, k) = big[k * ld_big + x]; KC: big[x * ld_big + k]
+    const float *small;   // small(y, k) = small[y * s_y + k * s_k]
+    float *out;           // out(x, y) = out[x * o_x + y * o_y]
+    int64_t batch_big, batch_small, batch_out;  // elements between batch entries
+    int64_t ld_big, s_y, s_k, o_x, o_y;
+    int X;                // x range
+    int r;                // y range, 1 .. kStripMax
+    int wgs;              // workgroups of this strip (0: no strip)
+};
+
+// Up to two strips in one launch: workgroups [0, s[0].wgs) take strip 0, the
+// next s[1].wgs strip 1; blockIdx.y is the batch entry (from z0 on).
+struct StripArgs {
+    Strip s[2];
+    int K;
+    int z0;
+    float alpha, beta;
+};
+
+template <bool KC>
+__device__ __forceinline__ void strip_block(const Strip &s, int wg, int K, int z, float alpha,
+                                            float beta, f32x4 *stage)
+{
+    const float *__restrict__ big = s.big + z * s.batch_big;
+    const float *__restrict__ small = s.small + z * s.batch_small;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int X = s.X;
+    constexpr int XB = KC ? kStripKcWidth : kStripXcWidth;
+    const int x0 = wg * XB;
+
+    // KC: acc[row][y]; XC: acc[y][x]
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+
+    // XC: lane group kr (8 lanes, 32 consecutive x) of wave w takes k = kr + 8w
+    // (mod 64).  KC: wave w reads rows x0 + 4*(w%4) .. +3 at k = 4*lane +
+    // 256*(w/4) (mod 512); rows past X are clamped to X-1 (read, never stored).
+    const int xq = lane & 7, kr = lane >> 3;
+    const int xc = x0 + 4 * xq;
+    const bool x_full = xc + 3 < X;
+    const int rg = wave & 3, kp = wave >> 2;
+    const float *rows[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int x = min(x0 + 4 * rg + i, X - 1);
+        rows[i] = big + (int64_t)x * s.ld_big;
+    }
+
+    for (int c0 = 0; c0 < K; c0 += kStripKChunk) {
+        const int clen = min(K - c0, kStripKChunk);
+        for (int k = tid; k < kStripKChunk; k += kStripThreads) {
+            f32x4 v;
+#pragma unroll
+            for (int y = 0; y < 4; ++y)
+                v[y] = (y < s.r && k < clen) ? small[y * s.s_y + (int64_t)(c0 + k) * s.s_k] : 0.0f;
+            stage[k] = v;
+        }
+        __syncthreads();
+        if constexpr (KC) {
+#pragma unroll 2
+            for (int kk = 256 * kp + 4 * lane; kk < clen; kk += 512) {
+                const int k = c0 + kk;
+                f32x4 sv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sv[e] = stage[kk + e];
+                f32x4 v[4];
+                if (k + 3 < K) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const f32x4u *>(rows[i] + k);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[i][e] = k + e < K ? rows[i][k + e] : 0.0f;
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+#pragma unroll
+                        for (int y = 0; y < 4; ++y) acc[i][y] += v[i][e] * sv[e][y];
+            }
+        } else {
+            const float *p = big + (int64_t)(c0 + kr + 8 * wave) * s.ld_big + xc;
+            const int64_t step = 64 * s.ld_big;
+#pragma unroll 4
+            for (int kk = kr + 8 * wave; kk < clen; kk += 64, p += step) {
+                f32x4 v;
+                if (x_full) {
+                    v = *reinterpret_cast<const f32x4u *>(p);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = xc + e < X ? p[e] : 0.0f;
+                }
+                const f32x4 sv = stage[kk];
+#pragma unroll
+                for (int y = 0; y < 4; ++y)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[y][e] += sv[y] * v[e];
+            }
+        }
+        __syncthreads();
+    }
+
+    // Fixed-order reduction: lanes that share outputs by xor butterflies, then
+    // the waves in order through LDS (the stage area, free after the last
+    // chunk's barrier).
+    float *red = reinterpret_cast<float *>(stage);
+    float *__restrict__ out = s.out + z * s.batch_out;
+    if constexpr (KC) {
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int y = 0; y < 4; ++y) acc[i][y] += __shfl_xor(acc[i][y], off);
+        if (lane == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int y = 0; y < 4; ++y) red[wave * 16 + i * 4 + y] = acc[i][y];
+        }
+        __syncthreads();
+        if (tid < XB * 4) {
+            const int xi = tid >> 2, y = tid & 3;
+            const int g = xi >> 2, i = xi & 3;
+            const float sum = red[g * 16 + i * 4 + y] + red[(g + 4) * 16 + i * 4 + y];
+            if (x0 + xi < X && y < s.r) {
+                float *p = out + (int64_t)(x0 + xi) * s.o_x + (int64_t)y * s.o_y;
+                *p = beta != 0.0f ? alpha * sum + beta * *p : alpha * sum;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int off = 8; off < 64; off <<= 1)
+#pragma unroll
+            for (int y = 0; y < 4; ++y)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[y][e] += __shfl_xor(acc[y][e], off);
+        if (kr == 0) {
+#pragma unroll
+            for (int y = 0; y < 4; ++y)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) red[(wave * 8 + xq) * 16 + y * 4 + e] = acc[y][e];
+        }
+        __syncthreads();
+        if (tid < XB * 4) {
+            const int y = tid / XB, xi = tid % XB;
+            const int q = xi >> 2, e = xi & 3;
+            float sum = red[q * 16 + y * 4 + e];
+#pragma unroll
+            for (int w = 1; w < kStripThreads / 64; ++w) sum += red[(w * 8 + q) * 16 + y * 4 + e];
+            if (x0 + xi < X && y < s.r) {
+                float *p = out + (int64_t)(x0 + xi) * s.o_x + (int64_t)y * s.o_y;
+                *p = beta != 0.0f ? alpha * sum + beta * *p : alpha * sum;
+            }
+        }
+    }
+}
+
+// KC0, KC1: storage order of strip 0's and strip 1's big operand.
+template <bool KC0, bool KC1>
+__global__ void __launch_bounds__(kStripThreads) sgemm_strip_kernel(StripArgs a)
+{
+    __shared__ __attribute__((aligned(16))) f32x4 stage[kStripKChunk];
+    const int z = a.z0 + blockIdx.y;
+    const int wg = blockIdx.x;
+    if (wg < a.s[0].wgs) strip_block<KC0>(a.s[0], wg, a.K, z, a.alpha, a.beta, stage);
+    else strip_block<KC1>(a.s[1], wg - a.s[0].wgs, a.K, z, a.alpha, a.beta, stage);
+}
+
+}  // namespace sgemm

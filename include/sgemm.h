@@ -54,6 +54,13 @@ typedef struct sgemm_cfg {
     int lds_bytes; /* LDS per workgroup */
     int tiles_m, tiles_n;
     long long workspace_bytes; /* workspace the configuration needs */
+    /* Edge strips (0 = none): the last strip_m rows of C, and the last
+       strip_n columns of the rows above them, are computed by a
+       bandwidth-bound strip kernel instead of by tiles, and the tile
+       geometry above (tiles_m, tiles_n, grid, splits, workspace_bytes)
+       describes the (M - strip_m) x (N - strip_n) block that remains.  At
+       most 4 each.  Chosen by plan/query; an input of sgemm_f32_ex. */
+    int strip_m, strip_n;
 } sgemm_cfg;
 
 /*
@@ -180,11 +187,13 @@ int sgemm_f32_workspace_size(int transa, int transb, int M, int N, int K,
  * sweeps and for the measured comparison kernels.  cfg == NULL behaves as
  * sgemm_f32_strided_batched.  Otherwise cfg->id selects the variant (see
  * sgemm_f32_variant), cfg->splits the requested K split (<= 1: none; the
- * split actually used is reported by sgemm_f32_plan), and cfg->group_m and
- * cfg->xcd_remap the tile order; the other fields are ignored.  Returns
- * hipErrorInvalidValue for an id out of range, a variant not compiled for
- * the operand layout, cfg->group_m < 0, or a workspace too small for the
- * split.  Same arguments, ownership and errors as sgemm_f32_strided_batched.
+ * split actually used is reported by sgemm_f32_plan), cfg->group_m and
+ * cfg->xcd_remap the tile order, and cfg->strip_m, cfg->strip_n the edge
+ * strips (0 .. min(4, M) rows and 0 .. min(4, N) columns; 0 for none); the
+ * other fields are ignored.  Returns hipErrorInvalidValue for an id out of
+ * range, a variant not compiled for the operand layout, cfg->group_m < 0,
+ * strips out of range, or a workspace too small for the split.  Same
+ * arguments, ownership and errors as sgemm_f32_strided_batched.
  */
 int sgemm_f32_ex(int transa, int transb, int M, int N, int K,
                  float alpha,
@@ -203,8 +212,11 @@ int sgemm_f32_ex(int transa, int transb, int M, int N, int K,
  * logic, no HIP call.  Writes *out; returns hipErrorInvalidValue for invalid
  * sizes, layouts or leading dimensions, or out == NULL.  The geometry follows
  * the round-up-and-guard rule (DD2360 workbook, Module 6, section 6.3):
- * tiles_m = ceil(M/BM), tiles_n = ceil(N/BN), grid = tiles_m * tiles_n *
- * splits * batch.
+ * tiles_m = ceil(M'/BM), tiles_n = ceil(N'/BN), grid = tiles_m * tiles_n *
+ * splits * batch, where M' = M - strip_m and N' = N - strip_n are the sizes
+ * left to the tiles when the selector hands a few edge rows or columns to the
+ * strip kernel (strip_m = M mod BM or strip_n = N mod BN when that is at most
+ * 4 and the cost model prefers it; all of M or N when it is that small).
  */
 int sgemm_f32_plan(int transa, int transb, int M, int N, int K,
                    int lda, int ldb, int ldc, int batch,
@@ -212,12 +224,13 @@ int sgemm_f32_plan(int transa, int transb, int M, int N, int K,
 
 /*
  * sgemm_f32_cfg_geometry: completes a forced configuration.  Reads cfg->id,
- * cfg->splits, cfg->group_m and cfg->xcd_remap (as sgemm_f32_ex does) and
- * fills in the rest as sgemm_f32_plan would for that variant and requested
- * split: the split actually used, k_chunk, the grid and the workspace bytes
- * it needs.  Pure host logic.  Returns hipErrorInvalidValue for invalid
- * sizes, an id out of range, a variant not compiled for the operand layout
- * or cfg->group_m < 0.
+ * cfg->splits, cfg->group_m, cfg->xcd_remap, cfg->strip_m and cfg->strip_n
+ * (as sgemm_f32_ex does) and fills in the rest as sgemm_f32_plan would for
+ * that variant, requested split and strips: the split actually used,
+ * k_chunk, the grid and the workspace bytes it needs.  Pure host logic.
+ * Returns hipErrorInvalidValue for invalid sizes, an id out of range, a
+ * variant not compiled for the operand layout, cfg->group_m < 0 or strips
+ * out of range.
  */
 int sgemm_f32_cfg_geometry(int transa, int transb, int M, int N, int K,
                            int lda, int ldb, int ldc, int batch, sgemm_cfg *cfg);

@@ -209,20 +209,38 @@ SHAPES = [(512, 512, 512), (2048, 2048, 2048), (3072, 3072, 3072), (8192, 8192, 
           (513, 8192, 1023), (100, 70, 50)]
 
 
+def _main_block(p, M, N):
+    """Rows and columns of C left to the tiles once the plan's edge strips
+    (at most 4 rows, 4 columns: the remainder past the last full tile row or
+    column, or all of a dimension that small) are taken out."""
+    assert 0 <= p.strip_m <= min(4, M) and 0 <= p.strip_n <= min(4, N)
+    assert p.strip_m in (0, M % p.bm) and p.strip_n in (0, N % p.bn)
+    return M - p.strip_m, N - p.strip_n
+
+
+def _check_tiles(p, M, N, batch=1):
+    Mm, Nn = _main_block(p, M, N)
+    if Mm == 0 or Nn == 0:
+        assert p.grid == 0 and p.splits == 1 and p.workspace_bytes == 0
+        return Mm, Nn
+    assert p.tiles_m == metrics.ceil_div(Mm, p.bm)
+    assert p.tiles_n == metrics.ceil_div(Nn, p.bn)
+    assert p.grid == p.tiles_m * p.tiles_n * p.splits * batch
+    return Mm, Nn
+
+
 @pytest.mark.parametrize("M,N,K", SHAPES)
 def test_plan_geometry(lib, M, N, K):
     for cus in (256, 80):
         for ws in (0, 1 << 40):
             p = sg.sgemm_f32_plan(M, N, K, max(K, 1), N, N, cus, workspace_bytes=ws)
             assert p.kernel == sg.binding.SGEMM_KERNEL_MFMA
-            assert p.tiles_m == metrics.ceil_div(M, p.bm)
-            assert p.tiles_n == metrics.ceil_div(N, p.bn)
-            assert p.grid == p.tiles_m * p.tiles_n * p.splits
+            Mm, Nn = _check_tiles(p, M, N)
             assert p.threads == 64 * p.waves_m * p.waves_n
             assert p.group_m > 0 and p.xcd_remap == 1
             if ws == 0:
                 assert p.splits == 1 and p.workspace_bytes == 0
-            _check_split(p, M, N, K, 1)
+            _check_split(p, Mm, Nn, K, 1)
 
 
 def _check_split(p, M, N, K, batch):
@@ -250,12 +268,55 @@ def test_selector_prefers_full_waves(lib):
 
 def test_selector_unaligned_rows(lib):
     """Rows that are not 16-byte aligned (ld = 4099) cannot take 16-byte
-    direct loads; the 192 x 192 tile with 4-byte direct loads serves them
-    (one launch, no workspace needed), for plain and transposed A."""
+    direct loads: a 4-byte direct-load tile serves them.  At 4099^3 the
+    tiles cover the 4096^2 block exactly (whole rounds), and the last 3 rows
+    and 3 columns go to the strip kernel (no workspace needed), for every
+    layout."""
     for ta in (0, 1):
-        p = sg.sgemm_f32_plan(4099, 4099, 4099, 4099, 4099, 4099, 256, ta, 0, 1, 0)
-        assert (p.bm, p.bn, p.splits) == (192, 192, 1)
-        assert sg.sgemm_f32_variant_ops(p.id) & (1 << ta)
+        for tb in (0, 1):
+            p = sg.sgemm_f32_plan(4099, 4099, 4099, 4099, 4099, 4099, 256, ta, tb, 1, 0)
+            assert sg.sgemm_f32_variant(p.id).bm == p.bm and p.splits == 1
+            assert (p.strip_m, p.strip_n) == (3, 3)
+            assert p.grid * p.bm * p.bn == 4096 * 4096 and p.grid % 256 == 0
+            assert sg.sgemm_f32_variant_ops(p.id) & (1 << (ta + 2 * tb))
+    # without an edge a few rows wide there is no strip
+    p = sg.sgemm_f32_plan(4000, 4000, 4000, 4001, 4001, 4000, 256)
+    assert (p.strip_m, p.strip_n) == (0, 0)
+
+
+def test_selector_strips(lib):
+    """A few rows or columns past the last full tile go to the strip kernel
+    when a tile row of them would cost a round; products with at most 4 rows
+    or columns run on the strip kernel alone."""
+    p = sg.sgemm_f32_plan(8196, 8192, 8192, 8192, 8192, 8192, 256)
+    assert (p.strip_m, p.strip_n, p.bm, p.grid) == (4, 0, 256, 1024)
+    p = sg.sgemm_f32_plan(2049, 2050, 2048, 2048, 2052, 2050, 256)
+    assert (p.strip_m, p.strip_n) == (1, 2) and p.grid * p.bm * p.bn == 2048 * 2048
+    for M, N in [(1, 4096), (4, 4096), (4096, 1), (4096, 3), (1, 1), (3, 2)]:
+        for ta in (0, 1):
+            for tb in (0, 1):
+                p = sg.sgemm_f32_plan(M, N, 4096, M if ta else 4096, 4096 if tb else N, N, 256,
+                                      ta, tb)
+                assert p.grid == 0, (M, N)
+                assert (p.strip_m == M) or (p.strip_n == N)
+
+
+def test_cfg_geometry_of_forced_strips(lib):
+    cfg = sg.SgemmCfg()
+    cfg.id, cfg.group_m, cfg.xcd_remap = 11, 8, 1
+    for sm, sn in [(0, 0), (1, 0), (0, 4), (3, 3), (4, 4)]:
+        cfg.strip_m, cfg.strip_n = sm, sn
+        g = sg.sgemm_f32_cfg_geometry(cfg, 0, 0, 1000, 700, 300, 300, 700, 700)
+        assert (g.strip_m, g.strip_n) == (sm, sn)
+        assert g.tiles_m == metrics.ceil_div(1000 - sm, 256)
+        assert g.tiles_n == metrics.ceil_div(700 - sn, 256)
+    cfg.strip_m, cfg.strip_n = 3, 0
+    g = sg.sgemm_f32_cfg_geometry(cfg, 0, 0, 3, 700, 300, 300, 700, 700)
+    assert g.grid == 0 and g.splits == 1
+    for sm, sn in [(5, 0), (0, 5), (-1, 0), (4, 0)]:
+        cfg.strip_m, cfg.strip_n = sm, sn
+        with pytest.raises(sg.SgemmError):
+            sg.sgemm_f32_cfg_geometry(cfg, 0, 0, 3 if sm == 4 else 100, 700, 300, 300, 700, 700)
 
 
 def test_selector_splits_k_for_few_tiles(lib):
@@ -318,12 +379,12 @@ def test_plan_invariants_random(lib):
         cus = int(rng.choice([256, 304, 80]))
         p = sg.sgemm_f32_plan(M, N, K, lda, ldb, ldc, cus, ta, tb, batch, ws)
         assert sg.sgemm_f32_variant_ops(p.id) & (1 << (ta + 2 * tb))
-        assert p.tiles_m == metrics.ceil_div(M, p.bm) and p.tiles_n == metrics.ceil_div(N, p.bn)
-        assert p.grid == p.tiles_m * p.tiles_n * p.splits * batch
+        Mm, Nn = _check_tiles(p, M, N, batch)
         assert p.workspace_bytes <= ws
-        _check_split(p, M, N, K, batch)
+        _check_split(p, Mm, Nn, K, batch)
         cfg = sg.SgemmCfg()
         cfg.id, cfg.splits, cfg.group_m, cfg.xcd_remap = p.id, p.splits, p.group_m, p.xcd_remap
+        cfg.strip_m, cfg.strip_n = p.strip_m, p.strip_n
         g = sg.sgemm_f32_cfg_geometry(cfg, ta, tb, M, N, K, lda, ldb, ldc, batch)
         assert (g.splits, g.k_chunk, g.grid, g.workspace_bytes) == \
             (p.splits, p.k_chunk, p.grid, p.workspace_bytes)
