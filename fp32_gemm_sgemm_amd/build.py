@@ -34,7 +34,7 @@ def _hipcc(out, sources, save_temps=None, verbose=False, extra=()):
     cmd = [HIPCC, *FLAGS, *extra]
     if save_temps:
         os.makedirs(save_temps, exist_ok=True)
-        cmd += ["-save-temps=obj", "-Rpass-analysis=kernel-resource-usage"]
+        cmd += ["-save-temps=cwd", "-Rpass-analysis=kernel-resource-usage"]
     cmd += ["-o", out + ".tmp", *sources]
     if verbose:
         print(" ".join(cmd), flush=True)

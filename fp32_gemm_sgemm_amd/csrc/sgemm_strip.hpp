@@ -28,13 +28,16 @@
 //
 // big is read in one of two storage orders:
 //   XC ("x contiguous"): big(x, k) = big[k * ld_big + x] (B in a row strip,
-//       a transposed A in a column strip).  Lanes run along x, 4 floats each;
-//       a workgroup covers 32 x, and its 64 K phases are 8 lane groups in
-//       each of 8 waves.
+//       a transposed A in a column strip).  Lanes run along x, 4 floats each,
+//       so 8 lanes read one 128-byte row segment; a workgroup covers 32 x, and
+//       its 128 K phases are the 8 lane groups of each of 16 waves.
 //   KC ("k contiguous"): big(x, k) = big[x * ld_big + k] (a transposed B in a
 //       row strip, A in a column strip).  Lanes run along k, 4 floats each; a
 //       wave reads 4 rows, and a workgroup covers 16 rows in 4 row groups
-//       times 2 K phases.
+//       times 4 K phases.
+// Both keep many loads in flight per compute unit (one workgroup of 16 waves
+// each, several independent 16-byte loads per lane), which is what a
+// streaming kernel's rate depends on.
 #pragma once
 
 #include "common.hpp"
@@ -42,8 +45,9 @@
 namespace sgemm {
 
 constexpr int kStripMax = 4;         // rows (or columns) of C one strip may hold
-constexpr int kStripThreads = 512;   // 8 waves
-constexpr int kStripKChunk = 2048;   // K values of the small operand staged at once
+constexpr int kStripThreads = 1024;  // 16 waves
+constexpr int kStripWaves = kStripThreads / 64;
+constexpr int kStripKChunk = 4608;   // K values of the small operand staged at once
 constexpr int kStripXcWidth = 32;    // x per workgroup, XC order
 constexpr int kStripKcWidth = 16;    // x per workgroup, KC order
 
@@ -73,7 +77,8 @@ __device__ __forceinline__ void strip_block(const Strip &s, int wg, int K, int z
 {
     const float *__restrict__ big = s.big + z * s.batch_big;
     const float *__restrict__ small = s.small + z * s.batch_small;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: KC rows in SGPRs
     const int X = s.X;
     constexpr int XB = KC ? kStripKcWidth : kStripXcWidth;
     const int x0 = wg * XB;
@@ -86,8 +91,8 @@ __device__ __forceinline__ void strip_block(const Strip &s, int wg, int K, int z
         for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
 
     // XC: lane group kr (8 lanes, 32 consecutive x) of wave w takes k = kr + 8w
-    // (mod 64).  KC: wave w reads rows x0 + 4*(w%4) .. +3 at k = 4*lane +
-    // 256*(w/4) (mod 512); rows past X are clamped to X-1 (read, never stored).
+    // (mod 128).  KC: wave w reads rows x0 + 4*(w%4) .. +3 at k = 4*lane +
+    // 256*(w/4) (mod 1024); rows past X are clamped to X-1 (read, never stored).
     const int xq = lane & 7, kr = lane >> 3;
     const int xc = x0 + 4 * xq;
     const bool x_full = xc + 3 < X;
@@ -102,22 +107,29 @@ __device__ __forceinline__ void strip_block(const Strip &s, int wg, int K, int z
     for (int c0 = 0; c0 < K; c0 += kStripKChunk) {
         const int clen = min(K - c0, kStripKChunk);
         for (int k = tid; k < kStripKChunk; k += kStripThreads) {
-            f32x4 v;
+            f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (k < clen) {
+                const float *q = small + (int64_t)(c0 + k) * s.s_k;
+                if (s.s_y == 1 && s.r == 4) {
+                    v = *reinterpret_cast<const f32x4u *>(q);
+                } else {
 #pragma unroll
-            for (int y = 0; y < 4; ++y)
-                v[y] = (y < s.r && k < clen) ? small[y * s.s_y + (int64_t)(c0 + k) * s.s_k] : 0.0f;
+                    for (int y = 0; y < 4; ++y) v[y] = y < s.r ? q[y * s.s_y] : 0.0f;
+                }
+            }
             stage[k] = v;
         }
         __syncthreads();
         if constexpr (KC) {
-#pragma unroll 2
-            for (int kk = 256 * kp + 4 * lane; kk < clen; kk += 512) {
+            // quads wholly inside K, two in flight; then at most one quad per
+            // lane (in the last chunk) that reaches past K, masked
+            auto quad = [&](int kk, bool masked) {
                 const int k = c0 + kk;
                 f32x4 sv[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) sv[e] = stage[kk + e];
                 f32x4 v[4];
-                if (k + 3 < K) {
+                if (!masked) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const f32x4u *>(rows[i] + k);
                 } else {
@@ -132,12 +144,17 @@ __device__ __forceinline__ void strip_block(const Strip &s, int wg, int K, int z
                     for (int e = 0; e < 4; ++e)
 #pragma unroll
                         for (int y = 0; y < 4; ++y) acc[i][y] += v[i][e] * sv[e][y];
-            }
+            };
+            const int kfull = min(clen, K - c0 - 3);  // kk < kfull: k + 3 < K
+            int kk = 256 * kp + 4 * lane;
+#pragma unroll 2
+            for (; kk < kfull; kk += 1024) quad(kk, false);
+            if (kk < clen) quad(kk, true);
         } else {
             const float *p = big + (int64_t)(c0 + kr + 8 * wave) * s.ld_big + xc;
-            const int64_t step = 64 * s.ld_big;
-#pragma unroll 4
-            for (int kk = kr + 8 * wave; kk < clen; kk += 64, p += step) {
+            const int64_t step = 128 * s.ld_big;
+#pragma unroll 8
+            for (int kk = kr + 8 * wave; kk < clen; kk += 128, p += step) {
                 f32x4 v;
                 if (x_full) {
                     v = *reinterpret_cast<const f32x4u *>(p);
@@ -177,7 +194,9 @@ __device__ __forceinline__ void strip_block(const Strip &s, int wg, int K, int z
         if (tid < XB * 4) {
             const int xi = tid >> 2, y = tid & 3;
             const int g = xi >> 2, i = xi & 3;
-            const float sum = red[g * 16 + i * 4 + y] + red[(g + 4) * 16 + i * 4 + y];
+            float sum = red[g * 16 + i * 4 + y];
+#pragma unroll
+            for (int q = 1; q < kStripWaves / 4; ++q) sum += red[(g + 4 * q) * 16 + i * 4 + y];
             if (x0 + xi < X && y < s.r) {
                 float *p = out + (int64_t)(x0 + xi) * s.o_x + (int64_t)y * s.o_y;
                 *p = beta != 0.0f ? alpha * sum + beta * *p : alpha * sum;
@@ -202,7 +221,7 @@ __device__ __forceinline__ void strip_block(const Strip &s, int wg, int K, int z
             const int q = xi >> 2, e = xi & 3;
             float sum = red[q * 16 + y * 4 + e];
 #pragma unroll
-            for (int w = 1; w < kStripThreads / 64; ++w) sum += red[(w * 8 + q) * 16 + y * 4 + e];
+            for (int w = 1; w < kStripWaves; ++w) sum += red[(w * 8 + q) * 16 + y * 4 + e];
             if (x0 + xi < X && y < s.r) {
                 float *p = out + (int64_t)(x0 + xi) * s.o_x + (int64_t)y * s.o_y;
                 *p = beta != 0.0f ? alpha * sum + beta * *p : alpha * sum;

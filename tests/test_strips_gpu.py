@@ -29,34 +29,39 @@ def with_strips(vid, sm, sn, splits=1):
 @pytest.mark.parametrize("ta,tb", LAYOUTS)
 def test_forced_strips_every_layout(ta, tb):
     """Forced strips of 1-4 rows and columns beside tiles of two families,
-    on a shape with ragged tiles and K past one staged chunk (2048) and not a
-    multiple of 4, with padded strides and an unaligned start."""
-    M, N, K = 517, 389, 2053
+    on a shape with ragged tiles and K past one staged chunk of the small
+    operand (4608) and not a multiple of 4, with padded strides and an
+    unaligned start."""
+    M, N, K = 517, 389, 4621
     A, B = inputs.make_operands(M, N, K, seed=300 + ta + 2 * tb)
     As, Bs = stored(A, ta), stored(B, tb)
+    ref, absb = oracle.gemm_ref(As, Bs, ta, tb)
     for vid in (11, 20):
         for sm, sn in [(1, 0), (0, 3), (4, 4), (3, 1), (2, 2)]:
             for pad, shift in [((0, 0, 0), (0, 0, 0)), ((3, 1, 5), (1, 1, 1))]:
                 note(f"strips ta={ta} tb={tb} variant {vid} sm={sm} sn={sn} pad={pad}")
                 C = run_general(As, Bs, ta, tb, cfg=with_strips(vid, sm, sn), pad=pad,
                                 shift=shift)
-                check_general(C, As, Bs, ta, tb)
+                rep = oracle.compare(C, ref, absb)
+                assert rep["n_bad"] == 0, rep
 
 
 @pytest.mark.parametrize("ta,tb", LAYOUTS)
-@pytest.mark.parametrize("M,N", [(1, 1000), (3, 777), (4, 64), (1000, 1), (700, 3), (2, 2),
-                                 (1, 1)])
-def test_strip_only_products(ta, tb, M, N):
+@pytest.mark.parametrize("M,N,K", [(1, 1000, 4100), (3, 777, 9301), (4, 64, 4100),
+                                   (1000, 1, 4100), (700, 3, 9301), (2, 2, 4100), (1, 1, 1),
+                                   (4, 33, 4608)])
+def test_strip_only_products(ta, tb, M, N, K):
     """Products with at most 4 rows or columns go to the strip kernel alone
-    (no tiles), through the default selector."""
-    K = 4100
+    (no tiles), through the default selector; K within one staged chunk of
+    the small operand, exactly one, and past two."""
     A, B = inputs.make_operands(M, N, K, seed=310 + M + N)
     As, Bs = stored(A, ta), stored(B, tb)
     note(f"strip-only ta={ta} tb={tb} {M}x{N}x{K}")
     C = run_general(As, Bs, ta, tb)
     check_general(C, As, Bs, ta, tb)
-    q = sg.sgemm_f32_plan(M, N, K, M if ta else K, K if tb else N, N, 256, ta, tb)
-    assert q.grid == 0 and (q.strip_m == M or q.strip_n == N)
+    if K >= 4096:
+        q = sg.sgemm_f32_plan(M, N, K, M if ta else K, K if tb else N, N, 256, ta, tb)
+        assert q.grid == 0 and (q.strip_m == M or q.strip_n == N)
 
 
 @pytest.mark.parametrize("alpha,beta", [(1.5, -0.75), (-2.0, 0.0), (0.25, 2.0)])
