@@ -38,8 +38,10 @@ One JSON line is printed.  Besides the driver's fields it holds:
                 configuration and the one-tile 128 x 128 x 32768 product with
                 and without a workspace (K split across workgroups), the
                 transposed-operand layouts at 8192^3 and 3072^3, strided
-                batches of attention-like products, and the 1024 x 8192 x 8192
-                row band one GPU would run if 8192^3 were split over 8 GPUs.
+                batches of attention-like products, the 1024 x 8192 x 8192
+                row band one GPU would run if 8192^3 were split over 8 GPUs,
+                and shapes whose few edge rows or columns (or all of them, for
+                products of 1 row or column) go to the strip kernel.
   mfma_probe    the sustained v_mfma_f32_32x32x2_f32 rate on register operands
                 (the matrix-core ceiling at the chip's actual clock), and the
                 headline's fraction of it.
@@ -198,7 +200,8 @@ def configs(torch, sg, steps, warm_ms, cus, peak):
         tf = w.flops / (ms * 1e-3) / 1e12
         out.append(dict(workload=name, value=round(tf, 3), unit="TFLOP/s", ms=round(ms, 5),
                         frac_of_fp32_matrix_peak=round(tf / peak, 4), variant=plan.id,
-                        tile=f"{plan.bm}x{plan.bn}x{plan.bk}"))
+                        tile=f"{plan.bm}x{plan.bn}x{plan.bk}",
+                        strips=[plan.strip_m, plan.strip_n]))
         del A, B, C
     torch.cuda.empty_cache()
     return out
@@ -223,7 +226,9 @@ def extras(torch, sg, steps, warm_ms, cus, peak):
         tf = flops / (ms * 1e-3) / 1e12
         out.append(dict(name=name, value=round(tf, 3), unit="TFLOP/s", ms=round(ms, 5),
                         frac_of_fp32_matrix_peak=round(tf / peak, 4), variant=plan.id,
-                        tile=f"{plan.bm}x{plan.bn}x{plan.bk}", splits=plan.splits, **kw))
+                        tile=f"{plan.bm}x{plan.bn}x{plan.bk}" if plan.grid else "none",
+                        splits=plan.splits,
+                        strips=[plan.strip_m, plan.strip_n], **kw))
 
     # K split across workgroups: the small configuration and one tile with long K
     w = inputs.WORKLOADS["sgemm_512x512x512_uniform_seed0"]
@@ -295,6 +300,27 @@ def extras(torch, sg, steps, warm_ms, cus, peak):
                                                 C.data_ptr(), N, h)), steps, warm_ms)
     record("row-band shard 1024x8192x8192 (8192^3 over 8 GPUs)", 2.0 * M * N * K, ms, plan)
     del A, B, C
+    torch.cuda.empty_cache()
+
+    # edge strips: a few rows or columns past the last full tile, and products
+    # of at most 4 rows (the strip kernel alone; reported with its HBM rate:
+    # the streamed operand's bytes over the call time)
+    for name, M, N, K in [("8196x8192x8192 (4-row edge strip)", 8196, 8192, 8192),
+                          ("2051^3 (3-row and 3-column strips, ld 2051)", 2051, 2051, 2051),
+                          ("513x8192x1023 (lda 1023)", 513, 8192, 1023),
+                          ("1x8192x8192 (vector-shaped: strip kernel)", 1, 8192, 8192),
+                          ("8192x1x8192 (vector-shaped: strip kernel)", 8192, 1, 8192)]:
+        A, B = operand((M, K)), operand((K, N))
+        C = torch.empty((M, N), device="cuda")
+        plan = sg.sgemm_f32_plan(M, N, K, K, N, N, cus)
+        h = stream.cuda_stream
+        ms = time_call(torch, lambda: chk(sg.sgemm_f32(M, N, K, A.data_ptr(), K, B.data_ptr(), N,
+                                                    C.data_ptr(), N, h)), steps, warm_ms)
+        kw = {}
+        if plan.grid == 0:
+            kw["GB_per_s"] = round(4.0 * K * max(M, N) / (ms * 1e-3) / 1e9, 1)
+        record(name, 2.0 * M * N * K, ms, plan, **kw)
+        del A, B, C
     torch.cuda.empty_cache()
     return out
 

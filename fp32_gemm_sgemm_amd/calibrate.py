@@ -1,0 +1,163 @@
+"""Measure the figures the selector's cost model uses, on the GPU at hand.
+
+    python -m fp32_gemm_sgemm_amd.calibrate [--variants 11,13,...] [--ms 150]
+
+For each selectable variant (or the ones listed) three shapes are timed with
+the variant forced, no K split and no strips, K = 4096 (4099 for the last):
+
+  full       32 BM x 32 BN      four rounds of full tiles on 256 CUs, rows
+                                16-byte aligned
+  one        16 BM x 16 BN      one round, one workgroup per CU
+  unaligned  (32 BM - 5) x (32 BN - 5), K = 4099: rows not 16-byte aligned
+
+and the cost model of select.hpp,
+
+  t = rounds * (2.5 us + slices * 2 BM BN BK / (614.4 FLOP/ns * eff)),
+
+is inverted for eff (x1000), the three numbers each variant carries in the
+table of sgemm.hip.  The strip kernel is timed alone on two sizes of a
+4-row product in both storage orders of its streamed operand, and its fixed
+cost and streaming rate are fitted (kStripFixedNs, kStripBytesPerNs).
+
+Each timing is the median of HIP events around single launches after a
+time-based warm-up (the chip needs about 0.1 s of load to reach its clock).
+Prints one JSON line per measurement and, at the end, the table lines.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+CU_FLOP_PER_NS = 157.3e3 / 256.0
+TILE_FIXED_NS = 2500.0
+CUS = 256
+
+
+def _time(torch, fn, warm_ms, reps=15):
+    torch.cuda.synchronize()
+    t0 = time.time()
+    while (time.time() - t0) * 1000 < warm_ms:
+        fn()
+        torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(s)
+    for i in range(reps):
+        fn()
+        ev[i + 1].record(s)
+    torch.cuda.synchronize()
+    t = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
+    return t[reps // 2] * 1e6  # ns
+
+
+def _operands(torch, M, N, K, ld_pad):
+    lda, ldb = K + ld_pad, N + ld_pad
+    A = torch.empty(M * lda, device="cuda").uniform_(-1, 1).view(M, lda)[:, :K]
+    B = torch.empty(K * ldb, device="cuda").uniform_(-1, 1).view(K, ldb)[:, :N]
+    C = torch.empty((M, N), device="cuda")
+    return A, B, C
+
+
+def eff_from_time(t_ns, bm, bn, bk, M, N, K):
+    tiles = -(-M // bm) * -(-N // bn)
+    rounds = -(-tiles // CUS)
+    slices = -(-K // bk)
+    per_round = t_ns / rounds - TILE_FIXED_NS
+    return 1000.0 * slices * 2.0 * bm * bn * bk / (CU_FLOP_PER_NS * per_round)
+
+
+def calibrate_variant(torch, sg, vid, warm_ms):
+    v = sg.sgemm_f32_variant(vid)
+    bm, bn, bk = v.bm, v.bn, v.bk
+    shapes = {
+        "full": (32 * bm, 32 * bn, 4096, 0),
+        "one": (16 * bm, 16 * bn, 4096, 0),
+        # odd leading dimensions: rows not 16-byte aligned
+        "unaligned": (32 * bm - 5, 32 * bn - 5, 4099, 0),
+    }
+    out = {}
+    for name, (M, N, K, pad) in shapes.items():
+        A, B, C = _operands(torch, M, N, K, pad)
+        cfg = sg.SgemmCfg()
+        cfg.id, cfg.group_m, cfg.xcd_remap, cfg.splits = vid, 8, 1, 1
+        t = _time(torch, lambda: sg.sgemm(A, B, out=C, cfg=cfg, workspace=False), warm_ms)
+        e = eff_from_time(t, bm, bn, bk, M, N, K)
+        out[name] = round(e)
+        print(json.dumps({"variant": vid, "tile": f"{bm}x{bn}x{bk}", "shape": name,
+                          "M": M, "N": N, "K": K, "us": round(t / 1e3, 2),
+                          "tflops": round(2.0 * M * N * K / t / 1e3, 2), "eff": round(e)}),
+              flush=True)
+        del A, B, C
+    return out
+
+
+def calibrate_strips(torch, sg, warm_ms):
+    """Fixed cost (ns) and rate (bytes/ns) of the strip kernel: a 4-row
+    product streams op(B) (x-contiguous, or k-contiguous when transposed)."""
+    pts = []
+    for tb in (0, 1):
+        for n in (2048, 8192):
+            M, N, K = 4, n, n
+            A = torch.empty((M, K), device="cuda").uniform_(-1, 1)
+            B = torch.empty((N, K) if tb else (K, N), device="cuda").uniform_(-1, 1)
+            C = torch.empty((M, N), device="cuda")
+            cfg = sg.SgemmCfg()
+            cfg.id, cfg.group_m, cfg.xcd_remap, cfg.strip_m = 11, 8, 1, M
+            t = _time(torch, lambda: sg.sgemm(A, B, out=C, cfg=cfg, transb=bool(tb),
+                                              workspace=False), warm_ms)
+            nbytes = 4.0 * K * N
+            pts.append((tb, nbytes, t))
+            print(json.dumps({"strip": "row", "transb": tb, "M": M, "N": N, "K": K,
+                              "us": round(t / 1e3, 2), "GB/s": round(nbytes / t, 1)}),
+                  flush=True)
+    fits = []
+    for tb in (0, 1):
+        (b0, t0), (b1, t1) = [(b, t) for (o, b, t) in pts if o == tb]
+        rate = (b1 - b0) / (t1 - t0)
+        fits.append((t0 - b0 / rate, rate))
+    fixed = max(f for f, _ in fits)
+    rate = min(r for _, r in fits)
+    return fixed, rate
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--variants", default="",
+                    help="comma-separated variant ids (default: every selectable one)")
+    ap.add_argument("--ms", type=float, default=150.0, help="warm-up per measurement, ms")
+    ap.add_argument("--no-strips", action="store_true")
+    args = ap.parse_args(argv)
+    import torch
+    import fp32_gemm_sgemm_amd as sg
+    if not torch.cuda.is_available():
+        raise SystemExit("calibration needs a GPU")
+    sg.load()
+    if args.variants:
+        vids = [int(x) for x in args.variants.split(",")]
+    else:
+        vids = [i for i in range(sg.sgemm_f32_num_variants()) if _is_mfma(sg, i)]
+    table = {}
+    for vid in vids:
+        table[vid] = calibrate_variant(torch, sg, vid, args.ms)
+    for vid, e in table.items():
+        print(f"variant {vid}: ({e['full']}, {e['one']}, {e['unaligned']})", flush=True)
+    if not args.no_strips:
+        fixed, rate = calibrate_strips(torch, sg, args.ms)
+        print(f"strips: kStripFixedNs = {fixed:.0f}, kStripBytesPerNs = {rate:.0f}", flush=True)
+    return 0
+
+
+def _is_mfma(sg, vid):
+    """Matrix-core variants (the ones the table rates; the vector-FMA
+    comparison kernel is measured only when named with --variants)."""
+    return sg.sgemm_f32_variant(vid).kernel == sg.binding.SGEMM_KERNEL_MFMA
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -222,11 +222,13 @@ inline double estimate_ns(const Variant &v, const Problem &p, int splits, int k_
 
 // The strip kernel: one launch for both strips, bound by streaming the
 // operand each strip reads whole (op(B) for the row strip, the first M - sm
-// rows of op(A) for the column strip).  Measured on MI355X: 67 MB strips in
-// 21-27 us, 268 MB in 62-72 us, both strips of 4099^3 (134 MB) in about
-// 48 us: about 10 us of fixed cost and 4.4 TB/s.
-constexpr double kStripFixedNs = 10000.0;
-constexpr double kStripBytesPerNs = 4400.0;
+// rows of op(A) for the column strip).  Fitted on MI355X to 4-row products
+// of 2048^2 and 8192^2 streamed elements (fp32_gemm_sgemm_amd.calibrate):
+// about 10.6 us of fixed cost, then 6.9 TB/s when the streamed operand's rows
+// run along the strip (x-contiguous) and 5.1 TB/s when they run along k; the
+// slower rate is used.
+constexpr double kStripFixedNs = 10500.0;
+constexpr double kStripBytesPerNs = 5100.0;
 
 inline double strip_ns(const Problem &p, int sm, int sn)
 {

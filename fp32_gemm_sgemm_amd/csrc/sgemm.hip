@@ -85,12 +85,14 @@ constexpr int kCrossSliceAgpr = 6;
 // variant's tile): over four rounds of full tiles with 16-byte aligned rows
 // (32 BM x 32 BN), over one round, one workgroup per CU (16 BM x 16 BN), and
 // with rows that are not 16-byte aligned (32 BM - 5 x 32 BN - 5, K = 4099).
+// `python -m fp32_gemm_sgemm_amd.calibrate` measures them; the figures below
+// come from one such run on MI355X.
 // The 4-byte direct-load variants serve only rows that are not 16-byte
 // aligned.  0 keeps a variant out of automatic selection (comparison
 // kernels, dominated tiles).
 const Variant kVariants[] = {
-    mfma_variant<256, 256, 16, 4, 2, 0>(897, 889, 700),    // 0: 8 waves of 64x128
-    mfma_variant<128, 128, 16, 2, 2, 0>(860, 767, 595),    // 1: 4 waves of 64x64
+    mfma_variant<256, 256, 16, 4, 2, 0>(896, 888, 699),    // 0: 8 waves of 64x128
+    mfma_variant<128, 128, 16, 2, 2, 0>(857, 760, 591),    // 1: 4 waves of 64x64
     mfma_variant<128, 128, 32, 2, 2, 1>(0, 0, 0),          // 2: 4 waves of 64x64, BK 32
     mfma_variant<128, 256, 16, 2, 2, 0>(0, 0, 0),          // 3: 4 waves of 64x128
     mfma_variant<256, 128, 16, 4, 1, 0>(0, 0, 0),          // 4: 4 waves of 64x128
@@ -98,20 +100,20 @@ const Variant kVariants[] = {
     mfma_variant<128, 128, 16, 2, 2, -1>(0, 0, 0),         // 6: plain order (comparison)
     valu_variant(),                                        // 7: vector-FMA comparison
     mfma_variant<192, 192, 16, 2, 6, 0>(0, 0, 0),          // 8: 12 waves of 96x32
-    mfma_variant<192, 192, 32, 2, 6, 1>(893, 883, 718),    // 9: 12 waves of 96x32, BK 32
+    mfma_variant<192, 192, 32, 2, 6, 1>(888, 880, 714),    // 9: 12 waves of 96x32, BK 32
     dl_variant<256, 256, 16, 4, 2, 4, 1>(0, 0, 0),         // 10: direct loads, 4 stages
-    dl_variant<256, 256, 32, 4, 2, 2, kAllOps, false, kCrossSliceAgpr>(966, 959, 660),  // 11: direct loads, 2 stages of BK 32
-    dl_variant<128, 128, 32, 2, 2, 3, kAllOps>(778, 770, 404),  // 12: direct loads
-    dl_variant<192, 192, 32, 2, 6, 2, kAllOps, false, kCrossSliceAgpr>(954, 947, 611),  // 13: direct loads
+    dl_variant<256, 256, 32, 4, 2, 2, kAllOps, false, kCrossSliceAgpr>(963, 955, 661),  // 11: direct loads, 2 stages of BK 32
+    dl_variant<128, 128, 32, 2, 2, 3, kAllOps>(776, 764, 403),  // 12: direct loads
+    dl_variant<192, 192, 32, 2, 6, 2, kAllOps, false, kCrossSliceAgpr>(953, 944, 610),  // 13: direct loads
     dl_variant<256, 256, 16, 4, 2, 3, 1>(0, 0, 0),         // 14: direct loads, 3 stages
-    dl_variant<128, 128, 32, 4, 2, 2, kAllOps, false, kCrossSliceAgpr>(955, 931, 661),  // 15: direct loads, 8 waves of 32x64
-    mfma_variant<128, 128, 16, 2, 4, 0>(831, 828, 678),    // 16: 8 waves of 64x32
-    mfma_variant<128, 128, 32, 2, 4, 1>(821, 800, 752),    // 17: 8 waves of 64x32, BK 32
-    dl_variant<192, 192, 32, 2, 6, 2, kAllOps, true, kCrossSliceAgpr>(948, 940, 945),  // 18: 4-byte direct loads
-    mfma_variant<64, 64, 32, 2, 2, 1>(779, 605, 597),      // 19: 4 waves of 32x32
-    dl_variant<64, 64, 32, 2, 2, 2, kAllOps, false, kCrossSliceAgpr>(943, 651, 507),  // 20: direct loads, 4 waves of 32x32
-    dl_variant<64, 64, 32, 2, 2, 2, kAllOps, true, kCrossSliceAgpr>(854, 640, 902),  // 21: 4-byte direct loads
-    dl_variant<128, 128, 32, 4, 2, 2, kAllOps, true, kCrossSliceAgpr>(950, 925, 950),  // 22: 4-byte direct loads, 8 waves of 32x64
+    dl_variant<128, 128, 32, 4, 2, 2, kAllOps, false, kCrossSliceAgpr>(952, 923, 663),  // 15: direct loads, 8 waves of 32x64
+    mfma_variant<128, 128, 16, 2, 4, 0>(830, 826, 676),    // 16: 8 waves of 64x32
+    mfma_variant<128, 128, 32, 2, 4, 1>(821, 796, 744),    // 17: 8 waves of 64x32, BK 32
+    dl_variant<192, 192, 32, 2, 6, 2, kAllOps, true, kCrossSliceAgpr>(946, 939, 944),  // 18: 4-byte direct loads
+    mfma_variant<64, 64, 32, 2, 2, 1>(775, 591, 591),      // 19: 4 waves of 32x32
+    dl_variant<64, 64, 32, 2, 2, 2, kAllOps, false, kCrossSliceAgpr>(935, 636, 505),  // 20: direct loads, 4 waves of 32x32
+    dl_variant<64, 64, 32, 2, 2, 2, kAllOps, true, kCrossSliceAgpr>(917, 625, 875),  // 21: 4-byte direct loads
+    dl_variant<128, 128, 32, 4, 2, 2, kAllOps, true, kCrossSliceAgpr>(947, 918, 945),  // 22: 4-byte direct loads, 8 waves of 32x64
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
