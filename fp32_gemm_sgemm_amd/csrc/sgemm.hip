@@ -375,6 +375,10 @@ hipError_t launch_strips(const Call &c, int sm, int sn, hipStream_t stream)
         const int w = p.transa ? sgemm::kStripXcWidth : sgemm::kStripKcWidth;
         cs.wgs = (int)sgemm::ceil_div_ll(m_main, w);
     }
+    // An x-contiguous stream reads non-temporally when the other strip shares
+    // the launch (it keeps L2 for that strip's staged operand).
+    rs.nt = cs.wgs > 0 ? 1 : 0;
+    cs.nt = rs.wgs > 0 ? 1 : 0;
     const long long wgs = (long long)rs.wgs + cs.wgs;
     if (wgs == 0) return hipSuccess;
     if (wgs > INT_MAX) return hipErrorInvalidValue;
