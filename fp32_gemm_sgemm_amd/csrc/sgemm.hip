@@ -15,6 +15,7 @@
 #include "sgemm.h"
 #include "sgemm_mfma.hpp"
 #include "sgemm_mfma_dl.hpp"
+#include "sgemm_mfma_sk.hpp"
 #include "sgemm_reduce.hpp"
 #include "sgemm_strip.hpp"
 #include "sgemm_valu.hpp"
@@ -62,6 +63,21 @@ Variant dl_variant(int eff_permille, int eff_one_permille, int eff_unaligned_per
         v.fn[3] = reinterpret_cast<const void *>(
             &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, true, true, DW, PIPE>);
     return v;
+}
+
+// 32x32 tiles with K split across the W waves of the workgroup (every layout).
+// waves_m = W describes the waves (they share the tile and split K).
+template <int W>
+Variant sk_variant(int eff_permille, int eff_one_permille, int eff_unaligned_permille)
+{
+    typedef sgemm::SkTraits<W> T;
+    return Variant{SGEMM_KERNEL_MFMA, T::BM, T::BN, 8, W, 1, -1, 0, 0,
+                   T::NT, (int)(T::LDS_FLOATS * sizeof(float)),
+                   {reinterpret_cast<const void *>(&sgemm::sgemm_mfma_sk_kernel<W, false, false>),
+                    reinterpret_cast<const void *>(&sgemm::sgemm_mfma_sk_kernel<W, true, false>),
+                    reinterpret_cast<const void *>(&sgemm::sgemm_mfma_sk_kernel<W, false, true>),
+                    reinterpret_cast<const void *>(&sgemm::sgemm_mfma_sk_kernel<W, true, true>)},
+                   eff_permille, eff_one_permille, eff_unaligned_permille};
 }
 
 Variant valu_variant()
@@ -114,6 +130,8 @@ const Variant kVariants[] = {
     dl_variant<64, 64, 32, 2, 2, 2, kAllOps, false, kCrossSliceAgpr>(935, 636, 505),  // 20: direct loads, 4 waves of 32x32
     dl_variant<64, 64, 32, 2, 2, 2, kAllOps, true, kCrossSliceAgpr>(917, 625, 875),  // 21: 4-byte direct loads
     dl_variant<128, 128, 32, 4, 2, 2, kAllOps, true, kCrossSliceAgpr>(947, 918, 945),  // 22: 4-byte direct loads, 8 waves of 32x64
+    sk_variant<4>(546, 318, 468),                           // 23: 32x32, K split over 4 waves
+    sk_variant<16>(467, 417, 395),                          // 24: 32x32, K split over 16 waves
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 

@@ -42,7 +42,9 @@ typedef struct sgemm_cfg {
     int id;        /* variant index, 0 .. sgemm_f32_num_variants()-1 */
     int kernel;    /* SGEMM_KERNEL_MFMA or SGEMM_KERNEL_VALU */
     int bm, bn, bk;       /* workgroup tile: BM x BN outputs, BK-deep K slices */
-    int waves_m, waves_n; /* wavefront grid inside a workgroup */
+    int waves_m, waves_n; /* wavefront grid inside a workgroup (the 32 x 32
+                             variants that split K over their waves report
+                             waves_m = that count, waves_n = 1) */
     int group_m;   /* raster: tile rows per group, walked column by column
                       (0 = plain row-major order over tiles) */
     int xcd_remap; /* 1: give each XCD a contiguous run of logical tiles */
