@@ -9,6 +9,7 @@
 
 #include <limits.h>
 #include <stdint.h>
+#include <string.h>
 
 #include <mutex>
 
@@ -421,12 +422,50 @@ Call main_part(const Call &c, int sm, int sn)
     return m;
 }
 
+// The selector's inputs and its choice, remembered per thread for the last
+// few distinct calls: the search over variants, splits and strips costs about
+// 2 us of host time, which a stream of small products would pay on every call.
+struct PlanKey {
+    Problem p;
+    int cus, aligned16, lds_ok;
+    long long ws;
+};
+struct PlanEntry {
+    PlanKey key;
+    Choice choice;
+    int valid;
+};
+constexpr int kPlanCacheEntries = 8;
+thread_local PlanEntry t_plan_cache[kPlanCacheEntries];
+thread_local int t_plan_next;
+
+Choice cached_plan(const Problem &p, int cus, bool aligned16, bool lds_ok, long long ws)
+{
+    PlanKey key;
+    memset(&key, 0, sizeof(key));  // padding too: keys compare bytewise
+    key.p = p;
+    key.cus = cus;
+    key.aligned16 = aligned16 ? 1 : 0;
+    key.lds_ok = lds_ok ? 1 : 0;
+    key.ws = ws;
+    for (int i = 0; i < kPlanCacheEntries; ++i)
+        if (t_plan_cache[i].valid && memcmp(&t_plan_cache[i].key, &key, sizeof(key)) == 0)
+            return t_plan_cache[i].choice;
+    const Choice ch = sgemm::select_plan(kVariants, kNumVariants, p, cus, aligned16, lds_ok, ws);
+    PlanEntry &e = t_plan_cache[t_plan_next];
+    t_plan_next = (t_plan_next + 1) % kPlanCacheEntries;
+    e.key = key;
+    e.choice = ch;
+    e.valid = 1;
+    return ch;
+}
+
 int plan_for(const Call &c, int cus, sgemm_cfg *out)
 {
     if (!out || !sgemm::sizes_ok(c.p)) return hipErrorInvalidValue;
     const long long ws = c.ws_bytes > (size_t)LLONG_MAX ? LLONG_MAX : (long long)c.ws_bytes;
-    const Choice ch = sgemm::select_plan(kVariants, kNumVariants, c.p, cus > 0 ? cus : 256,
-                                         rows_aligned16(c), sgemm::direct_lds_ok(c.p), ws);
+    const Choice ch = cached_plan(c.p, cus > 0 ? cus : 256, rows_aligned16(c),
+                                  sgemm::direct_lds_ok(c.p), ws);
     if (ch.id < 0) return hipErrorInvalidValue;
     return sgemm::finish_cfg(kVariants[ch.id], ch.id, c.p, ch.splits, ch.strip_m, ch.strip_n, out)
                ? hipSuccess

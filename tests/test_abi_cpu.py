@@ -388,3 +388,24 @@ def test_plan_invariants_random(lib):
         g = sg.sgemm_f32_cfg_geometry(cfg, ta, tb, M, N, K, lda, ldb, ldc, batch)
         assert (g.splits, g.k_chunk, g.grid, g.workspace_bytes) == \
             (p.splits, p.k_chunk, p.grid, p.workspace_bytes)
+
+
+def test_plan_cache_returns_each_problems_own_plan(lib):
+    """The library remembers recent plans per thread; cycling through more
+    distinct problems than it keeps, with the same sizes under different
+    layouts, workspaces and CU counts, every answer equals a cold one."""
+    import itertools
+    probs = []
+    for (M, N, K), (ta, tb), ws, cus in itertools.product(
+            [(512, 512, 512), (4099, 4099, 4099), (128, 128, 32768), (3, 700, 900)],
+            [(0, 0), (1, 1)], [0, 1 << 40], [256, 80]):
+        probs.append((M, N, K, ta, tb, ws, cus))
+    def plan(M, N, K, ta, tb, ws, cus):
+        p = sg.sgemm_f32_plan(M, N, K, M if ta else K, K if tb else N, N, cus, ta, tb, 1, ws)
+        return (p.id, p.splits, p.strip_m, p.strip_n, p.grid, p.workspace_bytes)
+    first = [plan(*q) for q in probs]
+    for _ in range(3):
+        for q, want in zip(probs, first):
+            assert plan(*q) == want, q
+    for q, want in zip(reversed(probs), reversed(first)):
+        assert plan(*q) == want, q
