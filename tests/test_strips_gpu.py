@@ -156,3 +156,45 @@ def test_ragged_4099_plan_full_rows():
     ref, absb = oracle.sgemm_ref_sampled(A, B, rows, cols)
     rep = oracle.compare(C[rows, cols], ref, absb)
     assert rep["n_bad"] == 0, rep
+
+
+def test_strip_only_batches_past_one_launch():
+    """70,000 strip-only products (the strip grid's second dimension holds
+    65,535 entries per launch): every entry checked."""
+    batch, M, N, K = 70000, 2, 3, 37
+    rng = np.random.default_rng(360)
+    A = rng.uniform(-1, 1, size=(batch, M, K)).astype(np.float32)
+    B = rng.uniform(-1, 1, size=(batch, K, N)).astype(np.float32)
+    note("strip-only batch 70000")
+    q = sg.sgemm_f32_plan(M, N, K, K, N, N, 256, 0, 0, batch)
+    assert q.grid == 0
+    C = sg.sgemm_batched(torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda())
+    torch.cuda.synchronize()
+    C = C.cpu().numpy()
+    ref = np.einsum("zmk,zkn->zmn", A.astype(np.float64), B.astype(np.float64))
+    absb = np.einsum("zmk,zkn->zmn", np.abs(A.astype(np.float64)), np.abs(B.astype(np.float64)))
+    assert np.all(np.abs(C - ref) <= oracle.TOL * absb)
+
+
+@pytest.mark.parametrize("vid", [23, 24])
+def test_ksplit_tiles_with_outer_splits_batches_and_strips(vid):
+    """The 32x32 tiles that split K over their waves, combined with a split
+    across workgroups (workspace), batches with a broadcast operand, strips
+    and alpha/beta, in every layout."""
+    batch, M, N, K = 3, 67, 98, 1500
+    rng = np.random.default_rng(370 + vid)
+    for ta, tb in LAYOUTS:
+        A = rng.uniform(-1, 1, size=(batch, M, K)).astype(np.float32)
+        B = rng.uniform(-1, 1, size=(1, K, N)).astype(np.float32)
+        C0 = rng.uniform(-1, 1, size=(batch, M, N)).astype(np.float32)
+        As = np.ascontiguousarray(np.swapaxes(A, 1, 2)) if ta else A
+        Bs = np.ascontiguousarray(np.swapaxes(B, 1, 2)) if tb else B
+        cfg = with_strips(vid, 3, 2, splits=3)
+        note(f"k-split tiles variant {vid} ta={ta} tb={tb} + split 3 + strips + batch")
+        Cd = torch.from_numpy(C0.copy()).cuda()
+        sg.sgemm_batched(torch.from_numpy(As).cuda(), torch.from_numpy(Bs).cuda(), out=Cd,
+                         transa=bool(ta), transb=bool(tb), alpha=-0.5, beta=1.25, cfg=cfg)
+        torch.cuda.synchronize()
+        ref, absb = oracle.gemm_ref_batched(As, Bs, ta, tb, -0.5, 1.25, C0)
+        rep = oracle.compare(Cd.cpu().numpy(), ref, absb)
+        assert rep["n_bad"] == 0, rep
