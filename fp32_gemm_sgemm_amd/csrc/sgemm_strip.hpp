@@ -25,9 +25,9 @@
 // shuffles, then the waves in order through LDS), so a result is the same on
 // every run and no workspace is needed.  The small operand is staged through
 // LDS in chunks of K, zero for y past the strip and k past K: the 4 values of y
-// at k = 4q + e sit at 16-byte slot e * (chunk / 4) + q, so a lane that reads
-// the 4 successive k of one quad (KC) and its neighbours touch consecutive
-// slots.  The big operand is read with non-temporal loads in KC order (each
+// at k = 4q + e sit at 16-byte slot e * plane + q, so a lane that reads the 4
+// successive k of one quad (KC) and its neighbours touch consecutive slots,
+// and the planes are padded so that 8 consecutive k (XC) do not collide.  The big operand is read with non-temporal loads in KC order (each
 // element is used once, which leaves L2 to the small operand every workgroup
 // re-reads), and in XC order when the launch also holds a KC strip (measured:
 // 4099^3's strips 1% faster with them, an XC strip alone 15% slower).
@@ -54,6 +54,10 @@ constexpr int kStripMax = 4;         // rows (or columns) of C one strip may hol
 constexpr int kStripThreads = 1024;  // 16 waves
 constexpr int kStripWaves = kStripThreads / 64;
 constexpr int kStripKChunk = 4608;   // K values of the small operand staged at once
+// 16-byte slots per residue plane of the staged chunk: a quarter of the chunk
+// plus 4, so the planes start 4 banks apart and the 8 different k one XC read
+// instruction touches (k, k+1, ..., k+7) fall in distinct banks.
+constexpr int kStripPlane = kStripKChunk / 4 + 4;
 constexpr int kStripXcWidth = 32;    // x per workgroup, XC order
 constexpr int kStripKcWidth = 32;    // x per workgroup, KC order
 constexpr int kStripKcGroups = 8;    // row groups of 4 rows, KC order
@@ -130,7 +134,7 @@ __device__ __forceinline__ void strip_block(const Strip &s, int wg, int K, int z
                     for (int y = 0; y < 4; ++y) v[y] = y < s.r ? q[y * s.s_y] : 0.0f;
                 }
             }
-            stage[slot] = v;
+            stage[(slot / Q) * kStripPlane + slot % Q] = v;
         }
         __syncthreads();
         if constexpr (KC) {
@@ -140,7 +144,7 @@ __device__ __forceinline__ void strip_block(const Strip &s, int wg, int K, int z
                 const int k = c0 + kk;
                 f32x4 sv[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sv[e] = stage[e * (kStripKChunk / 4) + kk / 4];
+                for (int e = 0; e < 4; ++e) sv[e] = stage[e * kStripPlane + kk / 4];
                 f32x4 v[4];
                 if (!masked) {
 #pragma unroll
@@ -181,7 +185,7 @@ __device__ __forceinline__ void strip_block(const Strip &s, int wg, int K, int z
 #pragma unroll
                         for (int e = 0; e < 4; ++e) v[e] = xc + e < X ? p[e] : 0.0f;
                     }
-                    const f32x4 sv = stage[(kk & 3) * (kStripKChunk / 4) + (kk >> 2)];
+                    const f32x4 sv = stage[(kk & 3) * kStripPlane + (kk >> 2)];
 #pragma unroll
                     for (int y = 0; y < 4; ++y)
 #pragma unroll
@@ -257,7 +261,7 @@ __device__ __forceinline__ void strip_block(const Strip &s, int wg, int K, int z
 template <bool KC0, bool KC1>
 __global__ void __launch_bounds__(kStripThreads) sgemm_strip_kernel(StripArgs a)
 {
-    __shared__ __attribute__((aligned(16))) f32x4 stage[kStripKChunk];
+    __shared__ __attribute__((aligned(16))) f32x4 stage[4 * kStripPlane];
     const int z = a.z0 + blockIdx.y;
     const int wg = blockIdx.x;
     if (wg < a.s[0].wgs) strip_block<KC0>(a.s[0], wg, a.K, z, a.alpha, a.beta, stage);
