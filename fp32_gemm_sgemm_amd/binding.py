@@ -53,8 +53,7 @@ def load():
         pass
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(
-            f"{LIB_PATH} is not built: run `python -m fp32_gemm_sgemm_amd.build` "
-            "(or __graft_entry__.build()) first")
+            f"{LIB_PATH} is not built: run `python -m fp32_gemm_sgemm_amd.build` first")
     lib = ctypes.CDLL(LIB_PATH)
     i, p, f = ctypes.c_int, ctypes.c_void_p, ctypes.c_float
     ll, sz = ctypes.c_longlong, ctypes.c_size_t
