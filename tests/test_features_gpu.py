@@ -311,6 +311,65 @@ def test_hip_graph_capture_and_replay():
         del graph
 
 
+def _stack(host, pad, sh):
+    """A (batch, rows, cols) device view of `host` with row stride cols + pad,
+    entries 3*pad floats apart, starting `sh` floats into its buffer."""
+    b, r, c = host.shape
+    ld = c + pad
+    stride = r * ld + 3 * pad
+    buf = torch.zeros(sh + b * stride + 4, dtype=torch.float32, device="cuda")
+    view = torch.as_strided(buf, (b, r, c), (stride, ld, 1), storage_offset=sh)
+    view.copy_(torch.from_numpy(host))
+    return view
+
+
+def test_random_configurations_with_strips():
+    """40 seeded random problems whose M and N are a multiple of 32 plus 0-4
+    (or at most 4), each through the selector and through a forced variant
+    with forced strips of 0-4 rows and columns and a forced K split, in any
+    layout, with alpha/beta, batches, padded strides and shifted starts."""
+    rng = np.random.default_rng(4242)
+    nvar = sg.sgemm_f32_num_variants()
+
+    def dim():
+        if rng.random() < 0.2:
+            return int(rng.integers(1, 5))
+        return 32 * int(rng.integers(1, 9)) + int(rng.integers(0, 5))
+
+    for case in range(40):
+        M, N = dim(), dim()
+        K = int(rng.integers(1, 700))
+        ta, tb = (int(x) for x in rng.integers(0, 2, size=2))
+        batch = int(rng.choice([1, 1, 2]))
+        alpha = float(rng.choice([1.0, -0.75, 2.5]))
+        beta = float(rng.choice([0.0, 0.0, -0.5]))
+        pads = [int(x) for x in rng.integers(0, 6, size=3)]
+        shift = [int(x) for x in rng.integers(0, 2, size=3)]
+        ops = [v for v in range(nvar) if sg.sgemm_f32_variant_ops(v) & (1 << (ta + 2 * tb))]
+        Ar, Br = ((K, M) if ta else (M, K)), ((N, K) if tb else (K, N))
+        Ah = rng.uniform(-1, 1, (batch,) + Ar).astype(np.float32)
+        Bh = rng.uniform(-1, 1, (batch,) + Br).astype(np.float32)
+        C0 = rng.uniform(-1, 1, (batch, M, N)).astype(np.float32)
+        ref, absb = oracle.gemm_ref_batched(Ah, Bh, ta, tb, alpha, beta, C0)
+        vid = int(rng.choice(ops))
+        sm = int(rng.integers(0, min(4, M) + 1))
+        sn = int(rng.integers(0, min(4, N) + 1))
+        splits = int(rng.choice([1, 2, 3]))
+        for cfg in (None, "forced"):
+            if cfg == "forced":
+                cfg = forced_split(vid, splits)
+                cfg.strip_m, cfg.strip_n = sm, sn
+            note(f"random strips case {case}: {M}x{N}x{K} ta={ta} tb={tb} batch={batch} "
+                 f"alpha={alpha} beta={beta} cfg={'selector' if cfg is None else (vid, splits, sm, sn)} "
+                 f"pads={pads} shift={shift}")
+            A, B, C = _stack(Ah, pads[0], shift[0]), _stack(Bh, pads[1], shift[1]), \
+                _stack(C0, pads[2], shift[2])
+            sg.sgemm_batched(A, B, out=C, transa=ta, transb=tb, alpha=alpha, beta=beta, cfg=cfg)
+            torch.cuda.synchronize()
+            rep = oracle.compare(C.cpu().numpy(), ref, absb)
+            assert rep["n_bad"] == 0, (case, rep)
+
+
 def test_random_configurations():
     """40 seeded random problems mixing every feature: layout, alpha/beta,
     batch with gaps between entries, a forced variant compiled for the layout
