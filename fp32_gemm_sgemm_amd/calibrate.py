@@ -2,6 +2,11 @@
 
     python -m fp32_gemm_sgemm_amd.calibrate [--variants 11,13,...] [--ms 150]
 
+First the launch floor: what every launch costs beyond the model (dispatch,
+completion, the events), from one-tile products of the small-tile reference
+variant.  It is the same for every variant and so left out of the model, and
+taken off each measured time below.
+
 For each selectable variant (or the ones listed) three shapes are timed with
 the variant forced, no K split and no strips, K = 4096 (4099 for the last):
 
@@ -15,12 +20,16 @@ and the cost model of select.hpp,
   t = rounds * (2.5 us + slices * 2 BM BN BK / (614.4 FLOP/ns * eff)),
 
 is inverted for eff (x1000), the three numbers each variant carries in the
-table of sgemm.hip.  The strip kernel is timed alone on two sizes of a
+table of sgemm.hip.  The variants that split K over their waves (32 x 32
+tiles, whose L2 spill the model prices) also get their own fixed cost and
+spill factor, and are measured at K where the operands one XCD reads fit in
+its L2 (calibrate_ksplit).  The strip kernel is timed alone on two sizes of a
 4-row product in both storage orders of its streamed operand, and its fixed
 cost and streaming rate are fitted (kStripFixedNs, kStripBytesPerNs).
 
-Each timing is the median of HIP events around single launches after a
-time-based warm-up (the chip needs about 0.1 s of load to reach its clock).
+Each timing is the median of HIP events around single launches queued behind
+a GPU sleep, after a time-based warm-up (the chip needs about 0.1 s of load
+to reach its clock).
 Prints one JSON line per measurement and, at the end, the table lines.
 """
 import argparse
@@ -37,9 +46,31 @@ if ROOT not in sys.path:
 CU_FLOP_PER_NS = 157.3e3 / 256.0
 TILE_FIXED_NS = 2500.0
 CUS = 256
+REF_VARIANT = 20  # 64 x 64 x 32 tiles, direct loads: the launch-floor reference
+
+
+_SLEEP = [0]
+
+
+def _sleep_cycles(torch, ms=2.0):
+    """GPU sleep cycles for about `ms` milliseconds (measured once)."""
+    if not _SLEEP[0]:
+        s = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(10 ** 5)
+        torch.cuda.synchronize()
+        e0.record(s)
+        torch.cuda._sleep(10 ** 6)
+        e1.record(s)
+        torch.cuda.synchronize()
+        _SLEEP[0] = int(10 ** 6 * ms / max(e0.elapsed_time(e1), 1e-3))
+    return _SLEEP[0]
 
 
 def _time(torch, fn, warm_ms, reps=15):
+    """Median GPU time of one launch of fn (ns).  The timed launches are
+    queued behind a GPU sleep, so the host's per-call cost does not pace
+    them."""
     torch.cuda.synchronize()
     t0 = time.time()
     while (time.time() - t0) * 1000 < warm_ms:
@@ -47,6 +78,7 @@ def _time(torch, fn, warm_ms, reps=15):
         torch.cuda.synchronize()
     s = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    torch.cuda._sleep(_sleep_cycles(torch))
     ev[0].record(s)
     for i in range(reps):
         fn()
@@ -64,36 +96,98 @@ def _operands(torch, M, N, K, ld_pad):
     return A, B, C
 
 
-def eff_from_time(t_ns, bm, bn, bk, M, N, K):
+def _forced(torch, sg, vid, M, N, K, warm_ms):
+    """GPU time (ns) of an M x N x K product with variant vid, no split or strips."""
+    A, B, C = _operands(torch, M, N, K, 0)
+    cfg = sg.SgemmCfg()
+    cfg.id, cfg.group_m, cfg.xcd_remap, cfg.splits = vid, 8, 1, 1
+    t = _time(torch, lambda: sg.sgemm(A, B, out=C, cfg=cfg, workspace=False), warm_ms)
+    del A, B, C
+    return t
+
+
+def slice_ns(bm, bn, bk, eff):
+    return 2.0 * bm * bn * bk / (CU_FLOP_PER_NS * eff / 1000.0)
+
+
+def eff_from_time(t_ns, bm, bn, bk, M, N, K, fixed_ns=TILE_FIXED_NS):
+    """t_ns: the launch's time less the launch floor."""
     tiles = -(-M // bm) * -(-N // bn)
     rounds = -(-tiles // CUS)
     slices = -(-K // bk)
-    per_round = t_ns / rounds - TILE_FIXED_NS
+    per_round = t_ns / rounds - fixed_ns
     return 1000.0 * slices * 2.0 * bm * bn * bk / (CU_FLOP_PER_NS * per_round)
 
 
-def calibrate_variant(torch, sg, vid, warm_ms):
+def launch_floor(torch, sg, warm_ms, ref=REF_VARIANT):
+    """Time every launch takes beyond the cost model (dispatch, completion,
+    the events): a one-tile product under the small-tile reference variant,
+    one slice deep, less the model's fixed cost and that slice (the time one
+    more slice adds, measured over 32 more)."""
+    v = sg.sgemm_f32_variant(ref)
+    t1 = _forced(torch, sg, ref, 8, 8, v.bk, warm_ms)
+    t33 = _forced(torch, sg, ref, 8, 8, 33 * v.bk, warm_ms)
+    floor = t1 - TILE_FIXED_NS - (t33 - t1) / 32.0
+    print(json.dumps({"floor": "launch", "variant": ref, "us": [round(t1 / 1e3, 2), round(t33 / 1e3, 2)],
+                      "floor_ns": round(floor)}), flush=True)
+    return max(floor, 0.0)
+
+
+def _record(vid, v, name, M, N, K, t, e):
+    print(json.dumps({"variant": vid, "tile": f"{v.bm}x{v.bn}x{v.bk}", "shape": name,
+                      "M": M, "N": N, "K": K, "us": round(t / 1e3, 2),
+                      "tflops": round(2.0 * M * N * K / t / 1e3, 2), "eff": round(e)}),
+          flush=True)
+
+
+def calibrate_variant(torch, sg, vid, warm_ms, floor):
     v = sg.sgemm_f32_variant(vid)
     bm, bn, bk = v.bm, v.bn, v.bk
     shapes = {
-        "full": (32 * bm, 32 * bn, 4096, 0),
-        "one": (16 * bm, 16 * bn, 4096, 0),
+        "full": (32 * bm, 32 * bn, 4096),
+        "one": (16 * bm, 16 * bn, 4096),
         # odd leading dimensions: rows not 16-byte aligned
-        "unaligned": (32 * bm - 5, 32 * bn - 5, 4099, 0),
+        "unaligned": (32 * bm - 5, 32 * bn - 5, 4099),
     }
     out = {}
-    for name, (M, N, K, pad) in shapes.items():
-        A, B, C = _operands(torch, M, N, K, pad)
-        cfg = sg.SgemmCfg()
-        cfg.id, cfg.group_m, cfg.xcd_remap, cfg.splits = vid, 8, 1, 1
-        t = _time(torch, lambda: sg.sgemm(A, B, out=C, cfg=cfg, workspace=False), warm_ms)
-        e = eff_from_time(t, bm, bn, bk, M, N, K)
+    for name, (M, N, K) in shapes.items():
+        t = _forced(torch, sg, vid, M, N, K, warm_ms)
+        e = eff_from_time(t - floor, bm, bn, bk, M, N, K)
         out[name] = round(e)
-        print(json.dumps({"variant": vid, "tile": f"{bm}x{bn}x{bk}", "shape": name,
-                          "M": M, "N": N, "K": K, "us": round(t / 1e3, 2),
-                          "tflops": round(2.0 * M * N * K / t / 1e3, 2), "eff": round(e)}),
-              flush=True)
-        del A, B, C
+        _record(vid, v, name, M, N, K, t, e)
+    return out
+
+
+def calibrate_ksplit(torch, sg, vid, warm_ms, floor):
+    """A variant that splits K over its waves (spill modelled): its fixed
+    cost and one-round rate from its one-round shape (16 BM x 16 BN) one
+    slice deep and at K = 2048, where the operands one XCD reads stay in its
+    L2; its
+    rate over four rounds (32 BM x 32 BN, K = 1024) and on unaligned rows
+    (32 BM - 5 x 32 BN - 5, K = 1027) with that fixed cost; and its spill
+    factor from the one-round shape at K = 4096, where they do not."""
+    v = sg.sgemm_f32_variant(vid)
+    bm, bn, bk = v.bm, v.bn, v.bk
+    M1, N1 = 16 * bm, 16 * bn
+    t1 = _forced(torch, sg, vid, M1, N1, bk, warm_ms)
+    t2k = _forced(torch, sg, vid, M1, N1, 2048, warm_ms)
+    fixed = max(t1 - (t2k - t1) / (2048.0 - bk) * bk - floor, 0.0)
+    out = {"fixed": round(fixed)}
+    e_one = eff_from_time(t2k - floor, bm, bn, bk, M1, N1, 2048, fixed)
+    out["one"] = round(e_one)
+    _record(vid, v, "one", M1, N1, 2048, t2k, e_one)
+    for name, (M, N, K) in {"full": (32 * bm, 32 * bn, 1024),
+                            "unaligned": (32 * bm - 5, 32 * bn - 5, 1027)}.items():
+        t = _forced(torch, sg, vid, M, N, K, warm_ms)
+        e = eff_from_time(t - floor, bm, bn, bk, M, N, K, fixed)
+        out[name] = round(e)
+        _record(vid, v, name, M, N, K, t, e)
+    t4k = _forced(torch, sg, vid, M1, N1, 4096, warm_ms)
+    slices = -(-4096 // bk)
+    out["spill"] = round(1000.0 * (t4k - floor - fixed) / (slices * slice_ns(bm, bn, bk, e_one)))
+    print(json.dumps({"variant": vid, "shape": "spill", "M": M1, "N": N1, "K": 4096,
+                      "us": round(t4k / 1e3, 2), "fixed_ns": out["fixed"],
+                      "spill_permille": out["spill"]}), flush=True)
     return out
 
 
@@ -142,11 +236,16 @@ def main(argv=None):
         vids = [int(x) for x in args.variants.split(",")]
     else:
         vids = [i for i in range(sg.sgemm_f32_num_variants()) if _is_mfma(sg, i)]
+    floor = launch_floor(torch, sg, args.ms)
     table = {}
     for vid in vids:
-        table[vid] = calibrate_variant(torch, sg, vid, args.ms)
+        if sg.sgemm_f32_variant(vid).spill_permille > 0:
+            table[vid] = calibrate_ksplit(torch, sg, vid, args.ms, floor)
+        else:
+            table[vid] = calibrate_variant(torch, sg, vid, args.ms, floor)
     for vid, e in table.items():
-        print(f"variant {vid}: ({e['full']}, {e['one']}, {e['unaligned']})", flush=True)
+        extra = f", {e['fixed']}, {e['spill']}" if "spill" in e else ""
+        print(f"variant {vid}: ({e['full']}, {e['one']}, {e['unaligned']}{extra})", flush=True)
     if not args.no_strips:
         fixed, rate = calibrate_strips(torch, sg, args.ms)
         print(f"strips: kStripFixedNs = {fixed:.0f}, kStripBytesPerNs = {rate:.0f}", flush=True)

@@ -39,6 +39,10 @@ struct Variant {
                                  // 16-byte aligned (4-byte direct loads for the variants
                                  // that have them, every slice fetched through registers
                                  // for the other direct-load ones)
+    int fixed_ns;                // fixed cost of a tile in the cost model (0: kTileFixedNs)
+    int spill_permille;          // slice cost (x1000 of the resident one) once the operand
+                                 // rows and columns the tiles of one XCD read exceed its
+                                 // L2 (0: not modelled)
 };
 
 // One call as the planner sees it.
@@ -126,6 +130,10 @@ inline long long split_workspace_bytes(const Problem &p, int splits)
     return (long long)p.batch * splits * p.M * partial_ld(p.N) * 4;
 }
 
+// Fixed cost of one tile (prologue fetch, pipeline fill, epilogue stores) for
+// the variants that do not carry their own.
+constexpr double kTileFixedNs = 2500.0;
+
 inline void describe(const Variant &v, int id, sgemm_cfg *out)
 {
     out->id = id;
@@ -147,6 +155,8 @@ inline void describe(const Variant &v, int id, sgemm_cfg *out)
     out->workspace_bytes = 0;
     out->strip_m = 0;
     out->strip_n = 0;
+    out->fixed_ns = v.fixed_ns > 0 ? v.fixed_ns : (int)kTileFixedNs;
+    out->spill_permille = v.spill_permille;
 }
 
 // Default tile order: groups of 8 tile rows and the XCD remap.
@@ -192,14 +202,30 @@ inline bool finish_cfg(const Variant &v, int id, const Problem &full, int want, 
 // ---- cost model (nanoseconds) ---------------------------------------------------
 // One compute unit at the FP32 matrix peak: 157.3 TFLOP/s over 256 CUs.
 constexpr double kCuFlopPerNs = 157.3e3 / 256.0;
-// Fixed cost of one tile (prologue fetch, pipeline fill, epilogue stores).
-constexpr double kTileFixedNs = 2500.0;
 // The reduction pass: the second launch and the wait for the first one to
 // drain (a split product measured 7-10 us above its main kernel's model at
 // 512^3 and 128 x 128 x 32768), and the rate at which it streams the
 // partials and writes C (about 5 TB/s).
 constexpr double kReduceFixedNs = 7500.0;
 constexpr double kReduceBytesPerNs = 5000.0;
+
+// L2 per XCD, and the XCDs of the chip.
+constexpr double kL2Bytes = 4.0 * 1024 * 1024;
+constexpr int kXcds = 8;
+
+// Bytes of op(A) rows and op(B) columns, over kc values of k, that the tiles
+// one XCD holds at once read: the tile order hands each XCD a run of
+// consecutive tiles, which with groups of kDefaultGroupM tile rows is a block
+// of up to that many tile rows by as many tile columns as the run needs.
+inline double xcd_operand_bytes(const Variant &v, long long tiles, int tiles_m, int kc, int cus)
+{
+    const long long per_xcd = ceil_div_ll(tiles < cus ? tiles : cus, kXcds);
+    long long r = tiles_m < kDefaultGroupM ? tiles_m : kDefaultGroupM;
+    if (r > per_xcd) r = per_xcd;
+    if (r < 1) r = 1;
+    const long long c = ceil_div_ll(per_xcd, r);
+    return 4.0 * kc * (double)(r * v.bm + c * v.bn);
+}
 
 // eff: the variant's fraction of peak (x1000) for this call's alignment.
 inline double estimate_ns(const Variant &v, const Problem &p, int splits, int k_chunk, int cus,
@@ -212,8 +238,12 @@ inline double estimate_ns(const Variant &v, const Problem &p, int splits, int k_
     if (v.stages == 0 && v.stage_at >= 0) slices += slices & 1;  // register pipeline takes pairs
     double e = eff;
     if (tiles <= cus) e = e * v.eff_one_permille / v.eff_permille;
-    const double slice_ns = 2.0 * v.bm * v.bn * v.bk / (kCuFlopPerNs * e / 1000.0);
-    double t = (double)rounds * (kTileFixedNs + (double)slices * slice_ns);
+    double slice_ns = 2.0 * v.bm * v.bn * v.bk / (kCuFlopPerNs * e / 1000.0);
+    if (v.spill_permille > 0 &&
+        xcd_operand_bytes(v, tiles, (int)ceil_div_ll(p.M, v.bm), kc, cus) > kL2Bytes)
+        slice_ns = slice_ns * v.spill_permille / 1000.0;
+    const double fixed = v.fixed_ns > 0 ? (double)v.fixed_ns : kTileFixedNs;
+    double t = (double)rounds * (fixed + (double)slices * slice_ns);
     if (splits > 1)
         t += kReduceFixedNs +
              4.0 * (double)p.batch * p.M * (double)partial_ld(p.N) * (splits + 1) / kReduceBytesPerNs;

@@ -38,7 +38,7 @@ Variant mfma_variant(int eff_permille, int eff_one_permille, int eff_unaligned_p
                    {reinterpret_cast<const void *>(
                         &sgemm::sgemm_mfma_kernel<BM, BN, BK, WM, WN, STAGE_AT>),
                     nullptr, nullptr, nullptr},
-                   eff_permille, eff_one_permille, eff_unaligned_permille};
+                   eff_permille, eff_one_permille, eff_unaligned_permille, 0, 0};
 }
 
 // OPS: bit (transa + 2*transb) set for each operand layout to compile.  DW:
@@ -51,7 +51,7 @@ Variant dl_variant(int eff_permille, int eff_one_permille, int eff_unaligned_per
     Variant v{SGEMM_KERNEL_MFMA, BM, BN, BK, WM, WN, -1, STAGES, DW ? 1 : 0,
               T::NT, (int)(T::LDS_FLOATS * sizeof(float)),
               {nullptr, nullptr, nullptr, nullptr}, eff_permille, eff_one_permille,
-              eff_unaligned_permille};
+              eff_unaligned_permille, 0, 0};
     v.fn[0] = reinterpret_cast<const void *>(
         &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, false, false, DW, PIPE>);
     if constexpr ((OPS & 2) != 0)
@@ -69,7 +69,8 @@ Variant dl_variant(int eff_permille, int eff_one_permille, int eff_unaligned_per
 // 32x32 tiles with K split across the W waves of the workgroup (every layout).
 // waves_m = W describes the waves (they share the tile and split K).
 template <int W>
-Variant sk_variant(int eff_permille, int eff_one_permille, int eff_unaligned_permille)
+Variant sk_variant(int eff_permille, int eff_one_permille, int eff_unaligned_permille, int fixed_ns,
+                   int spill_permille)
 {
     typedef sgemm::SkTraits<W> T;
     return Variant{SGEMM_KERNEL_MFMA, T::BM, T::BN, 8, W, 1, -1, 0, 0,
@@ -78,7 +79,8 @@ Variant sk_variant(int eff_permille, int eff_one_permille, int eff_unaligned_per
                     reinterpret_cast<const void *>(&sgemm::sgemm_mfma_sk_kernel<W, true, false>),
                     reinterpret_cast<const void *>(&sgemm::sgemm_mfma_sk_kernel<W, false, true>),
                     reinterpret_cast<const void *>(&sgemm::sgemm_mfma_sk_kernel<W, true, true>)},
-                   eff_permille, eff_one_permille, eff_unaligned_permille};
+                   eff_permille, eff_one_permille, eff_unaligned_permille, fixed_ns,
+                   spill_permille};
 }
 
 Variant valu_variant()
@@ -88,7 +90,7 @@ Variant valu_variant()
                    T::NT, (int)(T::LDS_FLOATS * sizeof(float)),
                    {reinterpret_cast<const void *>(&sgemm::sgemm_valu_kernel),
                     nullptr, nullptr, nullptr},
-                   0, 0, 0};
+                   0, 0, 0, 0, 0};
 }
 
 constexpr int kAllOps = 0xf;
@@ -103,13 +105,18 @@ constexpr int kCrossSliceAgpr = 6;
 // (32 BM x 32 BN), over one round, one workgroup per CU (16 BM x 16 BN), and
 // with rows that are not 16-byte aligned (32 BM - 5 x 32 BN - 5, K = 4099).
 // `python -m fp32_gemm_sgemm_amd.calibrate` measures them; the figures below
-// come from one such run on MI355X.
+// come from one such run on MI355X, with the launch floor every launch pays
+// taken off each time.  The K-split 32x32 tiles carry two more numbers:
+// their fixed cost per tile in ns, and the factor (x1000) by which a slice
+// slows once the operand rows and columns one XCD's tiles read exceed its L2;
+// their rates are measured where those fit (the others use the model's common
+// 2.5 us, and no spill term).
 // The 4-byte direct-load variants serve only rows that are not 16-byte
 // aligned.  0 keeps a variant out of automatic selection (comparison
 // kernels, dominated tiles).
 const Variant kVariants[] = {
-    mfma_variant<256, 256, 16, 4, 2, 0>(896, 888, 699),    // 0: 8 waves of 64x128
-    mfma_variant<128, 128, 16, 2, 2, 0>(857, 760, 591),    // 1: 4 waves of 64x64
+    mfma_variant<256, 256, 16, 4, 2, 0>(888, 887, 690),    // 0: 8 waves of 64x128
+    mfma_variant<128, 128, 16, 2, 2, 0>(848, 754, 587),    // 1: 4 waves of 64x64
     mfma_variant<128, 128, 32, 2, 2, 1>(0, 0, 0),          // 2: 4 waves of 64x64, BK 32
     mfma_variant<128, 256, 16, 2, 2, 0>(0, 0, 0),          // 3: 4 waves of 64x128
     mfma_variant<256, 128, 16, 4, 1, 0>(0, 0, 0),          // 4: 4 waves of 64x128
@@ -117,22 +124,22 @@ const Variant kVariants[] = {
     mfma_variant<128, 128, 16, 2, 2, -1>(0, 0, 0),         // 6: plain order (comparison)
     valu_variant(),                                        // 7: vector-FMA comparison
     mfma_variant<192, 192, 16, 2, 6, 0>(0, 0, 0),          // 8: 12 waves of 96x32
-    mfma_variant<192, 192, 32, 2, 6, 1>(888, 880, 714),    // 9: 12 waves of 96x32, BK 32
+    mfma_variant<192, 192, 32, 2, 6, 1>(886, 871, 710),    // 9: 12 waves of 96x32, BK 32
     dl_variant<256, 256, 16, 4, 2, 4, 1>(0, 0, 0),         // 10: direct loads, 4 stages
-    dl_variant<256, 256, 32, 4, 2, 2, kAllOps, false, kCrossSliceAgpr>(963, 955, 661),  // 11: direct loads, 2 stages of BK 32
-    dl_variant<128, 128, 32, 2, 2, 3, kAllOps>(776, 764, 403),  // 12: direct loads
-    dl_variant<192, 192, 32, 2, 6, 2, kAllOps, false, kCrossSliceAgpr>(953, 944, 610),  // 13: direct loads
+    dl_variant<256, 256, 32, 4, 2, 2, kAllOps, false, kCrossSliceAgpr>(959, 954, 660),  // 11: direct loads, 2 stages of BK 32
+    dl_variant<128, 128, 32, 2, 2, 3, kAllOps>(778, 761, 405),  // 12: direct loads
+    dl_variant<192, 192, 32, 2, 6, 2, kAllOps, false, kCrossSliceAgpr>(951, 936, 609),  // 13: direct loads
     dl_variant<256, 256, 16, 4, 2, 3, 1>(0, 0, 0),         // 14: direct loads, 3 stages
-    dl_variant<128, 128, 32, 4, 2, 2, kAllOps, false, kCrossSliceAgpr>(952, 923, 663),  // 15: direct loads, 8 waves of 32x64
-    mfma_variant<128, 128, 16, 2, 4, 0>(830, 826, 676),    // 16: 8 waves of 64x32
-    mfma_variant<128, 128, 32, 2, 4, 1>(821, 796, 744),    // 17: 8 waves of 64x32, BK 32
-    dl_variant<192, 192, 32, 2, 6, 2, kAllOps, true, kCrossSliceAgpr>(946, 939, 944),  // 18: 4-byte direct loads
-    mfma_variant<64, 64, 32, 2, 2, 1>(775, 591, 591),      // 19: 4 waves of 32x32
-    dl_variant<64, 64, 32, 2, 2, 2, kAllOps, false, kCrossSliceAgpr>(935, 636, 505),  // 20: direct loads, 4 waves of 32x32
-    dl_variant<64, 64, 32, 2, 2, 2, kAllOps, true, kCrossSliceAgpr>(917, 625, 875),  // 21: 4-byte direct loads
-    dl_variant<128, 128, 32, 4, 2, 2, kAllOps, true, kCrossSliceAgpr>(947, 918, 945),  // 22: 4-byte direct loads, 8 waves of 32x64
-    sk_variant<4>(546, 318, 468),                           // 23: 32x32, K split over 4 waves
-    sk_variant<16>(467, 417, 395),                          // 24: 32x32, K split over 16 waves
+    dl_variant<128, 128, 32, 4, 2, 2, kAllOps, false, kCrossSliceAgpr>(925, 928, 661),  // 15: direct loads, 8 waves of 32x64
+    mfma_variant<128, 128, 16, 2, 4, 0>(827, 825, 671),    // 16: 8 waves of 64x32
+    mfma_variant<128, 128, 32, 2, 4, 1>(817, 790, 743),    // 17: 8 waves of 64x32, BK 32
+    dl_variant<192, 192, 32, 2, 6, 2, kAllOps, true, kCrossSliceAgpr>(944, 936, 941),  // 18: 4-byte direct loads
+    mfma_variant<64, 64, 32, 2, 2, 1>(760, 612, 586),      // 19: 4 waves of 32x32
+    dl_variant<64, 64, 32, 2, 2, 2, kAllOps, false, kCrossSliceAgpr>(884, 659, 500),  // 20: direct loads, 4 waves of 32x32
+    dl_variant<64, 64, 32, 2, 2, 2, kAllOps, true, kCrossSliceAgpr>(877, 646, 906),  // 21: 4-byte direct loads
+    dl_variant<128, 128, 32, 4, 2, 2, kAllOps, true, kCrossSliceAgpr>(926, 903, 922),  // 22: 4-byte direct loads, 8 waves of 32x64
+    sk_variant<4>(997, 569, 733, 3757, 1604),              // 23: 32x32, K split over 4 waves
+    sk_variant<16>(693, 536, 398, 4554, 1094),             // 24: 32x32, K split over 16 waves
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 

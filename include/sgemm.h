@@ -63,6 +63,11 @@ typedef struct sgemm_cfg {
        describes the (M - strip_m) x (N - strip_n) block that remains.  At
        most 4 each.  Chosen by plan/query; an input of sgemm_f32_ex. */
     int strip_m, strip_n;
+    /* The cost model's figures for this variant (reported, never read): */
+    int fixed_ns;       /* fixed cost of one tile (ns) */
+    int spill_permille; /* slice cost, x1000 of the L2-resident one, once the
+                           operand rows and columns one XCD's tiles read exceed
+                           its L2 (0 = not modelled) */
 } sgemm_cfg;
 
 /*

@@ -66,6 +66,16 @@ def test_version_and_variants(lib):
         assert 0 < v.lds_bytes <= 160 * 1024
         assert v.bm % 32 == 0 and v.bn % 32 == 0 and v.bk % 8 == 0
     assert kinds == {sg.binding.SGEMM_KERNEL_MFMA, sg.binding.SGEMM_KERNEL_VALU}
+    # cost-model figures: every variant reports a fixed cost; only the tiles
+    # that split K over their waves (32 x 32 x 8) price an L2 spill, as a
+    # slowdown (>= 1000 permille)
+    for i in range(n):
+        v = sg.sgemm_f32_variant(i)
+        assert 0 < v.fixed_ns < 20000
+        if (v.bm, v.bn, v.bk) == (32, 32, 8):
+            assert v.spill_permille >= 1000
+        else:
+            assert v.spill_permille == 0 and v.fixed_ns == 2500
     with pytest.raises(sg.SgemmError):
         sg.sgemm_f32_variant(n)
     with pytest.raises(sg.SgemmError):
@@ -335,6 +345,21 @@ def test_selector_splits_k_for_few_tiles(lib):
     p = sg.sgemm_f32_plan(128, 128, 4096, 4096, 128, 128, 256, batch=512,
                           workspace_bytes=1 << 40)
     assert p.splits == 1 and p.grid == 512
+
+
+def test_selector_k_split_tiles_follow_the_l2(lib):
+    """Without a workspace, an output of 256 32 x 32 tiles goes to the tiles
+    that split K over their waves; the wider 16-wave form is picked only once
+    the operand rows and columns one XCD reads (8 tile rows and 4 tile
+    columns, 384 rows of 4 K bytes) exceed its 4 MiB L2, i.e. from K of
+    about 2730."""
+    widths = {}
+    for K in (512, 2048, 8192, 16384):
+        p = sg.sgemm_f32_plan(512, 512, K, K, 512, 512, 256)
+        assert (p.bm, p.bn, p.bk) == (32, 32, 8) and p.splits == 1
+        widths[K] = p.waves_m
+    assert widths[512] == widths[2048] == 4
+    assert widths[8192] == widths[16384] == 16
 
 
 def test_cfg_geometry_of_forced_splits(lib):
