@@ -22,8 +22,8 @@ and the cost model of select.hpp,
 is inverted for eff (x1000), the three numbers each variant carries in the
 table of sgemm.hip.  The variants that split K over their waves (32 x 32
 tiles, whose L2 spill the model prices) also get their own fixed cost and
-spill factor, and are measured at K where the operands one XCD reads fit in
-its L2 (calibrate_ksplit).  The strip kernel is timed alone on two sizes of a
+spill factors (one round, several rounds), and are measured at K where the
+operands one XCD reads fit in its L2 (calibrate_ksplit).  The strip kernel is timed alone on two sizes of a
 4-row product in both storage orders of its streamed operand, and its fixed
 cost and streaming rate are fitted (kStripFixedNs, kStripBytesPerNs).
 
@@ -162,10 +162,10 @@ def calibrate_ksplit(torch, sg, vid, warm_ms, floor):
     """A variant that splits K over its waves (spill modelled): its fixed
     cost and one-round rate from its one-round shape (16 BM x 16 BN) one
     slice deep and at K = 2048, where the operands one XCD reads stay in its
-    L2; its
-    rate over four rounds (32 BM x 32 BN, K = 1024) and on unaligned rows
-    (32 BM - 5 x 32 BN - 5, K = 1027) with that fixed cost; and its spill
-    factor from the one-round shape at K = 4096, where they do not."""
+    L2; its rate over four rounds (32 BM x 32 BN, K = 1024) and on unaligned
+    rows (32 BM - 5 x 32 BN - 5, K = 1027) with that fixed cost; and its
+    spill factors from the one-round and four-round shapes at K = 4096, where
+    those operands do not fit."""
     v = sg.sgemm_f32_variant(vid)
     bm, bn, bk = v.bm, v.bn, v.bk
     M1, N1 = 16 * bm, 16 * bn
@@ -182,12 +182,18 @@ def calibrate_ksplit(torch, sg, vid, warm_ms, floor):
         e = eff_from_time(t - floor, bm, bn, bk, M, N, K, fixed)
         out[name] = round(e)
         _record(vid, v, name, M, N, K, t, e)
-    t4k = _forced(torch, sg, vid, M1, N1, 4096, warm_ms)
     slices = -(-4096 // bk)
+    t4k = _forced(torch, sg, vid, M1, N1, 4096, warm_ms)
     out["spill"] = round(1000.0 * (t4k - floor - fixed) / (slices * slice_ns(bm, bn, bk, e_one)))
-    print(json.dumps({"variant": vid, "shape": "spill", "M": M1, "N": N1, "K": 4096,
-                      "us": round(t4k / 1e3, 2), "fixed_ns": out["fixed"],
-                      "spill_permille": out["spill"]}), flush=True)
+    M4, N4 = 32 * bm, 32 * bn
+    rounds = -(-(M4 // bm) * (N4 // bn) // CUS)
+    t4k_full = _forced(torch, sg, vid, M4, N4, 4096, warm_ms)
+    out["spill_full"] = round(1000.0 * ((t4k_full - floor) / rounds - fixed) /
+                              (slices * slice_ns(bm, bn, bk, out["full"])))
+    print(json.dumps({"variant": vid, "shape": "spill", "M": [M1, M4], "N": [N1, N4], "K": 4096,
+                      "us": [round(t4k / 1e3, 2), round(t4k_full / 1e3, 2)],
+                      "fixed_ns": out["fixed"], "spill_permille": out["spill"],
+                      "spill_full_permille": out["spill_full"]}), flush=True)
     return out
 
 
@@ -244,7 +250,7 @@ def main(argv=None):
         else:
             table[vid] = calibrate_variant(torch, sg, vid, args.ms, floor)
     for vid, e in table.items():
-        extra = f", {e['fixed']}, {e['spill']}" if "spill" in e else ""
+        extra = f", {e['fixed']}, {e['spill']}, {e['spill_full']}" if "spill" in e else ""
         print(f"variant {vid}: ({e['full']}, {e['one']}, {e['unaligned']}{extra})", flush=True)
     if not args.no_strips:
         fixed, rate = calibrate_strips(torch, sg, args.ms)

@@ -42,7 +42,8 @@ struct Variant {
     int fixed_ns;                // fixed cost of a tile in the cost model (0: kTileFixedNs)
     int spill_permille;          // slice cost (x1000 of the resident one) once the operand
                                  // rows and columns the tiles of one XCD read exceed its
-                                 // L2 (0: not modelled)
+                                 // L2, over one round (0: not modelled)
+    int spill_full_permille;     // the same over several rounds, where every CU streams
 };
 
 // One call as the planner sees it.
@@ -157,6 +158,7 @@ inline void describe(const Variant &v, int id, sgemm_cfg *out)
     out->strip_n = 0;
     out->fixed_ns = v.fixed_ns > 0 ? v.fixed_ns : (int)kTileFixedNs;
     out->spill_permille = v.spill_permille;
+    out->spill_full_permille = v.spill_full_permille;
 }
 
 // Default tile order: groups of 8 tile rows and the XCD remap.
@@ -241,7 +243,7 @@ inline double estimate_ns(const Variant &v, const Problem &p, int splits, int k_
     double slice_ns = 2.0 * v.bm * v.bn * v.bk / (kCuFlopPerNs * e / 1000.0);
     if (v.spill_permille > 0 &&
         xcd_operand_bytes(v, tiles, (int)ceil_div_ll(p.M, v.bm), kc, cus) > kL2Bytes)
-        slice_ns = slice_ns * v.spill_permille / 1000.0;
+        slice_ns = slice_ns * (tiles <= cus ? v.spill_permille : v.spill_full_permille) / 1000.0;
     const double fixed = v.fixed_ns > 0 ? (double)v.fixed_ns : kTileFixedNs;
     double t = (double)rounds * (fixed + (double)slices * slice_ns);
     if (splits > 1)

@@ -67,7 +67,8 @@ typedef struct sgemm_cfg {
     int fixed_ns;       /* fixed cost of one tile (ns) */
     int spill_permille; /* slice cost, x1000 of the L2-resident one, once the
                            operand rows and columns one XCD's tiles read exceed
-                           its L2 (0 = not modelled) */
+                           its L2, over one round (0 = not modelled) */
+    int spill_full_permille; /* the same over several rounds */
 } sgemm_cfg;
 
 /*

@@ -176,7 +176,7 @@ def test_strip_only_batches_past_one_launch():
     assert np.all(np.abs(C - ref) <= oracle.TOL * absb)
 
 
-@pytest.mark.parametrize("vid", [23, 24])
+@pytest.mark.parametrize("vid", [23, 24, 25])
 def test_ksplit_tiles_with_outer_splits_batches_and_strips(vid):
     """The 32x32 tiles that split K over their waves, combined with a split
     across workgroups (workspace), batches with a broadcast operand, strips
