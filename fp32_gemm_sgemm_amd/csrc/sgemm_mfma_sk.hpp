@@ -56,11 +56,14 @@ __global__ void __launch_bounds__(W * 64) sgemm_mfma_sk_kernel(GemmArgs g)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l31 = lane & 31, h = lane >> 5;
 
-    // this wave's K range [kb, ke), in 8-deep groups
+    // this wave's K range [kb, ke): nfull whole 8-deep groups, then rem < 8
+    // more k (only in the last wave, when K is not a multiple of 8)
     const int kc = (((K + W - 1) / W) + 7) & ~7;
     const int kb = wave * kc;
     const int ke = min(K, kb + kc);
-    const int ng = ke > kb ? (ke - kb + 7) / 8 : 0;
+    const int len = ke > kb ? ke - kb : 0;
+    const int nfull = len >> 3;
+    const int rem = len & 7;
 
     const int ia = min(m0 + l31, M - 1);  // row of op(A) this lane feeds
     const int jb = min(n0 + l31, N - 1);  // column of op(B) this lane feeds
@@ -73,44 +76,64 @@ __global__ void __launch_bounds__(W * 64) sgemm_mfma_sk_kernel(GemmArgs g)
     struct Frag {
         f32x4 a, b;
     };
-    // group q of this wave: k = kb + 8q + 4h + t, t = 0..3
+    // whole group q of this wave: k = kb + 8q + 4h + t, t = 0..3.  The loop
+    // below has no branch and no lane-dependent condition, so the compiler
+    // waits for each group's loads alone, with the later groups still in
+    // flight.
     auto load = [&](int q, Frag &f) {
         const int k = kb + 8 * q + 4 * h;
-        if (q < ng && kb + 8 * q + 8 <= ke) {
-            if constexpr (!TA) f.a = *reinterpret_cast<const f32x4u *>(pa + k);
-            else {
+        if constexpr (!TA) f.a = *reinterpret_cast<const f32x4u *>(pa + k);
+        else {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) f.a[t] = pa[(int64_t)(k + t) * sa];
-            }
-            if constexpr (TB) f.b = *reinterpret_cast<const f32x4u *>(pb + k);
-            else {
+            for (int t = 0; t < 4; ++t) f.a[t] = pa[(int64_t)(k + t) * sa];
+        }
+        if constexpr (TB) f.b = *reinterpret_cast<const f32x4u *>(pb + k);
+        else {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) f.b[t] = pb[(int64_t)(k + t) * sb];
-            }
-        } else {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const bool in = q < ng && k + t < ke;
-                f.a[t] = in ? pa[(int64_t)(k + t) * sa] : 0.0f;
-                f.b[t] = in ? pb[(int64_t)(k + t) * sb] : 0.0f;
-            }
+            for (int t = 0; t < 4; ++t) f.b[t] = pb[(int64_t)(k + t) * sb];
         }
     };
-
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-    Frag f[D];
+    auto mma = [&](const Frag &f) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) load(d, f[d]);
-    for (int q0 = 0; q0 < ng; q0 += D) {
+        for (int t = 0; t < 4; ++t)
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[t], f.b[t], acc, 0, 0, 0);
+    };
+
+    if (nfull > 0) {
+        // prefetch indices past the last whole group reload it (in bounds,
+        // never multiplied in)
+        const int last = nfull - 1;
+        Frag f[D];
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
+        for (int d = 0; d < D; ++d) load(min(d, last), f[d]);
+        int q0 = 0;
+        for (; q0 + D <= nfull; q0 += D) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(f[d].a[t], f[d].b[t], acc, 0, 0, 0);
-            load(q0 + D + d, f[d]);
+            for (int d = 0; d < D; ++d) {
+                mma(f[d]);
+                load(min(q0 + D + d, last), f[d]);
+            }
         }
+        // fewer than D whole groups left, already in f[0..]
+#pragma unroll
+        for (int d = 0; d < D - 1; ++d)
+            if (q0 + d < nfull) mma(f[d]);
+    }
+    if (rem > 0) {
+        // the ragged group: k past ke reads a clamped address and becomes 0
+        const int k = kb + 8 * nfull + 4 * h;
+        Frag f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int kk = min(k + t, ke - 1);
+            const float x = pa[(int64_t)kk * sa], y = pb[(int64_t)kk * sb];
+            f.a[t] = k + t < ke ? x : 0.0f;
+            f.b[t] = k + t < ke ? y : 0.0f;
+        }
+        mma(f);
     }
 
     // partial tiles -> LDS as [wave][register][lane]; then each thread adds
