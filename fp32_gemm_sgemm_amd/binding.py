@@ -34,7 +34,7 @@ class SgemmCfg(ctypes.Structure):
         "group_m", "xcd_remap", "splits", "k_chunk", "grid", "threads",
         "lds_bytes", "tiles_m", "tiles_n")] + [("workspace_bytes", ctypes.c_longlong)] + [
         (n, ctypes.c_int) for n in ("strip_m", "strip_n", "fixed_ns", "spill_permille",
-                                 "spill_full_permille")]
+                                 "spill_full_permille", "coresident")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

@@ -23,7 +23,9 @@ is inverted for eff (x1000), the three numbers each variant carries in the
 table of sgemm.hip.  The variants that split K over their waves (32 x 32
 tiles, whose L2 spill the model prices) also get their own fixed cost and
 spill factors (one round, several rounds), and are measured at K where the
-operands one XCD reads fit in its L2 (calibrate_ksplit).  The strip kernel is timed alone on two sizes of a
+operands one XCD reads fit in its L2 (calibrate_ksplit); several of their
+workgroups share a CU, and the model charges their fixed cost once per wave
+of co-resident workgroups.  The strip kernel is timed alone on two sizes of a
 4-row product in both storage orders of its streamed operand, and its fixed
 cost and streaming rate are fitted (kStripFixedNs, kStripBytesPerNs).
 
@@ -110,12 +112,14 @@ def slice_ns(bm, bn, bk, eff):
     return 2.0 * bm * bn * bk / (CU_FLOP_PER_NS * eff / 1000.0)
 
 
-def eff_from_time(t_ns, bm, bn, bk, M, N, K, fixed_ns=TILE_FIXED_NS):
-    """t_ns: the launch's time less the launch floor."""
+def eff_from_time(t_ns, bm, bn, bk, M, N, K, fixed_ns=TILE_FIXED_NS, coresident=1):
+    """t_ns: the launch's time less the launch floor.  Co-resident workgroups
+    pay the fixed cost once per wave of CUS * coresident tiles."""
     tiles = -(-M // bm) * -(-N // bn)
     rounds = -(-tiles // CUS)
+    waves = -(-tiles // (CUS * coresident)) if coresident > 1 else rounds
     slices = -(-K // bk)
-    per_round = t_ns / rounds - fixed_ns
+    per_round = (t_ns - waves * fixed_ns) / rounds
     return 1000.0 * slices * 2.0 * bm * bn * bk / (CU_FLOP_PER_NS * per_round)
 
 
@@ -159,15 +163,21 @@ def calibrate_variant(torch, sg, vid, warm_ms, floor):
 
 
 def calibrate_ksplit(torch, sg, vid, warm_ms, floor):
-    """A variant that splits K over its waves (spill modelled): its fixed
-    cost and one-round rate from its one-round shape (16 BM x 16 BN) one
-    slice deep and at K = 2048, where the operands one XCD reads stay in its
-    L2; its rate over four rounds (32 BM x 32 BN, K = 1024) and on unaligned
-    rows (32 BM - 5 x 32 BN - 5, K = 1027) with that fixed cost; and its
-    spill factors from the one-round and four-round shapes at K = 4096, where
-    those operands do not fit."""
+    """A variant that splits K over its waves (spill modelled):
+
+    - its fixed cost and one-round rate from its one-round shape (16 BM x 16
+      BN) one slice deep and at K = 2048, where the operands one XCD reads
+      stay in its L2;
+    - its rate over four rounds (32 BM x 32 BN, K = 1024) with that fixed cost;
+    - its spill factors from the one-round and four-round shapes at K = 4096,
+      where those operands do not fit;
+    - its rate on unaligned rows where these tiles serve: a few tiles with
+      long K (4 BM - 5 x 4 BN - 5, K = 16387, 16 tiles, spilled), the spill
+      factor taken out, stored scaled by full / one as the model scales it
+      back for one round."""
     v = sg.sgemm_f32_variant(vid)
     bm, bn, bk = v.bm, v.bn, v.bk
+    co = v.coresident
     M1, N1 = 16 * bm, 16 * bn
     t1 = _forced(torch, sg, vid, M1, N1, bk, warm_ms)
     t2k = _forced(torch, sg, vid, M1, N1, 2048, warm_ms)
@@ -176,24 +186,31 @@ def calibrate_ksplit(torch, sg, vid, warm_ms, floor):
     e_one = eff_from_time(t2k - floor, bm, bn, bk, M1, N1, 2048, fixed)
     out["one"] = round(e_one)
     _record(vid, v, "one", M1, N1, 2048, t2k, e_one)
-    for name, (M, N, K) in {"full": (32 * bm, 32 * bn, 1024),
-                            "unaligned": (32 * bm - 5, 32 * bn - 5, 1027)}.items():
-        t = _forced(torch, sg, vid, M, N, K, warm_ms)
-        e = eff_from_time(t - floor, bm, bn, bk, M, N, K, fixed)
-        out[name] = round(e)
-        _record(vid, v, name, M, N, K, t, e)
+    M, N, K = 32 * bm, 32 * bn, 1024
+    t = _forced(torch, sg, vid, M, N, K, warm_ms)
+    e_full = eff_from_time(t - floor, bm, bn, bk, M, N, K, fixed, co)
+    out["full"] = round(e_full)
+    _record(vid, v, "full", M, N, K, t, e_full)
     slices = -(-4096 // bk)
     t4k = _forced(torch, sg, vid, M1, N1, 4096, warm_ms)
-    out["spill"] = round(1000.0 * (t4k - floor - fixed) / (slices * slice_ns(bm, bn, bk, e_one)))
+    spill = (t4k - floor - fixed) / (slices * slice_ns(bm, bn, bk, e_one))
+    out["spill"] = round(1000.0 * spill)
     M4, N4 = 32 * bm, 32 * bn
-    rounds = -(-(M4 // bm) * (N4 // bn) // CUS)
+    tiles4 = (M4 // bm) * (N4 // bn)
+    rounds = -(-tiles4 // CUS)
+    waves = -(-tiles4 // (CUS * co)) if co > 1 else rounds
     t4k_full = _forced(torch, sg, vid, M4, N4, 4096, warm_ms)
-    out["spill_full"] = round(1000.0 * ((t4k_full - floor) / rounds - fixed) /
-                              (slices * slice_ns(bm, bn, bk, out["full"])))
+    out["spill_full"] = round(1000.0 * ((t4k_full - floor - waves * fixed) / rounds) /
+                              (slices * slice_ns(bm, bn, bk, e_full)))
     print(json.dumps({"variant": vid, "shape": "spill", "M": [M1, M4], "N": [N1, N4], "K": 4096,
                       "us": [round(t4k / 1e3, 2), round(t4k_full / 1e3, 2)],
                       "fixed_ns": out["fixed"], "spill_permille": out["spill"],
                       "spill_full_permille": out["spill_full"]}), flush=True)
+    M, N, K = 4 * bm - 5, 4 * bn - 5, 16387
+    t = _forced(torch, sg, vid, M, N, K, warm_ms)
+    e = eff_from_time(t - floor, bm, bn, bk, M, N, K, fixed, co) * spill
+    out["unaligned"] = round(e * e_full / e_one)
+    _record(vid, v, "unaligned (16 tiles, spill taken out)", M, N, K, t, e)
     return out
 
 

@@ -44,6 +44,8 @@ struct Variant {
                                  // rows and columns the tiles of one XCD read exceed its
                                  // L2, over one round (0: not modelled)
     int spill_full_permille;     // the same over several rounds, where every CU streams
+    int coresident;              // workgroups that share a CU and overlap their fixed
+                                 // costs (0: one, the fixed cost is paid every round)
 };
 
 // One call as the planner sees it.
@@ -159,6 +161,7 @@ inline void describe(const Variant &v, int id, sgemm_cfg *out)
     out->fixed_ns = v.fixed_ns > 0 ? v.fixed_ns : (int)kTileFixedNs;
     out->spill_permille = v.spill_permille;
     out->spill_full_permille = v.spill_full_permille;
+    out->coresident = v.coresident > 1 ? v.coresident : 1;
 }
 
 // Default tile order: groups of 8 tile rows and the XCD remap.
@@ -245,7 +248,11 @@ inline double estimate_ns(const Variant &v, const Problem &p, int splits, int k_
         xcd_operand_bytes(v, tiles, (int)ceil_div_ll(p.M, v.bm), kc, cus) > kL2Bytes)
         slice_ns = slice_ns * (tiles <= cus ? v.spill_permille : v.spill_full_permille) / 1000.0;
     const double fixed = v.fixed_ns > 0 ? (double)v.fixed_ns : kTileFixedNs;
-    double t = (double)rounds * (fixed + (double)slices * slice_ns);
+    // co-resident workgroups pay their fixed costs together, once per wave of
+    // cus * coresident tiles, and share the CU's matrix cores for the slices
+    const long long waves = v.coresident > 1 ? ceil_div_ll(tiles, (long long)cus * v.coresident)
+                                             : rounds;
+    double t = (double)waves * fixed + (double)rounds * (double)slices * slice_ns;
     if (splits > 1)
         t += kReduceFixedNs +
              4.0 * (double)p.batch * p.M * (double)partial_ld(p.N) * (splits + 1) / kReduceBytesPerNs;

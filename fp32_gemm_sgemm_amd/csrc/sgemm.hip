@@ -38,7 +38,7 @@ Variant mfma_variant(int eff_permille, int eff_one_permille, int eff_unaligned_p
                    {reinterpret_cast<const void *>(
                         &sgemm::sgemm_mfma_kernel<BM, BN, BK, WM, WN, STAGE_AT>),
                     nullptr, nullptr, nullptr},
-                   eff_permille, eff_one_permille, eff_unaligned_permille, 0, 0, 0};
+                   eff_permille, eff_one_permille, eff_unaligned_permille, 0, 0, 0, 0};
 }
 
 // OPS: bit (transa + 2*transb) set for each operand layout to compile.  DW:
@@ -51,7 +51,7 @@ Variant dl_variant(int eff_permille, int eff_one_permille, int eff_unaligned_per
     Variant v{SGEMM_KERNEL_MFMA, BM, BN, BK, WM, WN, -1, STAGES, DW ? 1 : 0,
               T::NT, (int)(T::LDS_FLOATS * sizeof(float)),
               {nullptr, nullptr, nullptr, nullptr}, eff_permille, eff_one_permille,
-              eff_unaligned_permille, 0, 0, 0};
+              eff_unaligned_permille, 0, 0, 0, 0};
     v.fn[0] = reinterpret_cast<const void *>(
         &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, false, false, DW, PIPE>);
     if constexpr ((OPS & 2) != 0)
@@ -70,7 +70,7 @@ Variant dl_variant(int eff_permille, int eff_one_permille, int eff_unaligned_per
 // waves_m = W describes the waves (they share the tile and split K).
 template <int W>
 Variant sk_variant(int eff_permille, int eff_one_permille, int eff_unaligned_permille, int fixed_ns,
-                   int spill_permille, int spill_full_permille)
+                   int spill_permille, int spill_full_permille, int coresident)
 {
     typedef sgemm::SkTraits<W> T;
     return Variant{SGEMM_KERNEL_MFMA, T::BM, T::BN, 8, W, 1, -1, 0, 0,
@@ -80,7 +80,7 @@ Variant sk_variant(int eff_permille, int eff_one_permille, int eff_unaligned_per
                     reinterpret_cast<const void *>(&sgemm::sgemm_mfma_sk_kernel<W, false, true>),
                     reinterpret_cast<const void *>(&sgemm::sgemm_mfma_sk_kernel<W, true, true>)},
                    eff_permille, eff_one_permille, eff_unaligned_permille, fixed_ns,
-                   spill_permille, spill_full_permille};
+                   spill_permille, spill_full_permille, coresident};
 }
 
 Variant valu_variant()
@@ -90,7 +90,7 @@ Variant valu_variant()
                    T::NT, (int)(T::LDS_FLOATS * sizeof(float)),
                    {reinterpret_cast<const void *>(&sgemm::sgemm_valu_kernel),
                     nullptr, nullptr, nullptr},
-                   0, 0, 0, 0, 0, 0};
+                   0, 0, 0, 0, 0, 0, 0};
 }
 
 constexpr int kAllOps = 0xf;
@@ -106,11 +106,14 @@ constexpr int kCrossSliceAgpr = 6;
 // with rows that are not 16-byte aligned (32 BM - 5 x 32 BN - 5, K = 4099).
 // `python -m fp32_gemm_sgemm_amd.calibrate` measures them; the figures below
 // come from one such run on MI355X, with the launch floor every launch pays
-// taken off each time.  The K-split 32x32 tiles carry three more numbers:
-// their fixed cost per tile in ns, and the factors (x1000) by which a slice
-// slows once the operand rows and columns one XCD's tiles read exceed its L2,
-// over one round and over several; their rates are measured where those fit
-// (the others use the model's common 2.5 us, and no spill term).
+// taken off each time.  The K-split 32x32 tiles carry four more numbers:
+// their fixed cost per tile in ns; the factors (x1000) by which a slice slows
+// once the operand rows and columns one XCD's tiles read exceed its L2, over
+// one round and over several (their rates are measured where those fit); and
+// how many of their workgroups share a CU (from their register use: 62, 72
+// and 72 per lane for W = 4, 8, 16 in the NN layout, so 8, 3 and 1), whose
+// fixed costs overlap.  The others use the model's common 2.5 us, no spill
+// term and one fixed cost per round.
 // The 4-byte direct-load variants serve only rows that are not 16-byte
 // aligned.  0 keeps a variant out of automatic selection (comparison
 // kernels, dominated tiles).
@@ -138,9 +141,9 @@ const Variant kVariants[] = {
     dl_variant<64, 64, 32, 2, 2, 2, kAllOps, false, kCrossSliceAgpr>(884, 659, 500),  // 20: direct loads, 4 waves of 32x32
     dl_variant<64, 64, 32, 2, 2, 2, kAllOps, true, kCrossSliceAgpr>(877, 646, 906),  // 21: 4-byte direct loads
     dl_variant<128, 128, 32, 4, 2, 2, kAllOps, true, kCrossSliceAgpr>(926, 903, 922),  // 22: 4-byte direct loads, 8 waves of 32x64
-    sk_variant<4>(1043, 582, 769, 3799, 1643, 1798),       // 23: 32x32, K split over 4 waves
-    sk_variant<16>(726, 550, 405, 4557, 1108, 1432),       // 24: 32x32, K split over 16 waves
-    sk_variant<8>(967, 584, 614, 3680, 1155, 1625),        // 25: 32x32, K split over 8 waves
+    sk_variant<4>(500, 576, 424, 3204, 1054, 990, 8),       // 23: 32x32, K split over 4 waves
+    sk_variant<16>(681, 572, 581, 3242, 1045, 1179, 1),    // 24: 32x32, K split over 16 waves
+    sk_variant<8>(608, 623, 507, 3207, 1053, 1085, 3),      // 25: 32x32, K split over 8 waves
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 

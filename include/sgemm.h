@@ -69,6 +69,7 @@ typedef struct sgemm_cfg {
                            operand rows and columns one XCD's tiles read exceed
                            its L2, over one round (0 = not modelled) */
     int spill_full_permille; /* the same over several rounds */
+    int coresident;     /* workgroups per CU whose fixed costs the model overlaps */
 } sgemm_cfg;
 
 /*

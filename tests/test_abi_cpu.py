@@ -67,15 +67,17 @@ def test_version_and_variants(lib):
         assert v.bm % 32 == 0 and v.bn % 32 == 0 and v.bk % 8 == 0
     assert kinds == {sg.binding.SGEMM_KERNEL_MFMA, sg.binding.SGEMM_KERNEL_VALU}
     # cost-model figures: every variant reports a fixed cost; only the tiles
-    # that split K over their waves (32 x 32 x 8) price an L2 spill, as a
-    # slowdown (>= 1000 permille)
+    # that split K over their waves (32 x 32 x 8) price an L2 spill and
+    # overlap the fixed costs of co-resident workgroups
     for i in range(n):
         v = sg.sgemm_f32_variant(i)
-        assert 0 < v.fixed_ns < 20000
+        assert 0 < v.fixed_ns < 20000 and v.coresident >= 1
         if (v.bm, v.bn, v.bk) == (32, 32, 8):
-            assert v.spill_permille >= 1000
+            assert v.spill_permille > 0 and v.spill_full_permille > 0
+            # LDS bounds the workgroups that can share a CU
+            assert v.coresident * v.lds_bytes <= 160 * 1024
         else:
-            assert v.spill_permille == 0 and v.fixed_ns == 2500
+            assert v.spill_permille == 0 and v.fixed_ns == 2500 and v.coresident == 1
     with pytest.raises(sg.SgemmError):
         sg.sgemm_f32_variant(n)
     with pytest.raises(sg.SgemmError):
