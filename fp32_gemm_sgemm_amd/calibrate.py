@@ -20,7 +20,7 @@ and the cost model of select.hpp,
   t = rounds * (2.5 us + slices * 2 BM BN BK / (614.4 FLOP/ns * eff)),
 
 is inverted for eff (x1000), the three numbers each variant carries in the
-table of sgemm.hip.  The variants that split K over their waves (32 x 32
+table of sgemm.hip (printed at the end as table lines).  The variants that split K over their waves (32 x 32
 tiles, whose L2 spill the model prices) also get their own fixed cost and
 spill factors (one round, several rounds), and are measured at K where the
 operands one XCD reads fit in its L2 (calibrate_ksplit); several of their
@@ -267,7 +267,8 @@ def main(argv=None):
         else:
             table[vid] = calibrate_variant(torch, sg, vid, args.ms, floor)
     for vid, e in table.items():
-        extra = f", {e['fixed']}, {e['spill']}, {e['spill_full']}" if "spill" in e else ""
+        co = sg.sgemm_f32_variant(vid).coresident
+        extra = f", {e['fixed']}, {e['spill']}, {e['spill_full']}, {co}" if "spill" in e else ""
         print(f"variant {vid}: ({e['full']}, {e['one']}, {e['unaligned']}{extra})", flush=True)
     if not args.no_strips:
         fixed, rate = calibrate_strips(torch, sg, args.ms)
