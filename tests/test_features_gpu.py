@@ -54,6 +54,33 @@ def test_transposed_layouts_every_variant(ta, tb):
             check_general(C, As, Bs, ta, tb)
 
 
+def _ksplit_variants():
+    return [v for v in range(sg.sgemm_f32_num_variants())
+            if (sg.sgemm_f32_variant(v).bm, sg.sgemm_f32_variant(v).bk) == (32, 8)]
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_ksplit_tiles_k_ranges(ta, tb):
+    """The tiles that split K over their W waves: each wave takes a range of
+    whole 8-deep groups and keeps four groups of loads in flight (prefetch
+    clamped to its last whole group); the last wave may end in a ragged
+    group.  K values cover a single k, one ragged group, exactly one group per
+    wave, one k more or less, waves left with no range (K below 8 (W - 1)),
+    whole prefetch blocks plus a remainder, and ragged M and N."""
+    for vid in _ksplit_variants():
+        W = sg.sgemm_f32_variant(vid).waves_m
+        ks = sorted({1, 3, 7, 8, 9, 8 * W - 1, 8 * W, 8 * W + 1, 8 * (W - 1) - 3,
+                     8 * W * 4 * 2 + 5, 8 * W * 4 * 3 + 8 * 3, 8 * W * 5 + 17} - {0})
+        for K in ks:
+            if K <= 0:
+                continue
+            M, N = 70, 45
+            note(f"k-split variant {vid} (W={W}) ta={ta} tb={tb} {M}x{N}x{K}")
+            A, B = inputs.make_operands(M, N, K, seed=700 + K + vid)
+            As, Bs = stored(A, ta), stored(B, tb)
+            check_general(run_general(As, Bs, ta, tb, cfg=forced(vid)), As, Bs, ta, tb)
+
+
 @pytest.mark.parametrize("ta,tb", LAYOUTS)
 def test_transposed_exact_cases(ta, tb):
     """Closed forms through the transposed paths: a stored permutation
