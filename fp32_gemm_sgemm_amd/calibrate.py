@@ -20,7 +20,9 @@ and the cost model of select.hpp,
   t = rounds * (2.5 us + slices * 2 BM BN BK / (614.4 FLOP/ns * eff)),
 
 is inverted for eff (x1000), the three numbers each variant carries in the
-table of sgemm.hip (printed at the end as table lines).  The variants that split K over their waves (32 x 32
+table of sgemm.hip (printed at the end as table lines).  With --fit-fixed the
+listed variants get their own fixed cost in place of the 2.5 us (fit_fixed),
+a fourth number in their table line.  The variants that split K over their waves (32 x 32
 tiles, whose L2 spill the model prices) also get their own fixed cost and
 spill factors (one round, several rounds), and are measured at K where the
 operands one XCD reads fit in its L2 (calibrate_ksplit); several of their
@@ -144,7 +146,22 @@ def _record(vid, v, name, M, N, K, t, e):
           flush=True)
 
 
-def calibrate_variant(torch, sg, vid, warm_ms, floor):
+def fit_fixed(torch, sg, vid, warm_ms, floor):
+    """Fixed cost per tile (ns) of a variant whose pipeline fill differs from
+    the common 2.5 us: its one-round shape (16 BM x 16 BN) two slices deep
+    and at K = 2048, the line through them taken back to K = 0."""
+    v = sg.sgemm_f32_variant(vid)
+    M1, N1, k1 = 16 * v.bm, 16 * v.bn, 2 * v.bk
+    t1 = _forced(torch, sg, vid, M1, N1, k1, warm_ms)
+    t2 = _forced(torch, sg, vid, M1, N1, 2048, warm_ms)
+    fixed = max(t1 - (t2 - t1) / (2048.0 - k1) * k1 - floor, 0.0)
+    print(json.dumps({"variant": vid, "fit": "fixed", "K": [k1, 2048],
+                      "us": [round(t1 / 1e3, 2), round(t2 / 1e3, 2)], "fixed_ns": round(fixed)}),
+          flush=True)
+    return fixed
+
+
+def calibrate_variant(torch, sg, vid, warm_ms, floor, fixed=TILE_FIXED_NS):
     v = sg.sgemm_f32_variant(vid)
     bm, bn, bk = v.bm, v.bn, v.bk
     shapes = {
@@ -156,7 +173,7 @@ def calibrate_variant(torch, sg, vid, warm_ms, floor):
     out = {}
     for name, (M, N, K) in shapes.items():
         t = _forced(torch, sg, vid, M, N, K, warm_ms)
-        e = eff_from_time(t - floor, bm, bn, bk, M, N, K)
+        e = eff_from_time(t - floor, bm, bn, bk, M, N, K, fixed)
         out[name] = round(e)
         _record(vid, v, name, M, N, K, t, e)
     return out
@@ -249,6 +266,9 @@ def main(argv=None):
                     help="comma-separated variant ids (default: every selectable one)")
     ap.add_argument("--ms", type=float, default=150.0, help="warm-up per measurement, ms")
     ap.add_argument("--no-strips", action="store_true")
+    ap.add_argument("--fit-fixed", default="",
+                    help="comma-separated tile variants whose fixed cost is fitted instead "
+                         "of taken as 2.5 us (the 64-deep-slice ones)")
     args = ap.parse_args(argv)
     import torch
     import fp32_gemm_sgemm_amd as sg
@@ -260,15 +280,22 @@ def main(argv=None):
     else:
         vids = [i for i in range(sg.sgemm_f32_num_variants()) if _is_mfma(sg, i)]
     floor = launch_floor(torch, sg, args.ms)
+    fit = {int(x) for x in args.fit_fixed.split(",") if x}
     table = {}
     for vid in vids:
         if sg.sgemm_f32_variant(vid).spill_permille > 0:
             table[vid] = calibrate_ksplit(torch, sg, vid, args.ms, floor)
+        elif vid in fit:
+            fixed = fit_fixed(torch, sg, vid, args.ms, floor)
+            table[vid] = calibrate_variant(torch, sg, vid, args.ms, floor, fixed)
+            table[vid]["fit"] = round(fixed)
         else:
             table[vid] = calibrate_variant(torch, sg, vid, args.ms, floor)
     for vid, e in table.items():
         co = sg.sgemm_f32_variant(vid).coresident
         extra = f", {e['fixed']}, {e['spill']}, {e['spill_full']}, {co}" if "spill" in e else ""
+        if "fit" in e:
+            extra = f", {e['fit']}"
         print(f"variant {vid}: ({e['full']}, {e['one']}, {e['unaligned']}{extra})", flush=True)
     if not args.no_strips:
         fixed, rate = calibrate_strips(torch, sg, args.ms)

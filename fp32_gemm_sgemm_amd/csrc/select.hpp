@@ -69,6 +69,18 @@ constexpr int kMaxLdX = (1 << 25) - 512;
 // to chunks that must read as zero).
 constexpr int kMaxLdKDirect = 1 << 20;
 constexpr int kMaxLdXDirect = 1 << 24;
+// Variants with 64-deep slices hold 64 rows of an index-contiguous operand,
+// so they serve only leading dimensions up to this (offsets below 2^31 on
+// every fetch path).
+constexpr int kMaxLdXDeep = 1 << 23;
+
+// Whether variant v can serve problem p (beyond the sizes every variant takes).
+inline bool variant_fits(const Variant &v, const Problem &p)
+{
+    if (v.bk <= 32) return true;
+    const int ldx_a = p.transa ? p.lda : 0, ldx_b = p.transb ? 0 : p.ldb;
+    return ldx_a <= kMaxLdXDeep && ldx_b <= kMaxLdXDeep;
+}
 
 inline bool sizes_ok(const Problem &p)
 {
@@ -332,7 +344,7 @@ inline Choice select_plan(const Variant *vs, int n, const Problem &p, int cus, b
         for (int i = 0; i < n; ++i) {
             const Variant &v = vs[i];
             if (v.kernel != SGEMM_KERNEL_MFMA || v.eff_permille <= 0 || v.eff_one_permille <= 0 ||
-                v.eff_unaligned_permille <= 0 || !v.fn[op])
+                v.eff_unaligned_permille <= 0 || !v.fn[op] || !variant_fits(v, p))
                 continue;
             const int eff = variant_eff(v, aligned16, lds_ok, pass == 0);
             if (eff <= 0) continue;

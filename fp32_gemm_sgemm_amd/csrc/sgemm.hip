@@ -45,13 +45,14 @@ Variant mfma_variant(int eff_permille, int eff_one_permille, int eff_unaligned_p
 // 4-byte direct loads (rows need only be 4-byte aligned).
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int OPS, bool DW = false,
           int PIPE = 0>
-Variant dl_variant(int eff_permille, int eff_one_permille, int eff_unaligned_permille)
+Variant dl_variant(int eff_permille, int eff_one_permille, int eff_unaligned_permille,
+                   int fixed_ns = 0)
 {
     typedef sgemm::DlTraits<BM, BN, BK, WM, WN, STAGES, false, false, DW> T;
     Variant v{SGEMM_KERNEL_MFMA, BM, BN, BK, WM, WN, -1, STAGES, DW ? 1 : 0,
               T::NT, (int)(T::LDS_FLOATS * sizeof(float)),
               {nullptr, nullptr, nullptr, nullptr}, eff_permille, eff_one_permille,
-              eff_unaligned_permille, 0, 0, 0, 0};
+              eff_unaligned_permille, fixed_ns, 0, 0, 0};
     v.fn[0] = reinterpret_cast<const void *>(
         &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, false, false, DW, PIPE>);
     if constexpr ((OPS & 2) != 0)
@@ -137,13 +138,15 @@ const Variant kVariants[] = {
     mfma_variant<128, 128, 16, 2, 4, 0>(827, 825, 671),    // 16: 8 waves of 64x32
     mfma_variant<128, 128, 32, 2, 4, 1>(817, 790, 743),    // 17: 8 waves of 64x32, BK 32
     dl_variant<192, 192, 32, 2, 6, 2, kAllOps, true, kCrossSliceAgpr>(944, 936, 941),  // 18: 4-byte direct loads
-    mfma_variant<64, 64, 32, 2, 2, 1>(760, 612, 586),      // 19: 4 waves of 32x32
-    dl_variant<64, 64, 32, 2, 2, 2, kAllOps, false, kCrossSliceAgpr>(884, 659, 500),  // 20: direct loads, 4 waves of 32x32
-    dl_variant<64, 64, 32, 2, 2, 2, kAllOps, true, kCrossSliceAgpr>(877, 646, 906),  // 21: 4-byte direct loads
+    mfma_variant<64, 64, 32, 2, 2, 1>(0, 0, 0),            // 19: 4 waves of 32x32 (dominated by 20)
+    dl_variant<64, 64, 32, 2, 2, 2, kAllOps, false, kCrossSliceAgpr>(895, 662, 509, 3329),  // 20: direct loads, 4 waves of 32x32
+    dl_variant<64, 64, 32, 2, 2, 2, kAllOps, true, kCrossSliceAgpr>(903, 651, 897, 3874),  // 21: 4-byte direct loads
     dl_variant<128, 128, 32, 4, 2, 2, kAllOps, true, kCrossSliceAgpr>(926, 903, 922),  // 22: 4-byte direct loads, 8 waves of 32x64
     sk_variant<4>(500, 576, 424, 3204, 1054, 990, 8),       // 23: 32x32, K split over 4 waves
     sk_variant<16>(681, 572, 581, 3242, 1045, 1179, 1),    // 24: 32x32, K split over 16 waves
     sk_variant<8>(608, 623, 507, 3207, 1053, 1085, 3),      // 25: 32x32, K split over 8 waves
+    dl_variant<64, 64, 64, 2, 2, 2, kAllOps, false, kCrossSliceAgpr>(893, 765, 336, 4108),  // 26: direct loads, 64-deep slices
+    dl_variant<64, 64, 64, 2, 2, 2, kAllOps, true, kCrossSliceAgpr>(863, 706, 855, 4808),  // 27: 4-byte direct loads, 64-deep slices
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -489,7 +492,8 @@ int forced_cfg(const Problem &p, const sgemm_cfg *force, sgemm_cfg *cfg)
     if (!sgemm::sizes_ok(p)) return hipErrorInvalidValue;
     if (force->id < 0 || force->id >= kNumVariants || force->group_m < 0) return hipErrorInvalidValue;
     const int id = force->id;
-    if (!kVariants[id].fn[sgemm::op_index(p)]) return hipErrorInvalidValue;
+    if (!kVariants[id].fn[sgemm::op_index(p)] || !sgemm::variant_fits(kVariants[id], p))
+        return hipErrorInvalidValue;
     const int group_m = force->group_m, xcd = force->xcd_remap ? 1 : 0;
     if (!sgemm::finish_cfg(kVariants[id], id, p, force->splits, force->strip_m, force->strip_n, cfg))
         return hipErrorInvalidValue;

@@ -21,7 +21,9 @@
 //    one 16-byte chunk each) free of bank conflicts; a lane loads the global
 //    data that belongs at its LDS position.  f uses only row bits 0-3:
 //    BK = 16: f(r) = ((r >> 1) ^ (r >> 2)) & 3;
-//    BK = 32: f(r) = (r ^ ((r >> 3) & 1)) & 7.
+//    BK = 32: f(r) = (r ^ ((r >> 3) & 1)) & 7;
+//    BK = 64: f(r) = r & 15 (a row is the 64 banks' width, so 16 rows read
+//    16 distinct chunk positions).
 //  * Loads go through buffer resources ending at the operands' last
 //    elements; rows past the end read as zero, and data wholly past K, M or N
 //    gets an offset beyond every resource (also zero).  With 16-byte loads,
@@ -54,7 +56,8 @@ namespace sgemm {
 template <int BK> __device__ __forceinline__ int chunk_swizzle(int r)
 {
     if constexpr (BK == 16) return ((r >> 1) ^ (r >> 2)) & 3;
-    else return (r ^ ((r >> 3) & 1)) & 7;
+    else if constexpr (BK == 32) return (r ^ ((r >> 3) & 1)) & 7;
+    else return r & 15;
 }
 
 // Three adjacent floats with 4-byte alignment (the compiler picks the LDS
@@ -170,7 +173,7 @@ struct DlTraits {
     static constexpr int A_FLOATS = BM * BK;
     static constexpr int STAGE_FLOATS = BM * BK + BK * BN;
     static constexpr int LDS_FLOATS = STAGES * STAGE_FLOATS;
-    static_assert(BK == 16 || BK == 32, "swizzle defined for BK 16 and 32");
+    static_assert(BK == 16 || BK == 32 || BK == 64, "swizzle defined for BK 16, 32 and 64");
     static_assert(NB == 1 || NB == 2 || NB == 4, "wave tile columns must be 32, 64 or 128");
     static_assert(STAGES >= 2, "at least two LDS stages");
     static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS budget of one CU");

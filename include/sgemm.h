@@ -200,7 +200,9 @@ int sgemm_f32_workspace_size(int transa, int transb, int M, int N, int K,
  * cfg->xcd_remap the tile order, and cfg->strip_m, cfg->strip_n the edge
  * strips (0 .. min(4, M) rows and 0 .. min(4, N) columns; 0 for none); the
  * other fields are ignored.  Returns hipErrorInvalidValue for an id out of
- * range, a variant not compiled for the operand layout, cfg->group_m < 0,
+ * range, a variant not compiled for the operand layout, a variant with
+ * 64-deep slices (bk = 64) when the leading dimension of the operand stored
+ * index-contiguous (B, or a transposed A) exceeds 2^23, cfg->group_m < 0,
  * strips out of range, or a workspace too small for the split.  Same
  * arguments, ownership and errors as sgemm_f32_strided_batched.
  */

@@ -66,9 +66,9 @@ def test_version_and_variants(lib):
         assert 0 < v.lds_bytes <= 160 * 1024
         assert v.bm % 32 == 0 and v.bn % 32 == 0 and v.bk % 8 == 0
     assert kinds == {sg.binding.SGEMM_KERNEL_MFMA, sg.binding.SGEMM_KERNEL_VALU}
-    # cost-model figures: every variant reports a fixed cost; only the tiles
-    # that split K over their waves (32 x 32 x 8) price an L2 spill and
-    # overlap the fixed costs of co-resident workgroups
+    # cost-model figures: every variant reports a fixed cost (2.5 us or its
+    # own); only the tiles that split K over their waves (32 x 32 x 8) price an
+    # L2 spill and overlap the fixed costs of co-resident workgroups
     for i in range(n):
         v = sg.sgemm_f32_variant(i)
         assert 0 < v.fixed_ns < 20000 and v.coresident >= 1
@@ -77,7 +77,7 @@ def test_version_and_variants(lib):
             # LDS bounds the workgroups that can share a CU
             assert v.coresident * v.lds_bytes <= 160 * 1024
         else:
-            assert v.spill_permille == 0 and v.fixed_ns == 2500 and v.coresident == 1
+            assert v.spill_permille == 0 and v.coresident == 1
     with pytest.raises(sg.SgemmError):
         sg.sgemm_f32_variant(n)
     with pytest.raises(sg.SgemmError):
@@ -367,6 +367,30 @@ def test_selector_k_split_tiles_follow_the_l2(lib):
         assert p.id in spill and p.splits == 1
         ids[K] = p.id
     assert max(spill[ids[8192]], spill[ids[16384]]) <= min(spill[ids[512]], spill[ids[2048]])
+
+
+def test_deep_slice_variants_respect_their_stride_limit(lib):
+    """Variants with 64-deep slices hold 64 rows of the index-contiguous
+    operand per slice, so they serve its leading dimension only up to 2^23:
+    the selector passes them over beyond that, and a forced one is refused."""
+    deep = [i for i in range(sg.sgemm_f32_num_variants()) if sg.sgemm_f32_variant(i).bk == 64]
+    assert deep
+    big = (1 << 23) + 4
+    for transb, ldb in [(0, big), (0, 1 << 23)]:
+        p = sg.sgemm_f32_plan(1024, 1024, 4096, 4096, ldb, 1024, 256, transb=transb)
+        if ldb > (1 << 23):
+            assert p.id not in deep
+        for vid in deep:
+            cfg = sg.SgemmCfg()
+            cfg.id, cfg.group_m, cfg.xcd_remap = vid, 8, 1
+            r = lib.sgemm_f32_cfg_geometry(0, transb, 1024, 1024, 4096, 4096, ldb, 1024, 1,
+                                           ctypes.byref(cfg))
+            assert (r == HIP_ERROR_INVALID_VALUE) == (ldb > (1 << 23))
+    # a transposed A is index-contiguous too
+    cfg = sg.SgemmCfg()
+    cfg.id, cfg.group_m, cfg.xcd_remap = deep[0], 8, 1
+    assert lib.sgemm_f32_cfg_geometry(1, 0, 64, 64, 64, big, 64, 64, 1,
+                                      ctypes.byref(cfg)) == HIP_ERROR_INVALID_VALUE
 
 
 def test_cfg_geometry_of_forced_splits(lib):

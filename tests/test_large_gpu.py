@@ -35,6 +35,7 @@ MAX_LD_K = (1 << 22) - 64
 MAX_LD_X = (1 << 25) - 512
 DIRECT_LD_K = 1 << 20
 DIRECT_LD_X = 1 << 24
+DEEP_LD_X = 1 << 23       # index-contiguous stride limit of the 64-deep-slice variants
 
 
 def _free():
@@ -146,9 +147,16 @@ def test_leading_dimension_limits_every_variant(ta, tb, which):
     Ad = place(As, pad=lda - As.shape[1])
     Bd = place(Bs, pad=ldb - Bs.shape[1])
     assert Ad.stride(0) == lda and Bd.stride(0) == ldb
+    # variants with 64-deep slices serve an index-contiguous operand (B, or a
+    # transposed A) only up to DEEP_LD_X
+    has_x = ta == 1 or tb == 0
     for vid in _variants_for(ta, tb) + [None]:
         note(f"ld limits {which} ta={ta} tb={tb} lda={lda} ldb={ldb} variant {vid}")
         C = torch.full((M, N), float("nan"), device="cuda")
+        if vid is not None and sg.sgemm_f32_variant(vid).bk == 64 and has_x and ld_x > DEEP_LD_X:
+            with pytest.raises(sg.SgemmError):
+                sg.sgemm(Ad, Bd, out=C, cfg=forced(vid), transa=bool(ta), transb=bool(tb))
+            continue
         sg.sgemm(Ad, Bd, out=C, cfg=None if vid is None else forced(vid),
                  transa=bool(ta), transb=bool(tb))
         torch.cuda.synchronize()
