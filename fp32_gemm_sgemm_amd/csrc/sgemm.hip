@@ -106,8 +106,8 @@ constexpr int kCrossSliceAgpr = 6;
 // (32 BM x 32 BN), over one round, one workgroup per CU (16 BM x 16 BN), and
 // with rows that are not 16-byte aligned (32 BM - 5 x 32 BN - 5, K = 4099).
 // `python -m fp32_gemm_sgemm_amd.calibrate` measures them; the figures below
-// come from one such run on MI355X, with the launch floor every launch pays
-// taken off each time.  The K-split 32x32 tiles carry four more numbers:
+// come from such runs on MI355X (each family of related tiles from one run),
+// with the launch floor every launch pays taken off each time.  The K-split 32x32 tiles carry four more numbers:
 // their fixed cost per tile in ns; the factors (x1000) by which a slice slows
 // once the operand rows and columns one XCD's tiles read exceed its L2, over
 // one round and over several (their rates are measured where those fit); and
