@@ -109,7 +109,7 @@ def test_alpha_beta(alpha, beta):
     A, B = inputs.make_operands(M, N, K, seed=100)
     C0 = inputs.make_operands(M, N, 1, seed=101)[0][:, :1] * np.linspace(-1, 1, N, dtype=np.float32)
     C0 = np.ascontiguousarray(C0.astype(np.float32))
-    for vid in (None, 1, 7, 9, 11, 12, 13, 23, 24, 25):
+    for vid in (None, 1, 7, 9, 11, 12, 13, 23, 24, 25, 26, 27):
         note(f"alpha={alpha} beta={beta} variant {vid}")
         cfg = None if vid is None else forced(vid)
         C = run_general(A, B, 0, 0, alpha, beta, C0, cfg=cfg)
@@ -132,7 +132,7 @@ def test_beta_zero_ignores_nan_and_k_zero_scales():
     assert np.array_equal(C, (np.float32(-0.5) * C0).astype(np.float32))
 
 
-SPLIT_VARIANTS = [1, 7, 9, 11, 12, 13, 23, 24, 25]
+SPLIT_VARIANTS = [1, 7, 9, 11, 12, 13, 23, 24, 25, 26, 27]
 
 
 @pytest.mark.parametrize("K", [1000, 1001, 130])
