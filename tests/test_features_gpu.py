@@ -81,6 +81,46 @@ def test_ksplit_tiles_k_ranges(ta, tb):
             check_general(run_general(As, Bs, ta, tb, cfg=forced(vid)), As, Bs, ta, tb)
 
 
+def test_random_problems_through_the_selector():
+    """100 seeded random problems through the default plan: small, medium,
+    skinny with long K and wide with short K, half with sizes that are
+    multiples of 4; random layout, alpha/beta, workspace or none, padded
+    strides and 4-byte shifted starts.  The plans this reaches include the
+    K-split 32 x 32 tiles (with and without an outer split), the 64 x 64
+    tiles with 32- and 64-deep slices and edge strips."""
+    rng = np.random.default_rng(20261202)
+    for case in range(100):
+        kind = rng.integers(0, 4)
+        if kind == 0:
+            M, N, K = (int(x) for x in rng.integers(1, 200, size=3))
+        elif kind == 1:
+            M, N, K = (int(x) for x in rng.integers(1, 1100, size=3))
+        elif kind == 2:
+            M, N = (int(x) for x in rng.integers(1, 300, size=2))
+            K = int(rng.integers(500, 9000))
+        else:
+            M, N = (int(x) for x in rng.integers(500, 1500, size=2))
+            K = int(rng.integers(1, 700))
+        if rng.random() < 0.5:
+            M, N, K = [max(1, (x // 4) * 4) for x in (M, N, K)]
+        ta, tb = int(rng.integers(0, 2)), int(rng.integers(0, 2))
+        alpha = float(rng.choice([1.0, -0.5, 2.0]))
+        beta = float(rng.choice([0.0, 0.0, 1.0, -1.5]))
+        ws = bool(rng.random() < 0.5)
+        pad = tuple(int(x) for x in rng.choice([0, 0, 3, 4], size=3))
+        shift = tuple(int(x) for x in rng.choice([0, 0, 1], size=3))
+        A, B = inputs.make_operands(M, N, K, seed=3000 + case)
+        C0 = inputs.make_operands(M, N, 1, seed=5000 + case)[0] if beta != 0 else None
+        if C0 is not None:
+            C0 = np.ascontiguousarray(np.repeat(C0[:, :1], N, axis=1))
+        As, Bs = stored(A, ta), stored(B, tb)
+        note(f"random case {case}: {M}x{N}x{K} ta={ta} tb={tb} alpha={alpha} beta={beta} "
+             f"ws={ws} pad={pad} shift={shift}")
+        C = run_general(As, Bs, ta, tb, alpha=alpha, beta=beta, C0=C0, workspace=ws, pad=pad,
+                        shift=shift)
+        check_general(C, As, Bs, ta, tb, alpha=alpha, beta=beta, C0=C0)
+
+
 @pytest.mark.parametrize("ta,tb", LAYOUTS)
 def test_transposed_exact_cases(ta, tb):
     """Closed forms through the transposed paths: a stored permutation
