@@ -58,10 +58,9 @@ constexpr int kStripKChunk = 4608;   // K values of the small operand staged at 
 // plus 4, so the planes start 4 banks apart and the 8 different k one XC read
 // instruction touches (k, k+1, ..., k+7) fall in distinct banks.
 constexpr int kStripPlane = kStripKChunk / 4 + 4;
-constexpr int kStripXcWidth = 32;    // x per workgroup, XC order
-constexpr int kStripKcWidth = 32;    // x per workgroup, KC order
-constexpr int kStripKcGroups = 8;    // row groups of 4 rows, KC order
-constexpr int kStripKcPhases = kStripWaves / kStripKcGroups;
+constexpr int kStripXcWidth = 32;    // x per workgroup, either order
+constexpr int kStripKcWidth = 32;
+constexpr int kStripNarrowWidth = 16;  // KC x per workgroup when the strips are too few for the CUs
 
 template <bool B> struct StripTag { static constexpr bool value = B; };
 
@@ -75,6 +74,8 @@ struct Strip {
     int r;                // y range, 1 .. kStripMax
     int wgs;              // workgroups of this strip (0: no strip)
     int nt;               // XC order: read big with non-temporal loads
+    int narrow;           // 1: kStripNarrowWidth x per workgroup, else 32 (KC order
+                          // only: XC keeps 128-byte row segments)
 };
 
 // Up to two strips in one launch: workgroups [0, s[0].wgs) take strip 0, the
@@ -95,7 +96,15 @@ __device__ __forceinline__ void strip_block(const Strip &s, int wg, int K, int z
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: KC rows in SGPRs
     const int X = s.X;
-    constexpr int XB = KC ? kStripKcWidth : kStripXcWidth;
+    // XB x per workgroup.  XC: XQ = XB/4 lanes cover one row segment, so a
+    // wave holds 64/XQ lane groups and the workgroup KPH = 16 * 64/XQ K
+    // phases.  KC: RG = XB/4 row groups of 4 rows, times KCP = 16/RG K phases.
+    const int xq_bits = s.narrow ? 2 : 3;  // log2(XQ) = log2(RG)
+    const int XB = 4 << xq_bits;
+    const int XQ = 1 << xq_bits;
+    const int LG = 64 >> xq_bits;          // XC lane groups per wave
+    const int KPH = LG * kStripWaves;      // XC K phases
+    const int KCP = kStripWaves >> xq_bits;  // KC K phases
     const int x0 = wg * XB;
 
     // KC: acc[row][y]; XC: acc[y][x]
@@ -105,13 +114,14 @@ __device__ __forceinline__ void strip_block(const Strip &s, int wg, int K, int z
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
 
-    // XC: lane group kr (8 lanes, 32 consecutive x) of wave w takes k = kr + 8w
-    // (mod 128).  KC: wave w reads rows x0 + 4*(w%8) .. +3 at k = 4*lane +
-    // 256*(w/8) (mod 512); rows past X are clamped to X-1 (read, never stored).
-    const int xq = lane & 7, kr = lane >> 3;
+    // XC: lane group kr (XQ lanes, XB consecutive x) of wave w takes k = kr +
+    // LG*w (mod KPH).  KC: wave w reads rows x0 + 4*(w % RG) .. +3 at k =
+    // 4*lane + 256*(w / RG) (mod 256*KCP); rows past X are clamped to X-1
+    // (read, never stored).
+    const int xq = lane & (XQ - 1), kr = lane >> xq_bits;
     const int xc = x0 + 4 * xq;
     const bool x_full = xc + 3 < X;
-    const int rg = wave % kStripKcGroups, kp = wave / kStripKcGroups;
+    const int rg = wave & (XQ - 1), kp = wave >> xq_bits;
     const float *rows[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -166,15 +176,15 @@ __device__ __forceinline__ void strip_block(const Strip &s, int wg, int K, int z
             const int kfull = min(clen, K - c0 - 3);  // kk < kfull: k + 3 < K
             int kk = 256 * kp + 4 * lane;
 #pragma unroll 2
-            for (; kk < kfull; kk += 256 * kStripKcPhases) quad(kk, false);
+            for (; kk < kfull; kk += 256 * KCP) quad(kk, false);
             if (kk < clen) quad(kk, true);
         } else {
             auto xc_loop = [&](auto nt) {
                 constexpr bool NT = decltype(nt)::value;
-                const float *p = big + (int64_t)(c0 + kr + 8 * wave) * s.ld_big + xc;
-                const int64_t step = 128 * s.ld_big;
+                const float *p = big + (int64_t)(c0 + kr + LG * wave) * s.ld_big + xc;
+                const int64_t step = (int64_t)KPH * s.ld_big;
 #pragma unroll 8
-                for (int kk = kr + 8 * wave; kk < clen; kk += 128, p += step) {
+                for (int kk = kr + LG * wave; kk < clen; kk += KPH, p += step) {
                     f32x4 v;
                     if (x_full) {
                         if constexpr (NT)
@@ -222,8 +232,8 @@ __device__ __forceinline__ void strip_block(const Strip &s, int wg, int K, int z
             const int g = xi >> 2, i = xi & 3;
             float sum = red[g * 16 + i * 4 + y];
 #pragma unroll
-            for (int q = 1; q < kStripKcPhases; ++q)
-                sum += red[(g + kStripKcGroups * q) * 16 + i * 4 + y];
+            for (int q = 1; q < KCP; ++q)
+                sum += red[(g + XQ * q) * 16 + i * 4 + y];
             if (x0 + xi < X && y < s.r) {
                 float *p = out + (int64_t)(x0 + xi) * s.o_x + (int64_t)y * s.o_y;
                 *p = beta != 0.0f ? alpha * sum + beta * *p : alpha * sum;
@@ -231,7 +241,7 @@ __device__ __forceinline__ void strip_block(const Strip &s, int wg, int K, int z
         }
     } else {
 #pragma unroll
-        for (int off = 8; off < 64; off <<= 1)
+        for (int off = XQ; off < 64; off <<= 1)
 #pragma unroll
             for (int y = 0; y < 4; ++y)
 #pragma unroll
@@ -240,7 +250,7 @@ __device__ __forceinline__ void strip_block(const Strip &s, int wg, int K, int z
 #pragma unroll
             for (int y = 0; y < 4; ++y)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) red[(wave * 8 + xq) * 16 + y * 4 + e] = acc[y][e];
+                for (int e = 0; e < 4; ++e) red[(wave * XQ + xq) * 16 + y * 4 + e] = acc[y][e];
         }
         __syncthreads();
         if (tid < XB * 4) {
@@ -248,7 +258,7 @@ __device__ __forceinline__ void strip_block(const Strip &s, int wg, int K, int z
             const int q = xi >> 2, e = xi & 3;
             float sum = red[q * 16 + y * 4 + e];
 #pragma unroll
-            for (int w = 1; w < kStripWaves; ++w) sum += red[(w * 8 + q) * 16 + y * 4 + e];
+            for (int w = 1; w < kStripWaves; ++w) sum += red[(w * XQ + q) * 16 + y * 4 + e];
             if (x0 + xi < X && y < s.r) {
                 float *p = out + (int64_t)(x0 + xi) * s.o_x + (int64_t)y * s.o_y;
                 *p = beta != 0.0f ? alpha * sum + beta * *p : alpha * sum;
