@@ -308,8 +308,8 @@ def extras(torch, sg, steps, warm_ms, cus, peak):
     for name, M, N, K in [("8196x8192x8192 (4-row edge strip)", 8196, 8192, 8192),
                           ("2051^3 (3-row and 3-column strips, ld 2051)", 2051, 2051, 2051),
                           ("513x8192x1023 (lda 1023)", 513, 8192, 1023),
-                          ("1x8192x8192 (vector-shaped: strip kernel)", 1, 8192, 8192),
-                          ("8192x1x8192 (vector-shaped: strip kernel)", 8192, 1, 8192)]:
+                          ("1x8192x8192 (vector-shaped)", 1, 8192, 8192),
+                          ("8192x1x8192 (vector-shaped)", 8192, 1, 8192)]:
         A, B = operand((M, K)), operand((K, N))
         C = torch.empty((M, N), device="cuda")
         plan = sg.sgemm_f32_plan(M, N, K, K, N, N, cus)
