@@ -275,20 +275,30 @@ inline double estimate_ns(const Variant &v, const Problem &p, int splits, int k_
 // operand each strip reads whole (op(B) for the row strip, the first M - sm
 // rows of op(A) for the column strip).  Fitted on MI355X to 4-row products
 // of 2048^2 and 8192^2 streamed elements (fp32_gemm_sgemm_amd.calibrate):
-// about 10.6 us of fixed cost, then 6.9 TB/s when the streamed operand's rows
-// run along the strip (x-contiguous) and 5.1 TB/s when they run along k; the
-// slower rate is used.
+// about 10.6 us of fixed cost, then 5.8-6.9 TB/s when the streamed operand's
+// rows run along the strip (x-contiguous, XC) and 5.1-5.8 TB/s when they run
+// along k (KC); the model takes 6.0 and 5.1.
 constexpr double kStripFixedNs = 10500.0;
-constexpr double kStripBytesPerNs = 5100.0;
+constexpr double kStripBytesPerNs = 5100.0;    // streamed rows along k (KC)
+constexpr double kStripBytesPerNsXc = 6000.0;  // streamed rows along the strip (XC)
+// The launch floor (dispatch, completion) inside kStripFixedNs: a strip
+// launch beside a tiled block pays it on top of the tiles' launch; strips
+// that are the whole product pay it as every plan does, so the model, which
+// leaves the floor out of the tiles' costs, leaves it out there too.
+constexpr double kLaunchFloorNs = 3300.0;
 
 inline double strip_ns(const Problem &p, int sm, int sn)
 {
     const long long rows_left = p.M - sm;
     const bool row_strip = sm > 0, col_strip = sn > 0 && rows_left > 0;
     if (!row_strip && !col_strip) return 0.0;
-    const double elems = (row_strip ? (double)p.K * p.N : 0.0) +
-                         (col_strip ? (double)p.K * rows_left : 0.0);
-    return kStripFixedNs + 4.0 * elems * p.batch / kStripBytesPerNs;
+    // the row strip streams op(B) (XC unless B is transposed), the column
+    // strip op(A) (XC when A is transposed)
+    const double rate_r = p.transb ? kStripBytesPerNs : kStripBytesPerNsXc;
+    const double rate_c = p.transa ? kStripBytesPerNsXc : kStripBytesPerNs;
+    const double ns = (row_strip ? 4.0 * p.K * (double)p.N / rate_r : 0.0) +
+                      (col_strip ? 4.0 * p.K * (double)rows_left / rate_c : 0.0);
+    return kStripFixedNs + ns * p.batch;
 }
 
 struct Choice {
@@ -353,8 +363,9 @@ inline Choice select_plan(const Variant *vs, int n, const Problem &p, int cus, b
             for (int a = 0; a < nsm; ++a) {
                 for (int b = 0; b < nsn; ++b) {
                     const Problem q = main_block(p, sms[a], sns[b]);
-                    const double ts = strip_ns(p, sms[a], sns[b]);
+                    double ts = strip_ns(p, sms[a], sns[b]);
                     if (q.M == 0 || q.N == 0) {
+                        ts -= kLaunchFloorNs;
                         // no tiled block: the strips are the whole product
                         if (best.id < 0 || ts < best_t) {
                             best = {i, 1, sms[a], sns[b]};
