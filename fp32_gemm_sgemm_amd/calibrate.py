@@ -1,6 +1,6 @@
 """Measure the figures the selector's cost model uses, on the GPU at hand.
 
-    python -m fp32_gemm_sgemm_amd.calibrate [--variants 11,13,...] [--ms 150]
+    python -m fp32_gemm_sgemm_amd.calibrate [--variants 4,6,...] [--ms 150]
 
 First the launch floor: what every launch costs beyond the model (dispatch,
 completion, the events), from one-tile products of the small-tile reference
@@ -50,7 +50,7 @@ if ROOT not in sys.path:
 CU_FLOP_PER_NS = 157.3e3 / 256.0
 TILE_FIXED_NS = 2500.0
 CUS = 256
-REF_VARIANT = 20  # 64 x 64 x 32 tiles, direct loads: the launch-floor reference
+REF_VARIANT = 11  # 64 x 64 x 32 tiles, direct loads: the launch-floor reference
 
 
 _SLEEP = [0]
@@ -242,7 +242,7 @@ def calibrate_strips(torch, sg, warm_ms):
             B = torch.empty((N, K) if tb else (K, N), device="cuda").uniform_(-1, 1)
             C = torch.empty((M, N), device="cuda")
             cfg = sg.SgemmCfg()
-            cfg.id, cfg.group_m, cfg.xcd_remap, cfg.strip_m = 11, 8, 1, M
+            cfg.id, cfg.group_m, cfg.xcd_remap, cfg.strip_m = 4, 8, 1, M
             t = _time(torch, lambda: sg.sgemm(A, B, out=C, cfg=cfg, transb=bool(tb),
                                               workspace=False), warm_ms)
             nbytes = 4.0 * K * N

@@ -116,37 +116,28 @@ constexpr int kCrossSliceAgpr = 6;
 // fixed costs overlap.  The others use the model's common 2.5 us, no spill
 // term and one fixed cost per round.
 // The 4-byte direct-load variants serve only rows that are not 16-byte
-// aligned.  0 keeps a variant out of automatic selection (comparison
-// kernels, dominated tiles).
+// aligned.  The vector-FMA comparison kernel carries no figures: the selector
+// never picks it.
 const Variant kVariants[] = {
     mfma_variant<256, 256, 16, 4, 2, 0>(888, 887, 690),    // 0: 8 waves of 64x128
     mfma_variant<128, 128, 16, 2, 2, 0>(848, 754, 587),    // 1: 4 waves of 64x64
-    mfma_variant<128, 128, 32, 2, 2, 1>(0, 0, 0),          // 2: 4 waves of 64x64, BK 32
-    mfma_variant<128, 256, 16, 2, 2, 0>(0, 0, 0),          // 3: 4 waves of 64x128
-    mfma_variant<256, 128, 16, 4, 1, 0>(0, 0, 0),          // 4: 4 waves of 64x128
-    mfma_variant<256, 256, 16, 4, 2, -1>(0, 0, 0),         // 5: plain order (comparison)
-    mfma_variant<128, 128, 16, 2, 2, -1>(0, 0, 0),         // 6: plain order (comparison)
-    valu_variant(),                                        // 7: vector-FMA comparison
-    mfma_variant<192, 192, 16, 2, 6, 0>(0, 0, 0),          // 8: 12 waves of 96x32
-    mfma_variant<192, 192, 32, 2, 6, 1>(886, 871, 710),    // 9: 12 waves of 96x32, BK 32
-    dl_variant<256, 256, 16, 4, 2, 4, 1>(0, 0, 0),         // 10: direct loads, 4 stages
-    dl_variant<256, 256, 32, 4, 2, 2, kAllOps, false, kCrossSliceAgpr>(959, 954, 660),  // 11: direct loads, 2 stages of BK 32
-    dl_variant<128, 128, 32, 2, 2, 3, kAllOps>(778, 761, 405),  // 12: direct loads
-    dl_variant<192, 192, 32, 2, 6, 2, kAllOps, false, kCrossSliceAgpr>(951, 936, 609),  // 13: direct loads
-    dl_variant<256, 256, 16, 4, 2, 3, 1>(0, 0, 0),         // 14: direct loads, 3 stages
-    dl_variant<128, 128, 32, 4, 2, 2, kAllOps, false, kCrossSliceAgpr>(925, 928, 661),  // 15: direct loads, 8 waves of 32x64
-    mfma_variant<128, 128, 16, 2, 4, 0>(827, 825, 671),    // 16: 8 waves of 64x32
-    mfma_variant<128, 128, 32, 2, 4, 1>(817, 790, 743),    // 17: 8 waves of 64x32, BK 32
-    dl_variant<192, 192, 32, 2, 6, 2, kAllOps, true, kCrossSliceAgpr>(944, 936, 941),  // 18: 4-byte direct loads
-    mfma_variant<64, 64, 32, 2, 2, 1>(0, 0, 0),            // 19: 4 waves of 32x32 (dominated by 20)
-    dl_variant<64, 64, 32, 2, 2, 2, kAllOps, false, kCrossSliceAgpr>(895, 662, 509, 3329),  // 20: direct loads, 4 waves of 32x32
-    dl_variant<64, 64, 32, 2, 2, 2, kAllOps, true, kCrossSliceAgpr>(903, 651, 897, 3874),  // 21: 4-byte direct loads
-    dl_variant<128, 128, 32, 4, 2, 2, kAllOps, true, kCrossSliceAgpr>(926, 903, 922),  // 22: 4-byte direct loads, 8 waves of 32x64
-    sk_variant<4>(500, 576, 424, 3204, 1054, 990, 8),       // 23: 32x32, K split over 4 waves
-    sk_variant<16>(681, 572, 581, 3242, 1045, 1179, 1),    // 24: 32x32, K split over 16 waves
-    sk_variant<8>(608, 623, 507, 3207, 1053, 1085, 3),      // 25: 32x32, K split over 8 waves
-    dl_variant<64, 64, 64, 2, 2, 2, kAllOps, false, kCrossSliceAgpr>(893, 765, 336, 4108),  // 26: direct loads, 64-deep slices
-    dl_variant<64, 64, 64, 2, 2, 2, kAllOps, true, kCrossSliceAgpr>(863, 706, 855, 4808),  // 27: 4-byte direct loads, 64-deep slices
+    valu_variant(),                                        // 2: vector-FMA comparison
+    mfma_variant<192, 192, 32, 2, 6, 1>(886, 871, 710),    // 3: 12 waves of 96x32, BK 32
+    dl_variant<256, 256, 32, 4, 2, 2, kAllOps, false, kCrossSliceAgpr>(959, 954, 660),  // 4: direct loads, 2 stages of BK 32
+    dl_variant<128, 128, 32, 2, 2, 3, kAllOps>(778, 761, 405),  // 5: direct loads
+    dl_variant<192, 192, 32, 2, 6, 2, kAllOps, false, kCrossSliceAgpr>(951, 936, 609),  // 6: direct loads
+    dl_variant<128, 128, 32, 4, 2, 2, kAllOps, false, kCrossSliceAgpr>(925, 928, 661),  // 7: direct loads, 8 waves of 32x64
+    mfma_variant<128, 128, 16, 2, 4, 0>(827, 825, 671),    // 8: 8 waves of 64x32
+    mfma_variant<128, 128, 32, 2, 4, 1>(817, 790, 743),    // 9: 8 waves of 64x32, BK 32
+    dl_variant<192, 192, 32, 2, 6, 2, kAllOps, true, kCrossSliceAgpr>(944, 936, 941),  // 10: 4-byte direct loads
+    dl_variant<64, 64, 32, 2, 2, 2, kAllOps, false, kCrossSliceAgpr>(895, 662, 509, 3329),  // 11: direct loads, 4 waves of 32x32
+    dl_variant<64, 64, 32, 2, 2, 2, kAllOps, true, kCrossSliceAgpr>(903, 651, 897, 3874),  // 12: 4-byte direct loads
+    dl_variant<128, 128, 32, 4, 2, 2, kAllOps, true, kCrossSliceAgpr>(926, 903, 922),  // 13: 4-byte direct loads, 8 waves of 32x64
+    sk_variant<4>(500, 576, 424, 3204, 1054, 990, 8),      // 14: 32x32, K split over 4 waves
+    sk_variant<16>(681, 572, 581, 3242, 1045, 1179, 1),    // 15: 32x32, K split over 16 waves
+    sk_variant<8>(608, 623, 507, 3207, 1053, 1085, 3),     // 16: 32x32, K split over 8 waves
+    dl_variant<64, 64, 64, 2, 2, 2, kAllOps, false, kCrossSliceAgpr>(893, 765, 336, 4108),  // 17: direct loads, 64-deep slices
+    dl_variant<64, 64, 64, 2, 2, 2, kAllOps, true, kCrossSliceAgpr>(863, 706, 855, 4808),  // 18: 4-byte direct loads, 64-deep slices
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 

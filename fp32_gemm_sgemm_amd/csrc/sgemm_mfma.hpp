@@ -49,10 +49,8 @@ __device__ __forceinline__ float frag_elem(const typename FragB<NB>::T &v, int c
     else return v[cb];
 }
 
-// STAGE_AT < 0: the plain order (fetch the next slice into registers,
-// multiply the current one, write the fetched slice to LDS at the end), kept
-// as a measured comparison.  STAGE_AT >= 0: the pipelined order described at
-// the main loop, with the LDS write after k group STAGE_AT.
+// STAGE_AT: the k group of a slice after which the next slice is written to
+// LDS (the pipelined order described at the main loop).
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGE_AT>
 struct MfmaTraits {
     static constexpr int NT = WAVES_M * WAVES_N * 64;
@@ -68,7 +66,8 @@ struct MfmaTraits {
     static_assert(WTM % 32 == 0 && RM >= 1, "wave tile rows must be a multiple of 32");
     static_assert(NB == 1 || NB == 2 || NB == 4, "wave tile columns must be 32, 64 or 128");
     static_assert(BK % 8 == 0, "BK must be a multiple of 8");
-    static_assert(STAGE_AT < BK / 8, "the LDS write must follow one of the slice's k groups");
+    static_assert(STAGE_AT >= 0 && STAGE_AT < BK / 8,
+                  "the LDS write must follow one of the slice's k groups");
     static_assert(A_VECS * NT * 4 == BM * BK, "A tile must split evenly into float4 per thread");
     static_assert(B_VECS * NT * 4 == BK * BN, "B tile must split evenly into float4 per thread");
     static_assert(NT % (BK / 4) == 0 && NT % (BN / 4) == 0, "load columns must not depend on v");
@@ -220,66 +219,44 @@ sgemm_mfma_kernel(GemmArgs g)
     // ---- main loop ---------------------------------------------------------------
     const int nk_real = (K + BK - 1) / BK;
     f32x4 ra0[A_VECS], rb0[B_VECS];
-    if constexpr (STAGE_AT < 0) {
-        const int nk = nk_real;
-        if (nk > 0) {
-            gload(0, ra0, rb0);
-            sstore(0, ra0, rb0);
-            __syncthreads();
-            for (int kt = 0; kt < nk; ++kt) {
-                const int cur = kt & 1;
-                const bool more = kt + 1 < nk;
-                if (more) gload(kt + 1, ra0, rb0);
+    // Pipelined order.  Two register staging sets: the global loads of
+    // slice kt+2 are issued at the start of slice kt, and slice kt+1
+    // (fetched one slice earlier) is written to the other LDS buffer after
+    // k group STAGE_AT, in the shadow of the remaining MFMAs.  A fetch has
+    // about one and a half slices of MFMA time to arrive, and the end of a
+    // slice holds only the barrier.  The LDS buffer written during slice
+    // kt was last read in slice kt-1, which every wave has left (the
+    // barrier closing it).  Fragments ping-pong between two register sets:
+    // the reads of group g+1 are issued before the MFMAs of group g.
+    f32x4 ra1[A_VECS], rb1[B_VECS];
+    // Slices are taken in pairs so the staging set of each is known at
+    // compile time; an odd count gets one more slice lying wholly past K,
+    // whose loads all read as zero, so the MFMA chain of the loop body is
+    // unconditional and its zero products leave the sums unchanged.
+    const int nk = (nk_real + 1) & ~1;
+    auto slice = [&](int kt, auto &ra_next, auto &rb_next, auto &ra_free, auto &rb_free) {
+        const int cur = kt & 1;
+        if (kt + 2 < nk) gload(kt + 2, ra_free, rb_free);
+        Frag f[2];
+        read_frag(cur, 0, f[0]);
 #pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    Frag f;
-                    read_frag(cur, g, f);
-                    mfma_frag(f);
-                }
-                if (more) sstore(cur ^ 1, ra0, rb0);
-                __syncthreads();
-            }
+        for (int g = 0; g < G; ++g) {
+            if (g + 1 < G) read_frag(cur, g + 1, f[(g + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_frag(f[g & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (g == STAGE_AT && kt + 1 < nk) sstore(cur ^ 1, ra_next, rb_next);
         }
-    } else {
-        // Pipelined order.  Two register staging sets: the global loads of
-        // slice kt+2 are issued at the start of slice kt, and slice kt+1
-        // (fetched one slice earlier) is written to the other LDS buffer after
-        // k group STAGE_AT, in the shadow of the remaining MFMAs.  A fetch has
-        // about one and a half slices of MFMA time to arrive, and the end of a
-        // slice holds only the barrier.  The LDS buffer written during slice
-        // kt was last read in slice kt-1, which every wave has left (the
-        // barrier closing it).  Fragments ping-pong between two register sets:
-        // the reads of group g+1 are issued before the MFMAs of group g.
-        f32x4 ra1[A_VECS], rb1[B_VECS];
-        // Slices are taken in pairs so the staging set of each is known at
-        // compile time; an odd count gets one more slice lying wholly past K,
-        // whose loads all read as zero, so the MFMA chain of the loop body is
-        // unconditional and its zero products leave the sums unchanged.
-        const int nk = (nk_real + 1) & ~1;
-        auto slice = [&](int kt, auto &ra_next, auto &rb_next, auto &ra_free, auto &rb_free) {
-            const int cur = kt & 1;
-            if (kt + 2 < nk) gload(kt + 2, ra_free, rb_free);
-            Frag f[2];
-            read_frag(cur, 0, f[0]);
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                if (g + 1 < G) read_frag(cur, g + 1, f[(g + 1) & 1]);
-                __builtin_amdgcn_sched_barrier(0);
-                mfma_frag(f[g & 1]);
-                __builtin_amdgcn_sched_barrier(0);
-                if (g == STAGE_AT && kt + 1 < nk) sstore(cur ^ 1, ra_next, rb_next);
-            }
-            __syncthreads();
-        };
-        if (nk > 0) {
-            gload(0, ra0, rb0);
-            sstore(0, ra0, rb0);
-            gload(1, ra1, rb1);
-            __syncthreads();
-            for (int kt = 0; kt < nk; kt += 2) {
-                slice(kt, ra1, rb1, ra0, rb0);
-                slice(kt + 1, ra0, rb0, ra1, rb1);
-            }
+        __syncthreads();
+    };
+    if (nk > 0) {
+        gload(0, ra0, rb0);
+        sstore(0, ra0, rb0);
+        gload(1, ra1, rb1);
+        __syncthreads();
+        for (int kt = 0; kt < nk; kt += 2) {
+            slice(kt, ra1, rb1, ra0, rb0);
+            slice(kt + 1, ra0, rb0, ra1, rb1);
         }
     }
 

@@ -33,11 +33,11 @@
 //    (DW kernels exist for that case).
 //
 // Pipelines (PIPE), one barrier per slice either way:
-//  * plain (PIPE & 3 == 0), per slice kt: wait for this thread's fetch of
+//  * plain (PIPE & 2 == 0), per slice kt: wait for this thread's fetch of
 //    slice kt, barrier (every wave's fetch of kt has landed and every wave has
 //    finished slice kt-1), issue the fetch of slice kt+STAGES-1 into the
 //    buffer slice kt-1 used, multiply slice kt.
-//  * cross-slice (PIPE & 3 == 2): the fetch of slice kt+STAGES-1 is
+//  * cross-slice (PIPE & 2): the fetch of slice kt+STAGES-1 is
 //    interleaved with the MFMAs of slice kt's first k group, the barrier sits
 //    before the last k group, and the next slice's first fragments are read
 //    in the shadow of that group's MFMAs, so no LDS latency and no burst of
@@ -239,9 +239,7 @@ sgemm_mfma_dl_kernel(GemmArgs g)
     // index at k0), the resource extent up to the operand's last element, and
     // the limit of the contiguous column (k for KC, the index for XC) below
     // which a chunk holds data.
-    // Loads [lo, hi) of the slice's A_LOADS + B_LOADS (A first); a slice that
-    // goes through registers is fetched whole by the call with lo == 0.
-    auto fetch = [&](int kt, int s, int lo, int hi) {
+    auto fetch = [&](int kt, int s) {
         const int k0 = kt * BK;
         const float *abase = TA ? A + (int64_t)k0 * lda + m0 : A + (int64_t)m0 * lda + k0;
         const float *bbase = TB ? B + (int64_t)n0 * ldb + k0 : B + (int64_t)k0 * ldb + n0;
@@ -261,7 +259,6 @@ sgemm_mfma_dl_kernel(GemmArgs g)
             // (the load size must be a literal: one call per size)
 #pragma unroll
             for (int j = 0; j < A_LOADS; ++j) {
-                if (j < lo || j >= hi) continue;
                 const int off = (int)(a_col[j] < a_lim ? a_off[j] : kOobOffset);
                 float *dst = smem + s * STAGE_FLOATS + (j * NW + wave) * 64 * EL;
                 if constexpr (DW) __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void *)dst, 4, off, 0, 0, 0);
@@ -269,13 +266,12 @@ sgemm_mfma_dl_kernel(GemmArgs g)
             }
 #pragma unroll
             for (int j = 0; j < B_LOADS; ++j) {
-                if (A_LOADS + j < lo || A_LOADS + j >= hi) continue;
                 const int off = (int)(b_col[j] < b_lim ? b_off[j] : kOobOffset);
                 float *dst = smem + s * STAGE_FLOATS + A_FLOATS + (j * NW + wave) * 64 * EL;
                 if constexpr (DW) __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_void *)dst, 4, off, 0, 0, 0);
                 else __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_void *)dst, 16, off, 0, 0, 0);
             }
-        } else if (lo == 0) {
+        } else {
             // One load's data at a time (loaded, masked, written to LDS), so
             // this rarely used path needs few staging registers.
             const auto ar = make_rsrc(abase, abytes);
@@ -410,7 +406,7 @@ sgemm_mfma_dl_kernel(GemmArgs g)
     constexpr int WAIT_LATER_LGKM0 = WAIT_LATER & ~(15 << 8);
     const int nk = (K + BK - 1) / BK;
     constexpr int LOADS_ALL = A_LOADS + B_LOADS;
-    if constexpr ((PIPE & 3) == 2) {
+    if constexpr ((PIPE & 2) != 0) {
         // Cross-slice pipeline.  Slice kt: the loads of slice kt+STAGES-1 are
         // issued among the MFMAs of k group 0; before the last k group each
         // thread waits for its own loads of slice kt+1 and its LDS reads of
@@ -423,7 +419,7 @@ sgemm_mfma_dl_kernel(GemmArgs g)
         if (nk > 0) {
 #pragma unroll
             for (int s = 0; s < STAGES - 1; ++s)
-                if (s < nk) fetch(s, s, 0, LOADS_ALL);
+                if (s < nk) fetch(s, s);
             if (STAGES - 2 < nk) __builtin_amdgcn_s_waitcnt(WAIT_LATER_LGKM0);
             else __builtin_amdgcn_s_waitcnt(WAIT_ALL);
             asm volatile("" ::: "memory");
@@ -448,7 +444,7 @@ sgemm_mfma_dl_kernel(GemmArgs g)
                     read_frag(s, gi + 1, f[(gi + 1) & 1]);
                     if (gi == 0) {
                         if constexpr (FULL) fetch_full(kt + STAGES - 1, (kt + STAGES - 1) % STAGES, af, bf);
-                        else if (more) fetch(kt + STAGES - 1, (kt + STAGES - 1) % STAGES, 0, LOADS_ALL);
+                        else if (more) fetch(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
                     }
                     mfma_frag(f[gi & 1]);
                     // fragment reads (and in group 0 the loads) among the MFMAs
@@ -501,35 +497,31 @@ sgemm_mfma_dl_kernel(GemmArgs g)
         }
         for (; kt < nk; ++kt) slice(kt, DlTag<false>());
     } else {
+        // Plain pipeline.
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
-        if (s < nk) fetch(s, s, 0, LOADS_ALL);
-    for (int kt = 0; kt < nk; ++kt) {
-        const int s = kt % STAGES;
-        // this thread's fetch of slice kt has landed once at most the later
-        // slices' fetches are outstanding (fewer near the end: wait for all)
-        if (kt + STAGES - 2 < nk) __builtin_amdgcn_s_waitcnt(WAIT_LATER_LGKM0);
-        else __builtin_amdgcn_s_waitcnt(WAIT_ALL);
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-        const bool more = kt + STAGES - 1 < nk;
-        const int kn = kt + STAGES - 1, sn = (kt + STAGES - 1) % STAGES;
-        // PIPE 1: the next slice's loads are issued a share per k group, between
-        // the fragment reads and the MFMAs, instead of all before the first read.
-        if ((PIPE & 3) == 0 && more) fetch(kn, sn, 0, LOADS_ALL);
-        Frag f[2];
-        read_frag(s, 0, f[0]);
+        for (int s = 0; s < STAGES - 1; ++s)
+            if (s < nk) fetch(s, s);
+        for (int kt = 0; kt < nk; ++kt) {
+            const int s = kt % STAGES;
+            // this thread's fetch of slice kt has landed once at most the later
+            // slices' fetches are outstanding (fewer near the end: wait for all)
+            if (kt + STAGES - 2 < nk) __builtin_amdgcn_s_waitcnt(WAIT_LATER_LGKM0);
+            else __builtin_amdgcn_s_waitcnt(WAIT_ALL);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            if (kt + STAGES - 1 < nk) fetch(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+            Frag f[2];
+            read_frag(s, 0, f[0]);
 #pragma unroll
-        for (int gi = 0; gi < G; ++gi) {
-            if (gi + 1 < G) read_frag(s, gi + 1, f[(gi + 1) & 1]);
-            if ((PIPE & 3) == 1 && more) fetch(kn, sn, gi * LOADS_ALL / G, (gi + 1) * LOADS_ALL / G);
-            __builtin_amdgcn_sched_barrier(0);
-            mfma_frag(f[gi & 1]);
-            __builtin_amdgcn_sched_barrier(0);
+            for (int gi = 0; gi < G; ++gi) {
+                if (gi + 1 < G) read_frag(s, gi + 1, f[(gi + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+                mfma_frag(f[gi & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-    }
     }
 
     // ---- epilogue ----------------------------------------------------------------------

@@ -232,8 +232,8 @@ __device__ __forceinline__ void strip_block(const Strip &s, int wg, int K, int z
             const int g = xi >> 2, i = xi & 3;
             float sum = red[g * 16 + i * 4 + y];
 #pragma unroll
-            for (int q = 1; q < KCP; ++q)
-                sum += red[(g + XQ * q) * 16 + i * 4 + y];
+            for (int q = 1; q < kStripWaves / 4; ++q)  // KCP = 2 or 4
+                if (q < KCP) sum += red[(g + XQ * q) * 16 + i * 4 + y];
             if (x0 + xi < X && y < s.r) {
                 float *p = out + (int64_t)(x0 + xi) * s.o_x + (int64_t)y * s.o_y;
                 *p = beta != 0.0f ? alpha * sum + beta * *p : alpha * sum;
@@ -241,11 +241,13 @@ __device__ __forceinline__ void strip_block(const Strip &s, int wg, int K, int z
         }
     } else {
 #pragma unroll
-        for (int off = XQ; off < 64; off <<= 1)
+        for (int off = 4; off < 64; off <<= 1) {  // off = XQ .. 32 (XQ = 4 or 8)
+            if (off < XQ) continue;
 #pragma unroll
             for (int y = 0; y < 4; ++y)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc[y][e] += __shfl_xor(acc[y][e], off);
+        }
         if (kr == 0) {
 #pragma unroll
             for (int y = 0; y < 4; ++y)

@@ -138,8 +138,8 @@ def test_ex_rejects_bad_forced_variant(lib):
     cfg.group_m = -1  # negative group height
     assert _ex(cfg) == HIP_ERROR_INVALID_VALUE
     cfg.group_m = 8
-    cfg.id = 7        # the vector-FMA comparison has no transposed-operand kernels
-    assert sg.sgemm_f32_variant_ops(7) == 1
+    cfg.id = 2        # the vector-FMA comparison has no transposed-operand kernels
+    assert sg.sgemm_f32_variant_ops(2) == 1
     assert _ex(cfg, ta=1) == HIP_ERROR_INVALID_VALUE
     cfg.id = 0
     cfg.splits = 4    # a split needs a workspace
@@ -315,7 +315,7 @@ def test_selector_strips(lib):
 
 def test_cfg_geometry_of_forced_strips(lib):
     cfg = sg.SgemmCfg()
-    cfg.id, cfg.group_m, cfg.xcd_remap = 11, 8, 1
+    cfg.id, cfg.group_m, cfg.xcd_remap = 4, 8, 1
     for sm, sn in [(0, 0), (1, 0), (0, 4), (3, 3), (4, 4)]:
         cfg.strip_m, cfg.strip_n = sm, sn
         g = sg.sgemm_f32_cfg_geometry(cfg, 0, 0, 1000, 700, 300, 300, 700, 700)
