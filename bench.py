@@ -24,13 +24,24 @@ One JSON line is printed.  Besides the driver's fields it holds:
                 under profiles/, or null if the kernel sources changed since.
   cpu_baseline  the CPU reference (oracle/) timed on this host on a bounded
                 sample of the same product (whole rows of C, about
-                --cpu-seconds of work), in TFLOP/s, with the threads used, and
-                on one thread over a smaller sample; the sampled rows are also
-                compared with the GPU result.
+                --cpu-seconds of work), in TFLOP/s, with the threads used and
+                the host's core count, and on one thread over a smaller
+                sample; the sampled rows are also compared with the GPU result
+                (n, n_bad, max normalised error, RRMSE).
   configs       every configuration of the measured workload set through
                 sgemm_f32 (the plain C ABI, no workspace): 512^3, 2048^3 (and
                 its identity-A run), 3072^3, 8192x8192x4096, 4096x4096x8192,
-                the ragged 4099^3 and 8192^3, each after a time-based warm-up.
+                the ragged 4099^3 and 8192^3, each after a time-based warm-up:
+                mean time per call over back-to-back calls, and the median,
+                min and p90 of per-call times.  Unless --no-cpu-baseline, each
+                carries `check`, its accuracy against the CPU reference (part
+                of the CPU-reference leg): full at 512^3 and for the
+                identity-A run (which must also equal B exactly), the seeded
+                4096-output sample otherwise, plus the last 3 rows and
+                columns of 4099^3 in full.
+  metric_figures  which numbers are the metric's 8192^3 and 3072^3 figures.
+  meta          device, HIP runtime and driver, ROCm and hipcc versions, the
+                power mode, and the host's cores.
   vendor        context only: torch.matmul in float32 (the ROCm BLAS libraries,
                 TF32 disabled) timed the same way at 8192^3 and 3072^3.
   extras        the library's other paths, each timed the same way after a
@@ -40,8 +51,10 @@ One JSON line is printed.  Besides the driver's fields it holds:
                 transposed-operand layouts at 8192^3 and 3072^3, strided
                 batches of attention-like products, the 1024 x 8192 x 8192
                 row band one GPU would run if 8192^3 were split over 8 GPUs,
-                and shapes whose few edge rows or columns (or all of them, for
-                products of 1 row or column) go to the strip kernel.
+                shapes whose few edge rows or columns (or all of them, for
+                products of 1 row or column) go to the strip kernel, and the
+                vector-FMA comparison kernel forced at 8192^3 and 3072^3
+                (with its fraction of valu_probe).
   mfma_probe    the sustained v_mfma_f32_32x32x2_f32 rate on register operands
                 (the matrix-core ceiling at the chip's actual clock), and the
                 headline's fraction of it.
@@ -143,9 +156,33 @@ def time_workload(torch, sg, w, steps, warmup, cfg=None, cold=False):
     }
 
 
-def time_call(torch, fn, steps, warm_ms):
-    """Mean ms per call of fn() over `steps` calls timed with HIP events on the
-    current stream, after at least warm_ms of warm-up calls."""
+_SLEEP_CYCLES = [0]
+
+
+def _queue_ahead(torch, ms=3.0):
+    """Enqueue a GPU sleep of about `ms` so that the launches queued after it
+    start back to back: the host's per-call cost (Python, ctypes, argument
+    checks) then does not pace small kernels."""
+    if not _SLEEP_CYCLES[0]:
+        s = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(10 ** 5)
+        e0.record(s)
+        torch.cuda._sleep(10 ** 6)
+        e1.record(s)
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES[0] = max(1, int(10 ** 6 / max(e0.elapsed_time(e1), 1e-3)))
+    torch.cuda._sleep(int(_SLEEP_CYCLES[0] * ms))
+
+
+def time_calls(torch, fn, steps, warm_ms, min_steps=20):
+    """GPU time per call of fn() on the current stream, after at least warm_ms
+    of warm-up calls.  Two passes, each queued behind a GPU sleep:
+      mean_ms  HIP events around max(steps, min_steps) back-to-back calls,
+               divided by the count (the throughput figure);
+      median_ms, min_ms, p90_ms  over per-call HIP event pairs of a second
+               pass of the same length (each pair brackets one call)."""
+    n = max(steps, min_steps)
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -156,12 +193,32 @@ def time_call(torch, fn, steps, warm_ms):
     for _ in range(max(3, int(warm_ms / one))):
         fn()
     torch.cuda.synchronize()
+    _queue_ahead(torch, min(20.0, 0.02 * n + 1.0))
     e0.record(stream)
-    for _ in range(steps):
+    for _ in range(n):
         fn()
     e1.record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    mean = e0.elapsed_time(e1) / n
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+    _queue_ahead(torch, min(20.0, 0.03 * n + 1.0))
+    for i in range(n):
+        ev[2 * i].record(stream)
+        fn()
+        ev[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n))
+    return {"mean_ms": mean, "median_ms": per[n // 2], "min_ms": per[0],
+            "p90_ms": per[min(n - 1, int(0.9 * n))], "calls": n}
+
+
+def time_call(torch, fn, steps, warm_ms):
+    """Mean ms per call of fn() (see time_calls)."""
+    return time_calls(torch, fn, steps, warm_ms)["mean_ms"]
+
+
+def _timing_fields(t):
+    return {k: round(t[k], 5) for k in ("median_ms", "min_ms", "p90_ms")}
 
 
 CONFIG_WORKLOADS = [
@@ -176,8 +233,11 @@ CONFIG_WORKLOADS = [
 ]
 
 
-def configs(torch, sg, steps, warm_ms, cus, peak):
-    """TFLOP/s of each workload configuration through sgemm_f32."""
+def configs(torch, sg, steps, warm_ms, cus, peak, checker=None):
+    """TFLOP/s of each workload configuration through sgemm_f32, with the
+    distribution of per-call times (at least 20 calls, 100 at the small
+    512^3).  `checker(w, A_np, B_np, C)`, when given, returns the accuracy
+    block of one configuration (the CPU-reference leg, cpu_config_check)."""
     from fp32_gemm_sgemm_amd import inputs
     out = []
     stream = torch.cuda.current_stream()
@@ -186,7 +246,6 @@ def configs(torch, sg, steps, warm_ms, cus, peak):
         A_np, B_np = inputs.workload_operands(w)
         A = torch.from_numpy(A_np).to("cuda")
         B = torch.from_numpy(B_np).to("cuda")
-        del A_np, B_np
         C = torch.empty((w.M, w.N), device="cuda")
         h = stream.cuda_stream
 
@@ -195,14 +254,20 @@ def configs(torch, sg, steps, warm_ms, cus, peak):
                                 C.data_ptr(), w.N, h)
             if code != 0:
                 raise RuntimeError(f"sgemm_f32 failed with hipError_t {code}")
-        ms = time_call(torch, call, steps, warm_ms)
+        t = time_calls(torch, call, steps, warm_ms, min_steps=100 if w.flops < 1e9 else 20)
+        ms = t["mean_ms"]
         plan = sg.sgemm_f32_plan(w.M, w.N, w.K, w.K, w.N, w.N, cus)
         tf = w.flops / (ms * 1e-3) / 1e12
-        out.append(dict(workload=name, value=round(tf, 3), unit="TFLOP/s", ms=round(ms, 5),
-                        frac_of_fp32_matrix_peak=round(tf / peak, 4), variant=plan.id,
-                        tile=f"{plan.bm}x{plan.bn}x{plan.bk}",
-                        strips=[plan.strip_m, plan.strip_n]))
-        del A, B, C
+        entry = dict(workload=name, value=round(tf, 3), unit="TFLOP/s", ms=round(ms, 5),
+                     **_timing_fields(t), calls=t["calls"],
+                     frac_of_fp32_matrix_peak=round(tf / peak, 4), variant=plan.id,
+                     tile=f"{plan.bm}x{plan.bn}x{plan.bk}",
+                     strips=[plan.strip_m, plan.strip_n])
+        if checker is not None:
+            torch.cuda.synchronize()
+            entry["check"] = checker(w, A_np, B_np, C)
+        out.append(entry)
+        del A, B, C, A_np, B_np
     torch.cuda.empty_cache()
     return out
 
@@ -269,6 +334,26 @@ def extras(torch, sg, steps, warm_ms, cus, peak):
             lay = ("T" if ta else "N") + ("T" if tb else "N")
             record(f"{n}^3 {lay}", 2.0 * n ** 3, ms, plan)
             del A, B, C
+    torch.cuda.empty_cache()
+
+    # the vector-FMA comparison kernel (the register-blocked design carried to
+    # 64-wide waves), forced, on the two shapes the metric names; its bound is
+    # the vector-ALU rate, reported beside it as frac_of_valu_probe
+    valu = next(i for i in range(sg.sgemm_f32_num_variants())
+                if sg.sgemm_f32_variant(i).kernel == sg.SGEMM_KERNEL_VALU)
+    for n in (8192, 3072):
+        A, B = operand((n, n)), operand((n, n))
+        C = torch.empty((n, n), device="cuda")
+        cfg = sg.SgemmCfg()
+        cfg.id, cfg.group_m, cfg.xcd_remap, cfg.splits = valu, 8, 1, 1
+        plan = sg.sgemm_f32_cfg_geometry(cfg, 0, 0, n, n, n, n, n, n)
+        h = stream.cuda_stream
+        ms = time_call(torch, lambda: chk(sg.sgemm_f32_ex(0, 0, n, n, n, 1.0, A.data_ptr(), n, 0,
+                                                      B.data_ptr(), n, 0, 0.0, C.data_ptr(), n, 0,
+                                                      1, 0, 0, h, cfg)), steps, warm_ms)
+        record(f"valu comparison {n}^3 (forced vector-FMA kernel)", 2.0 * n ** 3, ms, plan,
+               kernel="valu_fma")
+        del A, B, C
     torch.cuda.empty_cache()
 
     # strided batches: per-head products of attention (sequence 1024, head 128)
@@ -342,6 +427,24 @@ def vendor(torch, steps, warm_ms, peak):
     return out
 
 
+def host_cores():
+    """Cores of this host: all of them, and the ones this process may use."""
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover - non-Linux
+        affinity = os.cpu_count() or 1
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"os_cpu_count": os.cpu_count(), "affinity": affinity, "model": model}
+
+
 def cpu_baseline(w, A_np, B_np, C_gpu, seconds):
     """The CPU reference on whole rows of the same product, about `seconds` of
     work; its rows are also checked against the GPU result."""
@@ -352,6 +455,7 @@ def cpu_baseline(w, A_np, B_np, C_gpu, seconds):
     spent = 0.0
     n_bad = 0
     max_err = 0.0
+    sq_err = sq_ref = 0.0
     while rows < w.M and (spent < seconds or rows == 0):
         r1 = min(w.M, rows + nt)
         t0 = time.perf_counter()
@@ -360,6 +464,8 @@ def cpu_baseline(w, A_np, B_np, C_gpu, seconds):
         rep = oracle.compare(C_gpu[rows:r1], ref, absb)
         n_bad += rep["n_bad"]
         max_err = max(max_err, rep["max_norm_err"])
+        sq_err += float(np.sum((C_gpu[rows:r1].astype(np.float64) - ref) ** 2))
+        sq_ref += float(np.sum(ref * ref))
         rows = r1
     flops = 2.0 * rows * w.N * w.K
     # the same reference on one thread, over whole rows for about a sixth as long
@@ -372,13 +478,94 @@ def cpu_baseline(w, A_np, B_np, C_gpu, seconds):
     flops1 = 2.0 * rows1 * w.N * w.K
     return {
         "value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": nt, "kind": "oracle",
+        "threads": nt, "host_cores": host_cores(),
         "sample": f"rows 0..{rows - 1} of C ({rows} x {w.N} outputs, K = {w.K}, "
-                  f"{flops / 1e9:.1f} GFLOP) in {spent:.1f} s",
+                  f"{flops / 1e9:.1f} GFLOP) in {spent:.1f} s on {nt} threads",
         "single_thread": {"value": flops1 / spent1 / 1e12, "unit": "TFLOP/s",
                           "sample": f"rows 0..{rows1 - 1} in {spent1:.1f} s"},
         "check": {"n": rows * w.N, "n_bad": n_bad, "max_norm_err": max_err,
+                  "rrmse": (sq_err / sq_ref) ** 0.5 if sq_ref > 0 else 0.0,
                   "tol": oracle.TOL},
     }
+
+
+def cpu_config_check(w, A_np, B_np, C):
+    """Part of the CPU-reference leg: the accuracy of one configuration's GPU
+    result against the CPU reference.  Full comparison when the workload asks
+    for it (512^3, and the identity-A run, which must also equal B exactly);
+    otherwise the seeded sample of 4096 outputs (3584 uniform, 512 from the
+    256-wide edge band), plus every element of the last 3 rows and columns for
+    the ragged 4099^3."""
+    import numpy as np
+    import oracle
+    from fp32_gemm_sgemm_amd import inputs
+    import torch
+    t0 = time.perf_counter()
+    out = {}
+    if w.check == "full":
+        C_np = C.cpu().numpy()
+        ref, absb = oracle.sgemm_ref(A_np, B_np)
+        rep = oracle.compare(C_np, ref, absb)
+        out["mode"] = "full"
+        if w.variant == "identity":
+            out["exact_equal_B"] = bool(np.array_equal(C_np, B_np))
+    else:
+        last = 3 if w.M % 4 or w.N % 4 else 0
+        rows, cols = inputs.sample_indices(w.M, w.N, w.seed, last=last)
+        vals = C[torch.from_numpy(rows).to(C.device), torch.from_numpy(cols).to(C.device)]
+        ref, absb = oracle.sgemm_ref_sampled(A_np, B_np, rows, cols)
+        rep = oracle.compare(vals.cpu().numpy(), ref, absb)
+        out["mode"] = "sampled 4096 (3584 uniform + 512 edge band)" + \
+            (f", last {last} rows and columns in full" if last else "")
+    out.update({k: rep[k] for k in ("n", "n_bad", "max_norm_err", "rrmse")})
+    out["tol"] = oracle.TOL
+    out["cpu_s"] = round(time.perf_counter() - t0, 3)
+    return out
+
+
+def run_meta(torch):
+    """Where the numbers were taken: device, runtime and toolchain versions,
+    host (the workbook's rule for trustworthy timings: name the GPU, driver,
+    toolkit and power mode)."""
+    import ctypes
+    import subprocess
+    p = torch.cuda.get_device_properties(0)
+    meta = {"device": p.name, "arch": getattr(p, "gcnArchName", ""),
+            "compute_units": p.multi_processor_count,
+            "hbm_bytes": p.total_memory, "torch": torch.__version__,
+            "torch_hip": torch.version.hip}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so.7")
+        v = ctypes.c_int(0)
+        if hip.hipRuntimeGetVersion(ctypes.byref(v)) == 0:
+            meta["hip_runtime_version"] = v.value
+        if hip.hipDriverGetVersion(ctypes.byref(v)) == 0:
+            meta["hip_driver_version"] = v.value
+    except OSError:
+        pass
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            meta["rocm"] = f.read().strip()
+    except OSError:
+        pass
+    try:
+        r = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True,
+                           text=True, timeout=30)
+        meta["hipcc"] = " | ".join(l.strip() for l in r.stdout.splitlines()
+                                   if "version" in l.lower())[:300]
+    except (OSError, subprocess.SubprocessError):
+        pass
+    for card in sorted(os.listdir("/sys/class/drm")) if os.path.isdir("/sys/class/drm") else []:
+        path = f"/sys/class/drm/{card}/device/power_dpm_force_performance_level"
+        if card.startswith("card") and "-" not in card and os.path.exists(path):
+            try:
+                with open(path) as f:
+                    meta["power_dpm_force_performance_level"] = f.read().strip()
+                break
+            except OSError:
+                pass
+    meta["host"] = host_cores()
+    return meta
 
 
 def main(argv=None):
@@ -511,7 +698,8 @@ def main(argv=None):
         del r2
 
     if not args.no_configs:
-        result["configs"] = configs(torch, sg, args.steps, args.extra_warm_ms, cus, peak)
+        result["configs"] = configs(torch, sg, args.steps, args.extra_warm_ms, cus, peak,
+                                    checker=None if args.no_cpu_baseline else cpu_config_check)
     if not args.no_extras:
         result["extras"] = extras(torch, sg, args.steps, args.extra_warm_ms, cus, peak)
     if not args.no_vendor:
@@ -533,11 +721,23 @@ def main(argv=None):
             "what": "sustained non-packed v_fma_f32 rate, register operands only (the "
                     "instruction of the vector-FMA comparison kernel)",
         }
+        for e in result.get("extras", []):
+            if e.get("kernel") == "valu_fma":
+                e["frac_of_valu_probe"] = round(e["value"] / vceil, 4)
 
     if not args.no_cpu_baseline:
         C_host = r["C"].cpu().numpy()
         result["cpu_baseline"] = cpu_baseline(w, r["A"], r["B"], C_host, args.cpu_seconds)
 
+    # the metric's two figures: 8192^3 is `value` (the timed steps above),
+    # 3072^3 is `secondary` (the same protocol); the configs entries of those
+    # shapes are the same products timed by the per-configuration protocol
+    result["metric_figures"] = {
+        "8192^3": {"value": result["value"], "from": "value"},
+        "3072^3": ({"value": result["secondary"]["value"], "from": "secondary"}
+                   if "secondary" in result and args.secondary == SECONDARY else None),
+    }
+    result["meta"] = run_meta(torch)
     print(json.dumps(result), flush=True)
     return 0
 
