@@ -9,8 +9,8 @@ every entry point raises.
 """
 from .binding import (  # noqa: F401
     SgemmCfg, SgemmError, load, sgemm, sgemm_batched, sgemm_f32, sgemm_f32_cfg_geometry,
-    sgemm_f32_ex, sgemm_f32_gemm, sgemm_f32_num_variants, sgemm_f32_plan, sgemm_f32_query,
+    sgemm_f32_ex, sgemm_f32_ex_noalloc, sgemm_f32_gemm, sgemm_f32_num_variants, sgemm_f32_plan, sgemm_f32_query,
     sgemm_f32_strided_batched, sgemm_f32_variant, sgemm_f32_variant_ops, sgemm_f32_version,
     sgemm_f32_workspace_size, LIB_PATH, SGEMM_KERNEL_MFMA, SGEMM_KERNEL_VALU, SGEMM_OP_N,
-    SGEMM_OP_T,
+    SGEMM_OP_T, SGEMM_SCRATCH_BYTES,
 )

@@ -64,6 +64,7 @@ def load():
         "sgemm_f32_gemm": [i, i, i, i, i, f, p, i, p, i, f, p, i, p, sz, p],
         "sgemm_f32_strided_batched": [i, i, i, i, i, f, p, i, ll, p, i, ll, f, p, i, ll, i, p, sz, p],
         "sgemm_f32_ex": [i, i, i, i, i, f, p, i, ll, p, i, ll, f, p, i, ll, i, p, sz, p, cfgp],
+        "sgemm_f32_ex_noalloc": [i, i, i, i, i, f, p, i, ll, p, i, ll, f, p, i, ll, i, p, cfgp],
         "sgemm_f32_workspace_size": [i, i, i, i, i, i, i, i, i, ctypes.POINTER(sz)],
         "sgemm_f32_plan": [i, i, i, i, i, i, i, i, i, i, ll, cfgp],
         "sgemm_f32_cfg_geometry": [i, i, i, i, i, i, i, i, i, cfgp],
@@ -113,6 +114,18 @@ def sgemm_f32_ex(transa, transb, M, N, K, alpha, A, lda, stride_a, B, ldb, strid
     return load().sgemm_f32_ex(transa, transb, M, N, K, alpha, A, lda, stride_a, B, ldb,
                                stride_b, beta, C, ldc, stride_c, batch, workspace,
                                workspace_bytes, stream, ref)
+
+
+# Bytes of the library's per-GPU scratch (SGEMM_SCRATCH_BYTES in sgemm.h).
+SGEMM_SCRATCH_BYTES = 32 << 20
+
+
+def sgemm_f32_ex_noalloc(transa, transb, M, N, K, alpha, A, lda, stride_a, B, ldb, stride_b,
+                         beta, C, ldc, stride_c, batch, stream=0, cfg=None):
+    """Raw ABI call; K splits use the library's static per-GPU scratch."""
+    ref = ctypes.byref(cfg) if cfg is not None else None
+    return load().sgemm_f32_ex_noalloc(transa, transb, M, N, K, alpha, A, lda, stride_a, B,
+                                       ldb, stride_b, beta, C, ldc, stride_c, batch, stream, ref)
 
 
 def sgemm_f32_workspace_size(transa, transb, M, N, K, lda, ldb, ldc, batch=1):

@@ -163,6 +163,36 @@ hipError_t device_cus(int *cus)
     return hipSuccess;
 }
 
+// ---- static scratch (sgemm_f32_ex_noalloc) --------------------------------------
+// The partials of K splits for callers that cannot allocate: one array in each
+// GPU's memory, held from the code object's load until the process ends.  In
+// host code `scratch` names a host-side stand-in, not a device address: kernels
+// and copies use the address looked up per device below, never the name.
+static __device__ __align__(256) unsigned char scratch[SGEMM_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device (null: not yet)
+
+// The current device's address of `scratch`, looked up once per device with
+// that device current.
+hipError_t device_scratch(void **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
 // ---- validation ---------------------------------------------------------------
 bool misaligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) != 0; }
 
@@ -650,6 +680,33 @@ int sgemm_f32_ex(int transa, int transb, int M, int N, int K, float alpha,
 {
     const Call c = make_call(transa, transb, M, N, K, alpha, A, lda, stride_a, B, ldb, stride_b, beta,
                              C, ldc, stride_c, batch, workspace, workspace_bytes);
+    return run(c, stream, cfg);
+}
+
+int sgemm_f32_ex_noalloc(int transa, int transb, int M, int N, int K, float alpha,
+                         const float *A, int lda, long long stride_a,
+                         const float *B, int ldb, long long stride_b,
+                         float beta, float *C, int ldc, long long stride_c, int batch,
+                         hipStream_t stream, const sgemm_cfg *cfg)
+{
+    Call c = make_call(transa, transb, M, N, K, alpha, A, lda, stride_a, B, ldb, stride_b, beta,
+                       C, ldc, stride_c, batch, nullptr, 0);
+    // arguments are checked before the first HIP call (the scratch lookup)
+    const hipError_t v = validate(c);
+    if (v != hipSuccess) return v;
+    if (cfg) {
+        // a forced split must fit in the scratch (checked before any HIP call)
+        sgemm_cfg geo;
+        const int r = forced_cfg(c.p, cfg, &geo);
+        if (r != hipSuccess) return r;
+        if ((unsigned long long)geo.workspace_bytes > (unsigned long long)SGEMM_SCRATCH_BYTES)
+            return hipErrorOutOfMemory;
+    }
+    void *ws = nullptr;
+    const hipError_t e = device_scratch(&ws);
+    if (e != hipSuccess) return e;
+    c.ws = ws;
+    c.ws_bytes = SGEMM_SCRATCH_BYTES;
     return run(c, stream, cfg);
 }
 

@@ -216,6 +216,44 @@ int sgemm_f32_ex(int transa, int transb, int M, int N, int K,
                  void *workspace, size_t workspace_bytes,
                  hipStream_t stream, const sgemm_cfg *cfg);
 
+/* Bytes of device scratch the library holds per GPU for sgemm_f32_ex_noalloc. */
+#define SGEMM_SCRATCH_BYTES (32u << 20)
+
+/*
+ * sgemm_f32_ex_noalloc: sgemm_f32_ex without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Nothing is
+ * allocated on any call: a K split keeps its partial products in a scratch
+ * array of SGEMM_SCRATCH_BYTES that the library holds in the device memory of
+ * each GPU it runs on, from the first call on that GPU (which looks up the
+ * array's address there) until the process ends.  The caller still passes
+ * the operands and C as for sgemm_f32_ex.
+ *
+ *   cfg == NULL  the selector's choice among the plans whose partials fit in
+ *                the scratch (larger products run without a K split, as
+ *                sgemm_f32_strided_batched does with no workspace).
+ *   cfg != NULL  the forced configuration, as sgemm_f32_ex; a K split whose
+ *                partials need more than SGEMM_SCRATCH_BYTES is refused with
+ *                hipErrorOutOfMemory before anything is launched.
+ *
+ * The result is the one sgemm_f32_ex gives for the same plan with a
+ * workspace of SGEMM_SCRATCH_BYTES (bit for bit).  The scratch keeps the
+ * last call's partials; every split writes its partials before they are
+ * read, so nothing in it has to start at zero.  Every call on one GPU shares
+ * that GPU's scratch: calls that may overlap on one GPU (several streams or
+ * host threads) race on it and must be serialised by the caller.  Other
+ * arguments, ownership and errors as sgemm_f32_ex; the stream's device must
+ * be the current device.
+ */
+int sgemm_f32_ex_noalloc(int transa, int transb, int M, int N, int K,
+                         float alpha,
+                         const float *A, int lda, long long stride_a,
+                         const float *B, int ldb, long long stride_b,
+                         float beta,
+                         float *C, int ldc, long long stride_c,
+                         int batch,
+                         hipStream_t stream, const sgemm_cfg *cfg);
+
 /*
  * sgemm_f32_plan: the configuration the library chooses for these sizes on
  * a device with `num_cus` compute units (<= 0 means 256), given

@@ -45,6 +45,27 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, name)
 
 
+def test_scratch_size_matches_header(lib):
+    """The binding's scratch size is the header's, and the no-allocation
+    entry point is declared and exported."""
+    m = re.search(r"#define\s+SGEMM_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", open(HEADER).read())
+    assert m, "SGEMM_SCRATCH_BYTES not found"
+    assert sg.SGEMM_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))
+    assert "sgemm_f32_ex_noalloc" in declared_functions()
+
+
+def test_noalloc_refuses_bad_arguments_before_any_hip_call(lib):
+    """Invalid sizes or a forced variant out of range come back as errors from
+    the host checks (no device is touched: none exists here)."""
+    P = 1 << 20
+    assert sg.sgemm_f32_ex_noalloc(0, 0, -1, 4, 4, 1.0, P, 4, 0, 2 * P, 4, 0, 0.0, 3 * P, 4, 0,
+                                   1) == HIP_ERROR_INVALID_VALUE
+    cfg = sg.SgemmCfg()
+    cfg.id = sg.sgemm_f32_num_variants()
+    assert sg.sgemm_f32_ex_noalloc(0, 0, 4, 4, 4, 1.0, P, 4, 0, 2 * P, 4, 0, 0.0, 3 * P, 4, 0,
+                                   1, 0, cfg) == HIP_ERROR_INVALID_VALUE
+
+
 def test_no_undefined_own_symbols(lib):
     """Every kernel's host-side stub is present (a kernel template whose body
     cannot be compiled for the host would otherwise be left undefined)."""
