@@ -27,9 +27,11 @@ tiles, whose L2 spill the model prices) also get their own fixed cost and
 spill factors (one round, several rounds), and are measured at K where the
 operands one XCD reads fit in its L2 (calibrate_ksplit); several of their
 workgroups share a CU, and the model charges their fixed cost once per wave
-of co-resident workgroups.  The strip kernel is timed alone on two sizes of a
-4-row product in both storage orders of its streamed operand, and its fixed
-cost and streaming rate are fitted (kStripFixedNs, kStripBytesPerNs).
+of co-resident workgroups.  The strip kernel is timed alone on 4-row products
+in both storage orders of its streamed operand: two sizes that fill the chip
+give its fixed cost and the chip's streaming rates (kStripFixedNs,
+kStripBytesPerNs, kStripBytesPerNsXc), and a narrow product with long K the
+rate of one workgroup (kStripWgBytesPerNsXc, kStripWgBytesPerNsKcNarrow).
 
 Each timing is the median of HIP events around single launches queued behind
 a GPU sleep, after a time-based warm-up (the chip needs about 0.1 s of load
@@ -231,33 +233,56 @@ def calibrate_ksplit(torch, sg, vid, warm_ms, floor):
     return out
 
 
+def _strip_only(torch, sg, M, N, K, tb, warm_ms):
+    """GPU time (ns) of a product of M <= 4 rows run by the strip kernel alone
+    (a row strip streaming op(B): x-contiguous, k-contiguous when B is
+    transposed)."""
+    A = torch.empty((M, K), device="cuda").uniform_(-1, 1)
+    B = torch.empty((N, K) if tb else (K, N), device="cuda").uniform_(-1, 1)
+    C = torch.empty((M, N), device="cuda")
+    cfg = sg.SgemmCfg()
+    cfg.id, cfg.group_m, cfg.xcd_remap, cfg.strip_m = 4, 8, 1, M
+    t = _time(torch, lambda: sg.sgemm(A, B, out=C, cfg=cfg, transb=bool(tb), workspace=False),
+              warm_ms)
+    del A, B, C
+    return t
+
+
 def calibrate_strips(torch, sg, warm_ms):
-    """Fixed cost (ns) and rate (bytes/ns) of the strip kernel: a 4-row
-    product streams op(B) (x-contiguous, or k-contiguous when transposed)."""
-    pts = []
+    """The strip kernel's cost model: fixed cost (ns, the launch floor
+    included), the chip's streaming rate per order (bytes/ns) and the rate of
+    one workgroup when a strip has too few of them.  4-row products streaming
+    op(B): the chip's rates from N = 8192 and 16384 (256 and 512 workgroups,
+    K = 4096); the fixed cost is the larger of the two orders' intercepts.
+    The per-workgroup rates from N = 256 with K = 262144: 8 x-contiguous
+    workgroups, or 16 narrow k-contiguous ones."""
+    fits = {}
     for tb in (0, 1):
-        for n in (2048, 8192):
-            M, N, K = 4, n, n
-            A = torch.empty((M, K), device="cuda").uniform_(-1, 1)
-            B = torch.empty((N, K) if tb else (K, N), device="cuda").uniform_(-1, 1)
-            C = torch.empty((M, N), device="cuda")
-            cfg = sg.SgemmCfg()
-            cfg.id, cfg.group_m, cfg.xcd_remap, cfg.strip_m = 4, 8, 1, M
-            t = _time(torch, lambda: sg.sgemm(A, B, out=C, cfg=cfg, transb=bool(tb),
-                                              workspace=False), warm_ms)
+        pts = []
+        for n in (8192, 16384):
+            M, N, K = 4, n, 4096
+            t = _strip_only(torch, sg, M, N, K, tb, warm_ms)
             nbytes = 4.0 * K * N
-            pts.append((tb, nbytes, t))
+            pts.append((nbytes, t))
             print(json.dumps({"strip": "row", "transb": tb, "M": M, "N": N, "K": K,
                               "us": round(t / 1e3, 2), "GB/s": round(nbytes / t, 1)}),
                   flush=True)
-    fits = []
-    for tb in (0, 1):
-        (b0, t0), (b1, t1) = [(b, t) for (o, b, t) in pts if o == tb]
+        (b0, t0), (b1, t1) = pts
         rate = (b1 - b0) / (t1 - t0)
-        fits.append((t0 - b0 / rate, rate))
-    fixed = max(f for f, _ in fits)
-    rate = min(r for _, r in fits)
-    return fixed, rate
+        fits[tb] = (t0 - b0 / rate, rate)
+    fixed = max(f for f, _ in fits.values())
+    per_wg = {}
+    for tb in (0, 1):
+        M, N, K = 4, 256, 262144
+        t = _strip_only(torch, sg, M, N, K, tb, warm_ms)
+        wgs = N // 16 if tb else N // 32
+        nbytes = 4.0 * K * N
+        per_wg[tb] = nbytes / (t - fixed) / wgs
+        print(json.dumps({"strip": "row", "transb": tb, "M": M, "N": N, "K": K, "workgroups": wgs,
+                          "us": round(t / 1e3, 2), "GB/s per workgroup": round(per_wg[tb], 1)}),
+              flush=True)
+    return {"fixed": fixed, "kc": fits[1][1], "xc": fits[0][1], "wg_xc": per_wg[0],
+            "wg_kc_narrow": per_wg[1]}
 
 
 def main(argv=None):
@@ -266,6 +291,8 @@ def main(argv=None):
                     help="comma-separated variant ids (default: every selectable one)")
     ap.add_argument("--ms", type=float, default=150.0, help="warm-up per measurement, ms")
     ap.add_argument("--no-strips", action="store_true")
+    ap.add_argument("--strips-only", action="store_true",
+                    help="measure only the strip kernel's figures")
     ap.add_argument("--fit-fixed", default="",
                     help="comma-separated tile variants whose fixed cost is fitted instead "
                          "of taken as 2.5 us (the 64-deep-slice ones)")
@@ -275,11 +302,13 @@ def main(argv=None):
     if not torch.cuda.is_available():
         raise SystemExit("calibration needs a GPU")
     sg.load()
-    if args.variants:
+    if args.strips_only:
+        vids = []
+    elif args.variants:
         vids = [int(x) for x in args.variants.split(",")]
     else:
         vids = [i for i in range(sg.sgemm_f32_num_variants()) if _is_mfma(sg, i)]
-    floor = launch_floor(torch, sg, args.ms)
+    floor = launch_floor(torch, sg, args.ms) if vids else 0.0
     fit = {int(x) for x in args.fit_fixed.split(",") if x}
     table = {}
     for vid in vids:
@@ -298,8 +327,10 @@ def main(argv=None):
             extra = f", {e['fit']}"
         print(f"variant {vid}: ({e['full']}, {e['one']}, {e['unaligned']}{extra})", flush=True)
     if not args.no_strips:
-        fixed, rate = calibrate_strips(torch, sg, args.ms)
-        print(f"strips: kStripFixedNs = {fixed:.0f}, kStripBytesPerNs = {rate:.0f}", flush=True)
+        st = calibrate_strips(torch, sg, args.ms)
+        print(f"strips: kStripFixedNs = {st['fixed']:.0f}, kStripBytesPerNs = {st['kc']:.0f}, "
+              f"kStripBytesPerNsXc = {st['xc']:.0f}, kStripWgBytesPerNsXc = {st['wg_xc']:.1f}, "
+              f"kStripWgBytesPerNsKcNarrow = {st['wg_kc_narrow']:.1f}", flush=True)
     return 0
 
 

@@ -46,6 +46,8 @@ struct Variant {
     int spill_full_permille;     // the same over several rounds, where every CU streams
     int coresident;              // workgroups that share a CU and overlap their fixed
                                  // costs (0: one, the fixed cost is paid every round)
+    int ld64;                    // addresses its operands in 64 bits throughout: any
+                                 // leading dimension (0: the tile limits below apply)
 };
 
 // One call as the planner sees it.
@@ -58,11 +60,15 @@ struct Problem {
 
 inline int op_index(const Problem &p) { return p.transa + 2 * p.transb; }
 
-// Largest sizes accepted.  k0 + BK and similar sums stay in int, and the byte
-// offsets of a thread inside one slice stay below 2^32: up to 256 rows of a
-// k-contiguous operand (A, or a transposed B) and 32 rows of an
-// index-contiguous one (B, or a transposed A).
+// Largest sizes accepted (k0 + BK and similar sums stay in int); leading
+// dimensions up to the same.
 constexpr int kMaxDim = INT_MAX - 1024;
+// Leading dimensions the LDS-tiled kernels serve: the byte offsets of a
+// thread inside one slice stay below 2^32, for up to 256 rows of a
+// k-contiguous operand (A, or a transposed B) and 32 rows of an
+// index-contiguous one (B, or a transposed A).  Beyond them the selector
+// keeps to the variants that address in 64 bits (ld64: the 32 x 32 tiles that
+// split K over their waves) and to the strip kernel.
 constexpr int kMaxLdK = (1 << 22) - 64;
 constexpr int kMaxLdX = (1 << 25) - 512;
 // Direct global -> LDS loads keep those offsets below 2^31 (the offset given
@@ -77,6 +83,9 @@ constexpr int kMaxLdXDeep = 1 << 23;
 // Whether variant v can serve problem p (beyond the sizes every variant takes).
 inline bool variant_fits(const Variant &v, const Problem &p)
 {
+    if (v.ld64) return true;
+    if (p.lda > (p.transa ? kMaxLdX : kMaxLdK) || p.ldb > (p.transb ? kMaxLdK : kMaxLdX))
+        return false;
     if (v.bk <= 32) return true;
     const int ldx_a = p.transa ? p.lda : 0, ldx_b = p.transb ? 0 : p.ldb;
     return ldx_a <= kMaxLdXDeep && ldx_b <= kMaxLdXDeep;
@@ -91,7 +100,7 @@ inline bool sizes_ok(const Problem &p)
     if (p.lda < (a_min > 1 ? a_min : 1) || p.ldb < (b_min > 1 ? b_min : 1) ||
         p.ldc < (p.N > 1 ? p.N : 1))
         return false;
-    return p.lda <= (p.transa ? kMaxLdX : kMaxLdK) && p.ldb <= (p.transb ? kMaxLdK : kMaxLdX);
+    return p.lda <= kMaxDim && p.ldb <= kMaxDim && p.ldc <= kMaxDim;
 }
 
 inline bool direct_lds_ok(const Problem &p)
@@ -271,34 +280,88 @@ inline double estimate_ns(const Variant &v, const Problem &p, int splits, int k_
     return t;
 }
 
-// The strip kernel: one launch for both strips, bound by streaming the
-// operand each strip reads whole (op(B) for the row strip, the first M - sm
-// rows of op(A) for the column strip).  Fitted on MI355X to 4-row products
-// of 2048^2 and 8192^2 streamed elements (fp32_gemm_sgemm_amd.calibrate):
-// about 10.6 us of fixed cost, then 5.8-6.9 TB/s when the streamed operand's
-// rows run along the strip (x-contiguous, XC) and 5.1-5.8 TB/s when they run
-// along k (KC); the model takes 6.0 and 5.1.
-constexpr double kStripFixedNs = 10500.0;
-constexpr double kStripBytesPerNs = 5100.0;    // streamed rows along k (KC)
-constexpr double kStripBytesPerNsXc = 6000.0;  // streamed rows along the strip (XC)
+// ---- edge strips: geometry and cost ------------------------------------------
+// x (the strip's long index) per strip workgroup: 32, or 16 for a KC strip
+// (streamed rows along k) when the launch's strips have fewer workgroups than
+// the CUs, which doubles their workgroups (measured 20-23% faster on
+// 2048-row strips).  An XC strip keeps 32 (its 128-byte row segments).
+constexpr int kStripWidth = 32;
+constexpr int kStripNarrowWidth = 16;
+
+struct StripShape {
+    long long x;  // outputs along the strip (0: no strip)
+    int wgs;      // workgroups per batch entry
+    bool kc;      // the streamed operand's rows run along k
+    bool narrow;  // 16 x per workgroup
+};
+struct StripPlan {
+    StripShape row, col;  // rows M-sm.. of C (streams op(B)); columns N-sn.. of the rows above (op(A))
+};
+
+// The strips of a plan with sm rows and sn columns on `cus` compute units:
+// what the launch runs and what the cost model prices.
+inline StripPlan strip_plan(const Problem &p, int sm, int sn, int cus)
+{
+    StripPlan g = {};
+    const long long m_main = (long long)p.M - sm;
+    if (sm > 0) {
+        g.row.x = p.N;
+        g.row.kc = p.transb != 0;
+        g.row.wgs = (int)ceil_div_ll(p.N, kStripWidth);
+    }
+    if (sn > 0 && m_main > 0) {
+        g.col.x = m_main;
+        g.col.kc = p.transa == 0;
+        g.col.wgs = (int)ceil_div_ll(m_main, kStripWidth);
+    }
+    if (((long long)g.row.wgs + g.col.wgs) * p.batch < cus) {
+        for (StripShape *s : {&g.row, &g.col}) {
+            if (s->wgs && s->kc) {
+                s->narrow = true;
+                s->wgs = (int)ceil_div_ll(s->x, kStripNarrowWidth);
+            }
+        }
+    }
+    return g;
+}
+
+// The strip kernel's cost: one launch for both strips, each streaming the
+// operand it reads whole (op(B) for the row strip, the first M - sm rows of
+// op(A) for the column strip).  A strip streams at the chip's rate for its
+// order once it has enough workgroups, and otherwise at a per-workgroup rate
+// times its workgroups: a strip workgroup covers all of K, so a strip of few
+// columns runs on few CUs ("4.1 CUDA GEMM operator performance optimization",
+// section 12.5, on grids smaller than the SM count).  Fitted on MI355X by
+// fp32_gemm_sgemm_amd.calibrate: strip-only products streaming op(B), the
+// chip's rates from 256 and 512 workgroups, the per-workgroup rates from 8
+// (XC) and 16 narrow (KC) workgroups with long K.
+constexpr double kStripFixedNs = 7600.0;       // one launch, the launch floor included
+constexpr double kStripBytesPerNs = 3775.0;    // streamed rows along k (KC), whole chip
+constexpr double kStripBytesPerNsXc = 5556.0;  // streamed rows along the strip (XC), whole chip
+constexpr double kStripWgBytesPerNsXc = 37.0;  // one XC workgroup
+constexpr double kStripWgBytesPerNsKcNarrow = 30.8;  // one narrow KC workgroup
 // The launch floor (dispatch, completion) inside kStripFixedNs: a strip
 // launch beside a tiled block pays it on top of the tiles' launch; strips
 // that are the whole product pay it as every plan does, so the model, which
 // leaves the floor out of the tiles' costs, leaves it out there too.
 constexpr double kLaunchFloorNs = 3300.0;
 
-inline double strip_ns(const Problem &p, int sm, int sn)
+inline double strip_stream_ns(const StripShape &s, int K, int batch)
 {
-    const long long rows_left = p.M - sm;
-    const bool row_strip = sm > 0, col_strip = sn > 0 && rows_left > 0;
-    if (!row_strip && !col_strip) return 0.0;
-    // the row strip streams op(B) (XC unless B is transposed), the column
-    // strip op(A) (XC when A is transposed)
-    const double rate_r = p.transb ? kStripBytesPerNs : kStripBytesPerNsXc;
-    const double rate_c = p.transa ? kStripBytesPerNsXc : kStripBytesPerNs;
-    const double ns = (row_strip ? 4.0 * p.K * (double)p.N / rate_r : 0.0) +
-                      (col_strip ? 4.0 * p.K * (double)rows_left / rate_c : 0.0);
-    return kStripFixedNs + ns * p.batch;
+    if (s.wgs == 0) return 0.0;
+    const double chip = s.kc ? kStripBytesPerNs : kStripBytesPerNsXc;
+    // a 32-wide KC strip runs only when the launch fills the CUs
+    const double per_wg = s.kc ? (s.narrow ? kStripWgBytesPerNsKcNarrow : chip) : kStripWgBytesPerNsXc;
+    const double wgs = (double)s.wgs * batch;
+    const double rate = per_wg * wgs < chip ? per_wg * wgs : chip;
+    return 4.0 * K * (double)s.x * batch / rate;
+}
+
+inline double strip_ns(const Problem &p, int sm, int sn, int cus)
+{
+    const StripPlan g = strip_plan(p, sm, sn, cus);
+    if (g.row.wgs == 0 && g.col.wgs == 0) return 0.0;
+    return kStripFixedNs + strip_stream_ns(g.row, p.K, p.batch) + strip_stream_ns(g.col, p.K, p.batch);
 }
 
 struct Choice {
@@ -363,7 +426,7 @@ inline Choice select_plan(const Variant *vs, int n, const Problem &p, int cus, b
             for (int a = 0; a < nsm; ++a) {
                 for (int b = 0; b < nsn; ++b) {
                     const Problem q = main_block(p, sms[a], sns[b]);
-                    double ts = strip_ns(p, sms[a], sns[b]);
+                    double ts = strip_ns(p, sms[a], sns[b], cus);
                     if (q.M == 0 || q.N == 0) {
                         ts -= kLaunchFloorNs;
                         // no tiled block: the strips are the whole product

@@ -81,7 +81,7 @@ Variant sk_variant(int eff_permille, int eff_one_permille, int eff_unaligned_per
                     reinterpret_cast<const void *>(&sgemm::sgemm_mfma_sk_kernel<W, false, true>),
                     reinterpret_cast<const void *>(&sgemm::sgemm_mfma_sk_kernel<W, true, true>)},
                    eff_permille, eff_one_permille, eff_unaligned_permille, fixed_ns,
-                   spill_permille, spill_full_permille, coresident};
+                   spill_permille, spill_full_permille, coresident, 1};
 }
 
 Variant valu_variant()
@@ -376,12 +376,14 @@ hipError_t launch_strips(const Call &c, int sm, int sn, int cus, hipStream_t str
 {
     const Problem &p = c.p;
     const int m_main = p.M - sm, n_main = p.N - sn;
+    // workgroups, order and width of each strip (shared with the cost model)
+    const sgemm::StripPlan g = sgemm::strip_plan(p, sm, sn, cus);
     sgemm::StripArgs a = {};
     a.K = p.K;
     a.alpha = c.alpha;
     a.beta = c.beta;
     sgemm::Strip &rs = a.s[0], &cs = a.s[1];
-    if (sm > 0) {
+    if (g.row.wgs > 0) {
         // out(x, y) = C[m_main + y][x] = sum_k op(B)[k][x] * op(A)[m_main + y][k]
         rs.big = c.B;
         rs.ld_big = p.ldb;
@@ -402,9 +404,10 @@ hipError_t launch_strips(const Call &c, int sm, int sn, int cus, hipStream_t str
         rs.batch_out = c.sc;
         rs.X = p.N;
         rs.r = sm;
-        rs.wgs = (int)sgemm::ceil_div_ll(p.N, sgemm::kStripXcWidth);
+        rs.wgs = g.row.wgs;
+        rs.narrow = g.row.narrow ? 1 : 0;
     }
-    if (sn > 0 && m_main > 0) {
+    if (g.col.wgs > 0) {
         // out(x, y) = C[x][n_main + y] = sum_k op(A)[x][k] * op(B)[k][n_main + y]
         cs.big = c.A;
         cs.ld_big = p.lda;
@@ -425,21 +428,8 @@ hipError_t launch_strips(const Call &c, int sm, int sn, int cus, hipStream_t str
         cs.batch_out = c.sc;
         cs.X = m_main;
         cs.r = sn;
-        cs.wgs = (int)sgemm::ceil_div_ll(m_main, sgemm::kStripKcWidth);
-    }
-    // Strips too few for the CUs: a strip whose big operand runs along k
-    // (KC) takes workgroups of half the rows, twice as many (measured 20-23%
-    // faster on 2048-row strips).  An XC strip keeps its 128-byte row
-    // segments (halving them cost up to 36%).
-    if ((long long)(rs.wgs + cs.wgs) * p.batch < cus) {
-        if (rs.wgs && p.transb) {
-            rs.narrow = 1;
-            rs.wgs = (int)sgemm::ceil_div_ll(p.N, sgemm::kStripNarrowWidth);
-        }
-        if (cs.wgs && !p.transa) {
-            cs.narrow = 1;
-            cs.wgs = (int)sgemm::ceil_div_ll(m_main, sgemm::kStripNarrowWidth);
-        }
+        cs.wgs = g.col.wgs;
+        cs.narrow = g.col.narrow ? 1 : 0;
     }
     // An x-contiguous stream reads non-temporally when the other strip shares
     // the launch (it keeps L2 for that strip's staged operand).

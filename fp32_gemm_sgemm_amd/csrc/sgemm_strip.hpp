@@ -58,9 +58,6 @@ constexpr int kStripKChunk = 4608;   // K values of the small operand staged at 
 // plus 4, so the planes start 4 banks apart and the 8 different k one XC read
 // instruction touches (k, k+1, ..., k+7) fall in distinct banks.
 constexpr int kStripPlane = kStripKChunk / 4 + 4;
-constexpr int kStripXcWidth = 32;    // x per workgroup, either order
-constexpr int kStripKcWidth = 32;
-constexpr int kStripNarrowWidth = 16;  // KC x per workgroup when the strips are too few for the CUs
 
 template <bool B> struct StripTag { static constexpr bool value = B; };
 
@@ -74,8 +71,8 @@ struct Strip {
     int r;                // y range, 1 .. kStripMax
     int wgs;              // workgroups of this strip (0: no strip)
     int nt;               // XC order: read big with non-temporal loads
-    int narrow;           // 1: kStripNarrowWidth x per workgroup, else 32 (KC order
-                          // only: XC keeps 128-byte row segments)
+    int narrow;           // 1: 16 x per workgroup, else 32 (KC order only: XC keeps
+                          // 128-byte row segments); the host's strip_plan decides
 };
 
 // Up to two strips in one launch: workgroups [0, s[0].wgs) take strip 0, the

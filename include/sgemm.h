@@ -61,7 +61,12 @@ typedef struct sgemm_cfg {
        bandwidth-bound strip kernel instead of by tiles, and the tile
        geometry above (tiles_m, tiles_n, grid, splits, workspace_bytes)
        describes the (M - strip_m) x (N - strip_n) block that remains.  At
-       most 4 each.  Chosen by plan/query; an input of sgemm_f32_ex. */
+       most 4 each.  Chosen by plan/query; an input of sgemm_f32_ex.  A strip
+       whose streamed operand runs along k takes 16-row workgroups instead of
+       32 when the launch's strips have fewer workgroups (times the batch
+       count) than the device has compute units; the two forms add K in
+       different fixed orders, so a strip's bits depend on the batch count
+       and the device's CU count (and are reproducible for both fixed). */
     int strip_m, strip_n;
     /* The cost model's figures for this variant (reported, never read): */
     int fixed_ns;       /* fixed cost of one tile (ns) */
@@ -86,8 +91,11 @@ typedef struct sgemm_cfg {
  * Pointers must be 4-byte aligned; any dword-aligned start and stride runs
  * (16-byte loads and stores need only dword alignment on gfx950; rows that
  * start 16-byte aligned also allow direct global-to-LDS loads).  Limits:
- * M, N, K <= INT_MAX - 1024, lda <= 2^22 - 64, ldb <= 2^25 - 512 (byte
- * offsets inside one K slice are 32-bit).
+ * M, N, K, lda, ldb, ldc <= INT_MAX - 1024.  The LDS-tiled kernels use
+ * 32-bit byte offsets inside one K slice and serve lda <= 2^22 - 64 and
+ * ldb <= 2^25 - 512; larger leading dimensions run on the kernels that
+ * address in 64 bits (32 x 32 tiles that split K over their waves, and the
+ * edge-strip kernel), more slowly.
  *
  * Semantics of degenerate sizes: M == 0 or N == 0 does nothing; K == 0 sets
  * the M x N block of C to zero (an empty sum).
@@ -144,9 +152,10 @@ int sgemm_f32(int M, int N, int K,
  *             selector would like.  The workspace is scratch: its contents
  *             on entry do not matter, and the caller must not touch it until
  *             the work on `stream` completes.
- * Limits: the leading dimension of a k-contiguous operand (A, or a
- * transposed B) <= 2^22 - 64, of the other (B, or a transposed A)
- * <= 2^25 - 512.  Otherwise as sgemm_f32 (the two are the same for
+ * Limits: as sgemm_f32; the LDS-tiled kernels serve a leading dimension up
+ * to 2^22 - 64 for a k-contiguous operand (A, or a transposed B) and up to
+ * 2^25 - 512 for the other (B, or a transposed A), larger ones run on the
+ * 64-bit kernels.  Otherwise as sgemm_f32 (the two are the same for
  * transa = transb = SGEMM_OP_N, alpha = 1, beta = 0 and no workspace).
  */
 int sgemm_f32_gemm(int transa, int transb, int M, int N, int K,
@@ -200,9 +209,11 @@ int sgemm_f32_workspace_size(int transa, int transb, int M, int N, int K,
  * cfg->xcd_remap the tile order, and cfg->strip_m, cfg->strip_n the edge
  * strips (0 .. min(4, M) rows and 0 .. min(4, N) columns; 0 for none); the
  * other fields are ignored.  Returns hipErrorInvalidValue for an id out of
- * range, a variant not compiled for the operand layout, a variant with
- * 64-deep slices (bk = 64) when the leading dimension of the operand stored
- * index-contiguous (B, or a transposed A) exceeds 2^23, cfg->group_m < 0,
+ * range, a variant not compiled for the operand layout, an LDS-tiled
+ * variant for leading dimensions past its limits (2^22 - 64 for a
+ * k-contiguous operand, 2^25 - 512 for the other, 2^23 for an
+ * index-contiguous operand of a variant with 64-deep slices, bk = 64),
+ * cfg->group_m < 0,
  * strips out of range, or a workspace too small for the split.  Same
  * arguments, ownership and errors as sgemm_f32_strided_batched.
  */

@@ -66,6 +66,19 @@ def test_noalloc_refuses_bad_arguments_before_any_hip_call(lib):
                                    1, 0, cfg) == HIP_ERROR_INVALID_VALUE
 
 
+@pytest.mark.parametrize("M,N,K,tb", [(4, 32, 4194204, 0), (3, 100, 3000000, 0),
+                                     (4, 256, 1048576, 0), (4, 64, 2000000, 1)])
+def test_few_strip_workgroups_take_a_split_when_a_workspace_fits(lib, M, N, K, tb):
+    """A product of at most 4 rows whose strips would run on a handful of
+    workgroups (each covers all of K) is split across workgroups instead when
+    a workspace allows it; without one the strips remain."""
+    ldb = K if tb else N
+    q = sg.sgemm_f32_plan(M, N, K, K, ldb, N, 256, 0, tb, 1, 1 << 30)
+    assert q.grid > 0 and q.splits > 1 and q.grid >= 64, q.as_dict()
+    q = sg.sgemm_f32_plan(M, N, K, K, ldb, N, 256, 0, tb, 1, 0)
+    assert q.grid == 0 and q.strip_m == M
+
+
 def test_no_undefined_own_symbols(lib):
     """Every kernel's host-side stub is present (a kernel template whose body
     cannot be compiled for the host would otherwise be left undefined)."""
@@ -167,20 +180,40 @@ def test_ex_rejects_bad_forced_variant(lib):
     assert _ex(cfg, K=1024) == HIP_ERROR_INVALID_VALUE
 
 
-def test_ex_rejects_limits(lib):
-    # lda beyond the 32-bit in-slice offset limit
-    assert sg.sgemm_f32(4, 4, 4, P, 1 << 22, 2 * P, 4, 3 * P, 4, 0) == HIP_ERROR_INVALID_VALUE
-    assert sg.sgemm_f32(4, 4, 4, P, 4, 2 * P, 1 << 25, 3 * P, 4, 0) == HIP_ERROR_INVALID_VALUE
-    # the limits follow the layout: a transposed A is index-contiguous
-    cfg = sg.binding.SgemmCfg()
+def test_large_leading_dimensions_go_to_64_bit_kernels(lib):
+    """Any leading dimension up to INT_MAX - 1024 is accepted.  Past the
+    LDS-tiled kernels' 32-bit in-slice offsets (lda 2^22 - 64 for a
+    k-contiguous A, ldb 2^25 - 512 for B) the plan keeps to the variants that
+    address in 64 bits and the strip kernel; a forced tiled variant is
+    refused."""
     lib_ = sg.load()
-    out = sg.binding.SgemmCfg()
-    assert lib_.sgemm_f32_plan(1, 0, 4, 4, 4, (1 << 22), 4, 4, 1, 256, 0, ctypes.byref(out)) == 0
-    assert lib_.sgemm_f32_plan(0, 0, 4, 4, 4, (1 << 22), 4, 4, 1, 256, 0, ctypes.byref(out)) \
-        == HIP_ERROR_INVALID_VALUE
-    assert lib_.sgemm_f32_plan(0, 1, 4, 4, 4, 4, (1 << 22), 4, 1, 256, 0, ctypes.byref(out)) \
-        == HIP_ERROR_INVALID_VALUE
-    del cfg
+    ld64 = {i for i in range(sg.sgemm_f32_num_variants())
+            if (sg.sgemm_f32_variant(i).bm, sg.sgemm_f32_variant(i).bk) == (32, 8)}
+    big = (1 << 31) - 1 - 1024
+    cases = [(0, 0, 64, 64, 64, 1 << 23, 64), (0, 0, 64, 64, (1 << 22) + 64, (1 << 22) + 64, 64),
+             (0, 0, 1, 1, (1 << 22) + 64, (1 << 22) + 64, 1), (0, 0, 300, 200, 8, 8, 1 << 25),
+             (1, 0, 300, 200, 100, 1 << 26, 200), (0, 1, 300, 200, 100, 100, 1 << 23),
+             (0, 0, 4000, 4000, 100, big, big)]
+    for ta, tb, M, N, K, lda, ldb in cases:
+        out = sg.binding.SgemmCfg()
+        assert lib_.sgemm_f32_plan(ta, tb, M, N, K, lda, ldb, N, 1, 256, 0,
+                                   ctypes.byref(out)) == 0, (ta, tb, M, N, K, lda, ldb)
+        assert out.grid == 0 or out.id in ld64, (out.id, out.grid)
+        for ws in (0, 1 << 30):
+            q = sg.sgemm_f32_plan(M, N, K, lda, ldb, N, 256, ta, tb, 1, ws)
+            assert q.grid == 0 or q.id in ld64
+    # below the limits the tiled kernels stay available
+    assert sg.sgemm_f32_plan(4096, 4096, 4096, (1 << 22) - 64, 4096, 4096, 256).id not in ld64
+    # a forced tiled variant past its limit is refused; a 64-bit one is not
+    cfg = sg.binding.SgemmCfg()
+    cfg.id, cfg.group_m, cfg.xcd_remap = 4, 8, 1
+    assert lib_.sgemm_f32_cfg_geometry(0, 0, 64, 64, 64, 1 << 23, 64, 64, 1,
+                                       ctypes.byref(cfg)) == HIP_ERROR_INVALID_VALUE
+    cfg.id = min(ld64)
+    assert lib_.sgemm_f32_cfg_geometry(0, 0, 64, 64, 64, 1 << 23, 64, 64, 1,
+                                       ctypes.byref(cfg)) == 0
+    # past INT_MAX - 1024 still refused
+    assert sg.sgemm_f32(4, 4, 4, P, (1 << 31) - 1, 2 * P, 4, 3 * P, 4, 0) == HIP_ERROR_INVALID_VALUE
 
 
 def _gen(ta=0, tb=0, M=4, N=4, K=4, A=P, lda=None, sa=0, B=2 * P, ldb=None, sb=0,

@@ -164,3 +164,37 @@ def test_leading_dimension_limits_every_variant(ta, tb, which):
     del Ad, Bd
     _free()
 
+
+
+@pytest.mark.parametrize("case", [
+    # name,                               ta, tb,  M,   N,   K,             lda,        ldb
+    ("64x64xK lda 2^22+64 (packed A)",      0, 0,  64,  64, (1 << 22) + 64, None,      None),
+    ("1x1xK lda 2^22+64 (strips)",          0, 0,   1,   1, (1 << 22) + 64, None,      None),
+    ("300x200x8 ldb 2^25+4",                0, 0, 300, 200, 8,              None,      (1 << 25) + 4),
+    ("300x200x4 stored A^T lda 2^26",       1, 0, 300, 200, 4,              1 << 26,   None),
+    ("100x64x100 stored B^T ldb 2^23",      0, 1, 100,  64, 100,            None,      1 << 23),
+], ids=lambda c: c[0].split(" ")[0] + "_" + str(c[1]) + str(c[2]))
+def test_leading_dimensions_past_the_tiled_kernels(case):
+    """Leading dimensions past the LDS-tiled kernels' 32-bit in-slice offsets,
+    through the default plan (64-bit K-split tiles or strips), with and
+    without a workspace; inputs in [-1, 1] integers, so every sum is exact
+    (K < 2^24) and the result must equal the reference bit for bit."""
+    name, ta, tb, M, N, K, lda, ldb = case
+    seed = 500 + M + N
+    gen = np.random.default_rng(seed)
+    As = gen.integers(-1, 2, size=(K, M) if ta else (M, K)).astype(np.float32)
+    Bs = gen.integers(-1, 2, size=(N, K) if tb else (K, N)).astype(np.float32)
+    Ad = place(As, pad=0 if lda is None else lda - As.shape[1])
+    Bd = place(Bs, pad=0 if ldb is None else ldb - Bs.shape[1])
+    ref, absb = oracle.gemm_ref(As, Bs, ta, tb)
+    for workspace in (False, True):
+        note(f"large ld: {name} workspace={workspace} lda={Ad.stride(0)} ldb={Bd.stride(0)}")
+        C = torch.full((M, N), float("nan"), device="cuda")
+        sg.sgemm(Ad, Bd, out=C, transa=bool(ta), transb=bool(tb), workspace=workspace)
+        torch.cuda.synchronize()
+        got = C.cpu().numpy()
+        rep = oracle.compare(got, ref, absb)
+        assert rep["n_bad"] == 0, rep
+        assert np.array_equal(got.astype(np.float64), ref), rep
+    del Ad, Bd
+    _free()

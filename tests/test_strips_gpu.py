@@ -203,3 +203,27 @@ def test_ksplit_tiles_with_outer_splits_batches_and_strips(vid):
         ref, absb = oracle.gemm_ref_batched(As, Bs, ta, tb, -0.5, 1.25, C0)
         rep = oracle.compare(Cd.cpu().numpy(), ref, absb)
         assert rep["n_bad"] == 0, rep
+
+
+@pytest.mark.parametrize("ta,tb,M,N,K", [(0, 1, 4, 8192, 1000), (1, 1, 4, 8192, 1000),
+                                         (0, 1, 8192, 3, 1000), (0, 0, 8192, 3, 1001)])
+def test_wide_kc_strips_in_the_32_row_form(ta, tb, M, N, K):
+    """Strip-only products whose k-contiguous strip has 256 workgroups of 32
+    rows (as many as the CUs, so the launch keeps the 32-row form rather
+    than the 16-row one it takes for fewer): the row strip with B
+    transposed (NT, TT) and the column strip with A as stored (NT, NN)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    x = N if M <= 4 else M
+    if -(-x // 32) < cus:
+        pytest.skip(f"{cus} CUs: this strip would take the 16-row form")
+    As, Bs = inputs.make_operands(M, N, K, seed=380 + M + ta + 2 * tb)
+    As, Bs = stored(As, ta), stored(Bs, tb)
+    # the strips forced to be the whole product
+    cfg = with_strips(4, M, 0) if M <= 4 else with_strips(4, 0, N)
+    q = sg.sgemm_f32_cfg_geometry(cfg, ta, tb, M, N, K, As.shape[1], Bs.shape[1], N)
+    assert q.grid == 0, q.as_dict()
+    note(f"wide KC strip ta={ta} tb={tb} {M}x{N}x{K}")
+    C1 = run_general(As, Bs, ta, tb, cfg=cfg, workspace=False)
+    C2 = run_general(As, Bs, ta, tb, cfg=cfg, workspace=False)
+    assert np.array_equal(C1, C2)
+    check_general(C1, As, Bs, ta, tb)
