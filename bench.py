@@ -60,6 +60,9 @@ One JSON line is printed.  Besides the driver's fields it holds:
                 headline's fraction of it.
   valu_probe    the sustained non-packed v_fma_f32 rate on register operands
                 (the vector-ALU ceiling the comparison kernel is bound by).
+  launch_floor  an empty launch with the 512^3 plan's grid (256 workgroups of
+                512 threads), timed like the configurations: the part of a
+                small product's time that is not its work.
 """
 import argparse
 import hashlib
@@ -414,7 +417,7 @@ def vendor(torch, steps, warm_ms, peak):
     """torch.matmul (rocBLAS / hipBLASLt) in float32 on the same shapes, for context."""
     out = []
     torch.backends.cuda.matmul.allow_tf32 = False
-    for n in (8192, 3072):
+    for n in (8192, 3072, 4096, 2048, 512):
         A = torch.rand((n, n), device="cuda") * 2 - 1
         B = torch.rand((n, n), device="cuda") * 2 - 1
         C = torch.empty((n, n), device="cuda")
@@ -724,6 +727,15 @@ def main(argv=None):
         for e in result.get("extras", []):
             if e.get("kernel") == "valu_fma":
                 e["frac_of_valu_probe"] = round(e["value"] / vceil, 4)
+        # the floor of a launch with the small products' grid: 256 empty
+        # workgroups of 512 threads, timed like the configurations
+        t = time_calls(torch, probes.empty_launch(256), args.steps, args.extra_warm_ms,
+                       min_steps=100)
+        result["launch_floor"] = {
+            "mean_ms": round(t["mean_ms"], 5), **_timing_fields(t),
+            "what": "empty launch of 256 workgroups x 512 threads (the 512^3 grid), HIP "
+                    "events like configs: back-to-back mean and per-call distribution",
+        }
 
     if not args.no_cpu_baseline:
         C_host = r["C"].cpu().numpy()

@@ -7,6 +7,11 @@
 // sustains at its actual clock: FLOPs = iters * 8 * 4096 * waves.  Each thread
 // writes one float (a sum of its accumulators) so nothing is optimised away.
 //
+// sgemm_probe_empty: a launch that does nothing but write one float per
+// workgroup, with the grid of the small products (256 workgroups of 512
+// threads: the 512^3 plan), so its time is the floor any launch of that
+// shape pays (dispatch of the waves, completion) before doing work.
+//
 // sgemm_probe_valu_peak: every thread runs `iters` rounds of 16 independent
 // single-precision FMA chains (x = x * a + b) on registers, the vector-ALU
 // counterpart: FLOPs = iters * 16 * 2 * threads.  The library is built with
@@ -36,6 +41,11 @@ __global__ void __launch_bounds__(256) mfma_peak_kernel(int iters, float *out)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s += acc[j][r];
     out[(size_t)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+__global__ void __launch_bounds__(512) empty_kernel(float *out)
+{
+    if (threadIdx.x == 0) out[blockIdx.x] = (float)blockIdx.x;
 }
 
 __global__ void __launch_bounds__(256) valu_peak_kernel(int iters, float *out)
@@ -88,6 +98,16 @@ int sgemm_probe_valu_peak(int workgroups, int iters, float *out, hipStream_t str
 double sgemm_probe_valu_peak_flops(int workgroups, int iters)
 {
     return (double)workgroups * 256.0 * (double)iters * 16.0 * 2.0;
+}
+
+// The empty launch: `workgroups` workgroups of 512 threads; `out` must hold
+// `workgroups` floats of device memory.  Asynchronous on `stream`.
+int sgemm_probe_empty(int workgroups, float *out, hipStream_t stream)
+{
+    if (workgroups <= 0 || !out) return hipErrorInvalidValue;
+    void *args[] = {&out};
+    return hipLaunchKernel((const void *)&empty_kernel, dim3((unsigned)workgroups), dim3(512),
+                           args, 0, stream);
 }
 
 }  // extern "C"

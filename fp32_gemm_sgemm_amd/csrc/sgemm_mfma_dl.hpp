@@ -253,9 +253,15 @@ sgemm_mfma_dl_kernel(GemmArgs g)
         // the data goes through registers; 4-byte loads are masked one by one)
         const bool partial = !DW && (((a_lim & 3) && a_lim < (TA ? BM : BK)) ||
                                      ((b_lim & 3) && b_lim < (TB ? BK : BN)));
+        // One resource per operand serves both paths: with direct loads allowed
+        // every in-slice offset of data is below 2^31 (the leading-dimension
+        // limits of direct loads), so the extent can stop at kOobOffset,
+        // beyond which chunks past the data are sent; otherwise the register
+        // path needs the full extent.
+        const int64_t cap = g.direct ? (int64_t)kOobOffset : (int64_t)0xffffffff;
+        const auto ar = make_rsrc(abase, abytes < cap ? abytes : cap);
+        const auto br = make_rsrc(bbase, bbytes < cap ? bbytes : cap);
         if (g.direct && !partial) {
-            const auto ar = make_rsrc(abase, abytes < (int64_t)kOobOffset ? abytes : (int64_t)kOobOffset);
-            const auto br = make_rsrc(bbase, bbytes < (int64_t)kOobOffset ? bbytes : (int64_t)kOobOffset);
             // (the load size must be a literal: one call per size)
 #pragma unroll
             for (int j = 0; j < A_LOADS; ++j) {
@@ -274,8 +280,6 @@ sgemm_mfma_dl_kernel(GemmArgs g)
         } else {
             // One load's data at a time (loaded, masked, written to LDS), so
             // this rarely used path needs few staging registers.
-            const auto ar = make_rsrc(abase, abytes);
-            const auto br = make_rsrc(bbase, bbytes);
             auto put = [&](float *dst, const float (&v)[EL]) {
                 if constexpr (EL == 4) *reinterpret_cast<f32x4 *>(dst) = f32x4{v[0], v[1], v[2], v[3]};
                 else *dst = v[0];

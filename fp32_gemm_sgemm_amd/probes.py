@@ -25,6 +25,8 @@ def load():
         lib.sgemm_probe_valu_peak.restype = ctypes.c_int
         lib.sgemm_probe_valu_peak_flops.argtypes = [ctypes.c_int, ctypes.c_int]
         lib.sgemm_probe_valu_peak_flops.restype = ctypes.c_double
+        lib.sgemm_probe_empty.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        lib.sgemm_probe_empty.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -71,3 +73,20 @@ def valu_peak_tflops(workgroups_per_cu=16, iters=40000, reps=3):
     lib = load()
     return _best_tflops(lib.sgemm_probe_valu_peak, lib.sgemm_probe_valu_peak_flops,
                         _cus() * workgroups_per_cu, iters, reps)
+
+
+def empty_launch(workgroups=256):
+    """A launch of `workgroups` empty workgroups of 512 threads (the grid of
+    the 512^3 plan): returns a callable that enqueues it on the current
+    stream, for timing the floor of such a launch."""
+    import torch
+    lib = load()
+    out = torch.empty(workgroups, dtype=torch.float32, device="cuda")
+
+    def launch():
+        rc = lib.sgemm_probe_empty(workgroups, out.data_ptr(),
+                                   torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"probe launch failed with hipError_t {rc}")
+    launch.out = out
+    return launch
