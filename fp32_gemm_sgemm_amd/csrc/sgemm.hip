@@ -106,7 +106,8 @@ constexpr int kCrossSliceAgpr = 6;
 // (32 BM x 32 BN), over one round, one workgroup per CU (16 BM x 16 BN), and
 // with rows that are not 16-byte aligned (32 BM - 5 x 32 BN - 5, K = 4099).
 // `python -m fp32_gemm_sgemm_amd.calibrate` measures them; the figures below
-// come from such runs on MI355X (each family of related tiles from one run),
+// come from such runs on MI355X (each family of related tiles from one run:
+// the 64x64 tiles together, the 4-byte-load tiles of 128x128 and up together),
 // with the launch floor every launch pays taken off each time.  The K-split 32x32 tiles carry four more numbers:
 // their fixed cost per tile in ns; the factors (x1000) by which a slice slows
 // once the operand rows and columns one XCD's tiles read exceed its L2, over
@@ -129,15 +130,16 @@ const Variant kVariants[] = {
     dl_variant<128, 128, 32, 4, 2, 2, kAllOps, false, kCrossSliceAgpr>(925, 928, 661),  // 7: direct loads, 8 waves of 32x64
     mfma_variant<128, 128, 16, 2, 4, 0>(827, 825, 671),    // 8: 8 waves of 64x32
     mfma_variant<128, 128, 32, 2, 4, 1>(817, 790, 743),    // 9: 8 waves of 64x32, BK 32
-    dl_variant<192, 192, 32, 2, 6, 2, kAllOps, true, kCrossSliceAgpr>(944, 936, 941),  // 10: 4-byte direct loads
+    dl_variant<192, 192, 32, 2, 6, 2, kAllOps, true, kCrossSliceAgpr>(946, 910, 942),  // 10: 4-byte direct loads
     dl_variant<64, 64, 32, 2, 2, 2, kAllOps, false, kCrossSliceAgpr>(895, 662, 509, 3329),  // 11: direct loads, 4 waves of 32x32
     dl_variant<64, 64, 32, 2, 2, 2, kAllOps, true, kCrossSliceAgpr>(903, 651, 897, 3874),  // 12: 4-byte direct loads
-    dl_variant<128, 128, 32, 4, 2, 2, kAllOps, true, kCrossSliceAgpr>(926, 903, 922),  // 13: 4-byte direct loads, 8 waves of 32x64
+    dl_variant<128, 128, 32, 4, 2, 2, kAllOps, true, kCrossSliceAgpr>(923, 888, 915),  // 13: 4-byte direct loads, 8 waves of 32x64
     sk_variant<4>(500, 576, 424, 3204, 1054, 990, 8),      // 14: 32x32, K split over 4 waves
     sk_variant<16>(681, 572, 581, 3242, 1045, 1179, 1),    // 15: 32x32, K split over 16 waves
     sk_variant<8>(608, 623, 507, 3207, 1053, 1085, 3),     // 16: 32x32, K split over 8 waves
     dl_variant<64, 64, 64, 2, 2, 2, kAllOps, false, kCrossSliceAgpr>(893, 765, 336, 4108),  // 17: direct loads, 64-deep slices
     dl_variant<64, 64, 64, 2, 2, 2, kAllOps, true, kCrossSliceAgpr>(863, 706, 855, 4808),  // 18: 4-byte direct loads, 64-deep slices
+    dl_variant<256, 256, 16, 4, 2, 2, kAllOps, true, kCrossSliceAgpr>(932, 955, 927),  // 19: 4-byte direct loads, 16-deep slices
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
