@@ -8,11 +8,15 @@ torch is imported before the library is loaded so that the library binds to
 the HIP runtime torch already loaded (both carry the soname libamdhip64.so.7):
 streams and device pointers from torch are then valid in the library.
 """
+import contextlib
 import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsgemm.so")
+# The LDS race check build of the same sources (LDS words set to NaN before
+# each refill); only tests route calls to it, through library().
+POISON_LIB_PATH = os.path.join(HERE, "libsgemm_lds_poison.so")
 
 SGEMM_KERNEL_MFMA = 0
 SGEMM_KERNEL_VALU = 1
@@ -40,22 +44,38 @@ class SgemmCfg(ctypes.Structure):
         return {n: getattr(self, n) for n, _ in self._fields_}
 
 
-_lib = None
+_libs = {}      # loaded builds by path
+_active = None  # path calls go to while library() is in effect (None: LIB_PATH)
 
 
-def load():
-    """Load libsgemm.so once; raise if it is not built."""
-    global _lib
-    if _lib is not None:
-        return _lib
+@contextlib.contextmanager
+def library(path):
+    """Route every call of this module to another build of the library (such
+    as POISON_LIB_PATH) until the block ends.  Not thread-safe: meant for
+    tests."""
+    global _active
+    load(path)
+    prev, _active = _active, path
+    try:
+        yield
+    finally:
+        _active = prev
+
+
+def load(path=None):
+    """Load a build of the library once (by default libsgemm.so, or the one
+    library() selected); raise if it is not built."""
+    path = path or _active or LIB_PATH
+    if path in _libs:
+        return _libs[path]
     try:
         import torch  # noqa: F401  (binds the shared HIP runtime first)
     except ImportError:  # pragma: no cover
         pass
-    if not os.path.exists(LIB_PATH):
+    if not os.path.exists(path):
         raise RuntimeError(
-            f"{LIB_PATH} is not built: run `python -m fp32_gemm_sgemm_amd.build` first")
-    lib = ctypes.CDLL(LIB_PATH)
+            f"{path} is not built: run `python -m fp32_gemm_sgemm_amd.build` first")
+    lib = ctypes.CDLL(path)
     i, p, f = ctypes.c_int, ctypes.c_void_p, ctypes.c_float
     ll, sz = ctypes.c_longlong, ctypes.c_size_t
     cfgp = ctypes.POINTER(SgemmCfg)
@@ -79,7 +99,7 @@ def load():
         fn.restype = i
     lib.sgemm_f32_version.argtypes = []
     lib.sgemm_f32_version.restype = ctypes.c_char_p
-    _lib = lib
+    _libs[path] = lib
     return lib
 
 

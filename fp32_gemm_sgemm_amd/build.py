@@ -5,6 +5,11 @@
 Always recompiles.  All device code is built with packed-FP32 instruction
 selection switched off (-target-feature -packed-fp32-ops); the host pass
 warns that it does not know that feature, which is harmless.
+
+Besides the product library it builds the measurement probes
+(libsgemm_probes.so) and the LDS race check build of the same sources
+(libsgemm_lds_poison.so, SGEMM_LDS_POISON=1: LDS words are set to NaN before
+each refill), which only the tests load.  The three compile in parallel.
 """
 import argparse
 import os
@@ -17,6 +22,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsgemm.so")
 PROBES_LIB = os.path.join(HERE, "libsgemm_probes.so")
+POISON_LIB = os.path.join(HERE, "libsgemm_lds_poison.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -31,6 +37,7 @@ FLAGS = [
 
 
 def _hipcc(out, sources, save_temps=None, verbose=False, extra=()):
+    """Start one compilation; returns (process, output path)."""
     cmd = [HIPCC, *FLAGS, *extra]
     if save_temps:
         os.makedirs(save_temps, exist_ok=True)
@@ -38,16 +45,27 @@ def _hipcc(out, sources, save_temps=None, verbose=False, extra=()):
     cmd += ["-o", out + ".tmp", *sources]
     if verbose:
         print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True, cwd=save_temps or HERE)
-    os.replace(out + ".tmp", out)
-    return out
+    return subprocess.Popen(cmd, cwd=save_temps or HERE), out
 
 
 def build(save_temps: str = None, verbose: bool = False, extra=()) -> str:
-    """Compile libsgemm.so (the product) and libsgemm_probes.so (measurement
-    probes); returns the product library's path."""
-    _hipcc(LIB, SOURCES, save_temps, verbose, extra)
-    _hipcc(PROBES_LIB, PROBE_SOURCES, save_temps, verbose, extra)
+    """Compile libsgemm.so (the product), libsgemm_probes.so (measurement
+    probes) and libsgemm_lds_poison.so (the LDS race check build); returns
+    the product library's path.  With save_temps, only the product library is
+    built (its intermediate files go there)."""
+    jobs = [_hipcc(LIB, SOURCES, save_temps, verbose, extra)]
+    if not save_temps:
+        jobs.append(_hipcc(PROBES_LIB, PROBE_SOURCES, None, verbose, extra))
+        jobs.append(_hipcc(POISON_LIB, SOURCES, None, verbose,
+                           ("-DSGEMM_LDS_POISON=1", *extra)))
+    failed = []
+    for proc, out in jobs:
+        if proc.wait() != 0:
+            failed.append(out)
+        else:
+            os.replace(out + ".tmp", out)
+    if failed:
+        raise subprocess.CalledProcessError(1, "hipcc", f"failed to build {failed}")
     return LIB
 
 

@@ -134,6 +134,35 @@ __device__ __forceinline__ void store_row(float *p, int col, int N, const float 
         if (col + j < N) p[j] = beta != 0.0f ? alpha * v[j] + beta * p[j] : alpha * v[j];
 }
 
+// LDS race check.  A build with SGEMM_LDS_POISON=1 sets every LDS word to a
+// quiet NaN before it is refilled, from the moment the words are free (the
+// barrier after their last reads) or just before their fill is issued, and
+// waits for those writes before the fill.  A read that comes too early (the
+// fill has not landed) or too late (the words were already released) then
+// returns NaN, which spreads into the results; bitwise equality with the
+// normal build shows that no read of the parity cases raced.  The normal
+// build (SGEMM_LDS_POISON=0) compiles none of it.
+#ifndef SGEMM_LDS_POISON
+#define SGEMM_LDS_POISON 0
+#endif
+constexpr bool kLdsPoison = SGEMM_LDS_POISON != 0;
+
+// Writes a quiet NaN to n consecutive LDS floats at p.
+__device__ __forceinline__ void lds_poison(float *p, int n)
+{
+    for (int i = 0; i < n; ++i) p[i] = __builtin_nanf("");
+}
+
+// Waits for this thread's LDS writes (the poison) to complete, so that a fill
+// issued afterwards (a direct load whose data reaches LDS later) lands on top
+// of them, and keeps the compiler from moving LDS accesses across.
+__device__ __forceinline__ void lds_poison_done()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));  // lgkmcnt(0), other counters free
+    asm volatile("" ::: "memory");
+}
+
 // A raw buffer resource over [base, base + bytes): loads at or past its end
 // return zero and never fault.  bytes <= 0 gives an empty resource; sizes
 // above 4 GiB - 1 are clamped (offsets used with a resource stay below that).

@@ -186,6 +186,24 @@ sgemm_mfma_kernel(GemmArgs g)
         }
     };
 
+    // LDS race check build: this thread's words of buffer `buf` (those sstore
+    // writes) set to NaN once the buffer is free.
+    auto poison = [&](int buf) {
+        if constexpr (kLdsPoison) {
+#pragma unroll
+            for (int v = 0; v < A_VECS; ++v) {
+                const int idx = tid + v * NT;
+                lds_poison(&As[buf][(idx / A_ROW_VECS) * LDA_S + 4 * (idx % A_ROW_VECS)], 4);
+            }
+#pragma unroll
+            for (int v = 0; v < B_VECS; ++v) {
+                const int idx = tid + v * NT;
+                lds_poison(&Bs[buf][(idx / B_ROW_VECS) * LDB_S + 4 * (idx % B_ROW_VECS)], 4);
+            }
+            lds_poison_done();
+        }
+    };
+
     // ---- LDS -> fragments -> MFMA ---------------------------------------------
     // Fragments of one 8-deep k group: RM float4 of A (4 k values of one row
     // per lane) and 4 NB-wide reads of B (one k row each).
@@ -236,6 +254,8 @@ sgemm_mfma_kernel(GemmArgs g)
     const int nk = (nk_real + 1) & ~1;
     auto slice = [&](int kt, auto &ra_next, auto &rb_next, auto &ra_free, auto &rb_free) {
         const int cur = kt & 1;
+        // (buffer cur ^ 1 was last read in slice kt-1, which every wave has left)
+        if (kt + 1 < nk) poison(cur ^ 1);
         if (kt + 2 < nk) gload(kt + 2, ra_free, rb_free);
         Frag f[2];
         read_frag(cur, 0, f[0]);

@@ -235,11 +235,26 @@ sgemm_mfma_dl_kernel(GemmArgs g)
     // host, which would silently drop this kernel's host-side stub.
     typedef __attribute__((address_space(3))) void lds_void;
 
+    // LDS race check build: this thread's share of stage s (the words its
+    // fetch fills) is set to NaN before the fill is issued.
+    auto poison_stage = [&](int s) {
+        if constexpr (kLdsPoison) {
+#pragma unroll
+            for (int j = 0; j < A_LOADS; ++j)
+                lds_poison(smem + s * STAGE_FLOATS + ((j * NW + wave) * 64 + lane) * EL, EL);
+#pragma unroll
+            for (int j = 0; j < B_LOADS; ++j)
+                lds_poison(smem + s * STAGE_FLOATS + A_FLOATS + ((j * NW + wave) * 64 + lane) * EL, EL);
+            lds_poison_done();
+        }
+    };
+
     // Fetch slice kt into stage s.  Per operand: the slice's base (its first
     // index at k0), the resource extent up to the operand's last element, and
     // the limit of the contiguous column (k for KC, the index for XC) below
     // which a chunk holds data.
     auto fetch = [&](int kt, int s) {
+        poison_stage(s);
         const int k0 = kt * BK;
         const float *abase = TA ? A + (int64_t)k0 * lda + m0 : A + (int64_t)m0 * lda + k0;
         const float *bbase = TB ? B + (int64_t)n0 * ldb + k0 : B + (int64_t)k0 * ldb + n0;
@@ -313,6 +328,7 @@ sgemm_mfma_dl_kernel(GemmArgs g)
     // throughout, with the tile's fixed offsets (full_slice_off): one
     // resource per operand, no checks, nothing that needs a branch.
     auto fetch_full = [&](int kt, int s, const uint32_t (&af)[A_LOADS], const uint32_t (&bf)[B_LOADS]) {
+        poison_stage(s);
         const int k0 = kt * BK;
         const float *abase = TA ? A + (int64_t)k0 * lda + m0 : A + (int64_t)m0 * lda + k0;
         const float *bbase = TB ? B + (int64_t)n0 * ldb + k0 : B + (int64_t)k0 * ldb + n0;

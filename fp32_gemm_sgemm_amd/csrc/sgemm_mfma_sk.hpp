@@ -46,6 +46,15 @@ __global__ void __launch_bounds__(W * 64) sgemm_mfma_sk_kernel(GemmArgs g)
     constexpr int D = T::DEPTH;
     __shared__ __attribute__((aligned(16))) float red[T::LDS_FLOATS];
 
+    if constexpr (kLdsPoison) {
+        // LDS race check build: the partial-tile area starts as NaN everywhere
+        const int w0 = threadIdx.x >> 6, l0 = threadIdx.x & 63;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) lds_poison(&red[(w0 * 16 + r) * 64 + l0], 1);
+        lds_poison_done();
+        __syncthreads();
+    }
+
     const Work wk = map_work(g);
     locate<TA, TB>(g, wk);
     const float *__restrict__ A = g.A;

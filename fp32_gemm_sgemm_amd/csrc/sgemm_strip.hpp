@@ -126,8 +126,21 @@ __device__ __forceinline__ void strip_block(const Strip &s, int wg, int K, int z
         rows[i] = big + (int64_t)x * s.ld_big;
     }
 
+    // LDS race check build: this thread's slots of the stage set to NaN (the
+    // stage is free here: before the first chunk, or after a chunk's barrier)
+    auto poison_slots = [&]() {
+        if constexpr (kLdsPoison) {
+            for (int slot = tid; slot < kStripKChunk; slot += kStripThreads) {
+                constexpr int Q = kStripKChunk / 4;
+                lds_poison(reinterpret_cast<float *>(&stage[(slot / Q) * kStripPlane + slot % Q]), 4);
+            }
+            lds_poison_done();
+        }
+    };
+
     for (int c0 = 0; c0 < K; c0 += kStripKChunk) {
         const int clen = min(K - c0, kStripKChunk);
+        poison_slots();
         for (int slot = tid; slot < kStripKChunk; slot += kStripThreads) {
             constexpr int Q = kStripKChunk / 4;
             const int k = 4 * (slot % Q) + slot / Q;
@@ -210,6 +223,10 @@ __device__ __forceinline__ void strip_block(const Strip &s, int wg, int K, int z
     // chunk's barrier).
     float *red = reinterpret_cast<float *>(stage);
     float *__restrict__ out = s.out + z * s.batch_out;
+    if constexpr (kLdsPoison) {
+        poison_slots();
+        __syncthreads();
+    }
     if constexpr (KC) {
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1)

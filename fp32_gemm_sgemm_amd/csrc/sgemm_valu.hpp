@@ -107,6 +107,15 @@ sgemm_valu_kernel(GemmArgs g)
         __syncthreads();
         for (int kt = 0; kt < nk; ++kt) {
             const int cur = kt & 1;
+            if constexpr (kLdsPoison) {
+                // LDS race check build: this thread's words of the free buffer
+                if (kt + 1 < nk) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) lds_poison(&As[cur ^ 1][(a_col + e) * LDA_S + a_row], 1);
+                    lds_poison(&Bs[cur ^ 1][b_row * LDB_S + b_col], 4);
+                    lds_poison_done();
+                }
+            }
             if (kt + 1 < nk) gload(kt + 1);
             compute(cur);
             if (kt + 1 < nk) sstore(cur ^ 1);

@@ -36,13 +36,28 @@ def test_header_declares_expected_entry_points():
     assert len(names) >= 7
 
 
-def test_every_declared_symbol_is_exported(lib):
-    out = subprocess.run(["nm", "-D", "--defined-only", sg.LIB_PATH],
+@pytest.mark.parametrize("path", [sg.LIB_PATH, sg.POISON_LIB_PATH],
+                         ids=["product", "lds_poison"])
+def test_every_declared_symbol_is_exported(lib, path):
+    """The product library and its LDS race check build export every entry
+    point the header declares."""
+    out = subprocess.run(["nm", "-D", "--defined-only", path],
                          capture_output=True, text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    handle = sg.load(path)
     for name in declared_functions():
         assert name in exported, name
-        assert hasattr(lib, name)
+        assert hasattr(handle, name)
+
+
+def test_library_switch_routes_calls():
+    """library() sends calls to the other build and restores the default."""
+    from fp32_gemm_sgemm_amd import binding
+    assert binding.load() is binding.load(sg.LIB_PATH)
+    with sg.library(sg.POISON_LIB_PATH):
+        assert binding.load() is binding.load(sg.POISON_LIB_PATH)
+        assert sg.sgemm_f32_num_variants() == binding.load(sg.LIB_PATH).sgemm_f32_num_variants()
+    assert binding.load() is binding.load(sg.LIB_PATH)
 
 
 def test_scratch_size_matches_header(lib):
