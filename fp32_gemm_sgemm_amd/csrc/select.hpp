@@ -44,6 +44,7 @@ struct Variant {
                                  // rows and columns the tiles of one XCD read exceed its
                                  // L2, over one round (0: not modelled)
     int spill_full_permille;     // the same over several rounds, where every CU streams
+                                 // (0: not modelled)
     int coresident;              // workgroups that share a CU and overlap their fixed
                                  // costs (0: one, the fixed cost is paid every round)
     int ld64;                    // addresses its operands in 64 bits throughout: any
@@ -235,22 +236,53 @@ constexpr double kCuFlopPerNs = 157.3e3 / 256.0;
 constexpr double kReduceFixedNs = 7500.0;
 constexpr double kReduceBytesPerNs = 5000.0;
 
-// L2 per XCD, and the XCDs of the chip.
+// L2 per XCD, and the XCDs of the chip.  Operands count as held in L2 up to
+// 15/16 of it (the rest holds C and whatever else passes through): a round of
+// 64 x 64 tiles slows past 3.8-3.9 MiB of operand rows and columns per XCD
+// (1024 x 1024 x K, K = 1280 to 1344, measured on MI355X).
 constexpr double kL2Bytes = 4.0 * 1024 * 1024;
+constexpr double kL2OperandBytes = kL2Bytes * 15.0 / 16.0;
 constexpr int kXcds = 8;
 
 // Bytes of op(A) rows and op(B) columns, over kc values of k, that the tiles
-// one XCD holds at once read: the tile order hands each XCD a run of
-// consecutive tiles, which with groups of kDefaultGroupM tile rows is a block
-// of up to that many tile rows by as many tile columns as the run needs.
-inline double xcd_operand_bytes(const Variant &v, long long tiles, int tiles_m, int kc, int cus)
+// one XCD runs in the first round read, for the XCD that reads the most.  It
+// follows the launch order of the kernels (common.hpp xcd_order and work_of,
+// with groups of kDefaultGroupM tile rows): each XCD takes a contiguous run of
+// logical tile ids, which walks a group of tile rows column by column, and a
+// run that crosses into the next group (or the next K split or batch entry,
+// whose operands differ) reads the rows and columns of both.
+inline double xcd_operand_bytes(const Variant &v, long long tiles_m, long long tiles_n,
+                                long long grid, int kc, int cus)
 {
-    const long long per_xcd = ceil_div_ll(tiles < cus ? tiles : cus, kXcds);
-    long long r = tiles_m < kDefaultGroupM ? tiles_m : kDefaultGroupM;
-    if (r > per_xcd) r = per_xcd;
-    if (r < 1) r = 1;
-    const long long c = ceil_div_ll(per_xcd, r);
-    return 4.0 * kc * (double)(r * v.bm + c * v.bn);
+    const long long mn = tiles_m * tiles_n;
+    const long long per_group = kDefaultGroupM * tiles_n;
+    const long long q = grid / kXcds, r = grid % kXcds;
+    const long long first_round = grid < cus ? grid : cus;
+    double worst = 0.0;
+    for (int x = 0; x < kXcds; ++x) {
+        // hardware workgroups x, x + 8, ... of the first round; their logical
+        // ids start at the XCD's block
+        const long long n = first_round > x ? (first_round - 1 - x) / kXcds + 1 : 0;
+        long long pos = x * q + (x < r ? x : r);
+        const long long end = pos + n;
+        long long rows = 0, cols = 0;
+        while (pos < end) {
+            const long long t = pos % mn;  // tile within its (split, batch) block
+            const long long grp = t / per_group;
+            const long long g_rows = tiles_m - grp * kDefaultGroupM < kDefaultGroupM
+                                         ? tiles_m - grp * kDefaultGroupM
+                                         : kDefaultGroupM;
+            const long long a = t - grp * per_group;  // first index inside the group
+            long long b = a + (end - pos);             // one past the last, capped at the group
+            if (b > g_rows * tiles_n) b = g_rows * tiles_n;
+            rows += b - a < g_rows ? b - a : g_rows;
+            cols += (b - 1) / g_rows - a / g_rows + 1;
+            pos += b - a;
+        }
+        const double bytes = 4.0 * kc * (double)(rows * v.bm + cols * v.bn);
+        if (bytes > worst) worst = bytes;
+    }
+    return worst;
 }
 
 // eff: the variant's fraction of peak (x1000) for this call's alignment.
@@ -265,9 +297,10 @@ inline double estimate_ns(const Variant &v, const Problem &p, int splits, int k_
     double e = eff;
     if (tiles <= cus) e = e * v.eff_one_permille / v.eff_permille;
     double slice_ns = 2.0 * v.bm * v.bn * v.bk / (kCuFlopPerNs * e / 1000.0);
-    if (v.spill_permille > 0 &&
-        xcd_operand_bytes(v, tiles, (int)ceil_div_ll(p.M, v.bm), kc, cus) > kL2Bytes)
-        slice_ns = slice_ns * (tiles <= cus ? v.spill_permille : v.spill_full_permille) / 1000.0;
+    const int spill = tiles <= cus ? v.spill_permille : v.spill_full_permille;
+    if (spill > 0 && xcd_operand_bytes(v, ceil_div_ll(p.M, v.bm), ceil_div_ll(p.N, v.bn), tiles, kc,
+                                       cus) > kL2OperandBytes)
+        slice_ns = slice_ns * spill / 1000.0;
     const double fixed = v.fixed_ns > 0 ? (double)v.fixed_ns : kTileFixedNs;
     // co-resident workgroups pay their fixed costs together, once per wave of
     // cus * coresident tiles, and share the CU's matrix cores for the slices
