@@ -22,12 +22,9 @@ and the cost model of select.hpp,
 is inverted for eff (x1000), the three numbers each variant carries in the
 table of sgemm.hip (printed at the end as table lines).  With --fit-fixed the
 listed variants get their own fixed cost in place of the 2.5 us (fit_fixed),
-a fourth number in their table line.  With --one-round-spill the listed variants
-get their one-round rate measured with the operands one XCD reads held in its
-L2, their own fixed cost, and a one-round spill factor for K past that
-(calibrate_one_round_spill): a fourth and fifth number.  The variants that
-split K over their waves (32 x 32
-tiles, whose L2 spill the model prices) also get their own fixed cost and
+a fourth number in their table line.  The variants that split K over their
+waves (32 x 32 tiles, whose L2 spill the model prices) also get their own
+fixed cost and
 spill factors (one round, several rounds), and are measured at K where the
 operands one XCD reads fit in its L2 (calibrate_ksplit); several of their
 workgroups share a CU, and the model charges their fixed cost once per wave
@@ -154,10 +151,12 @@ def _record(vid, v, name, M, N, K, t, e):
 
 def fit_fixed(torch, sg, vid, warm_ms, floor):
     """Fixed cost per tile (ns) of a variant whose pipeline fill differs from
-    the common 2.5 us: its one-round shape (16 BM x 16 BN) two slices deep
-    and at K = 2048, the line through them taken back to K = 0."""
+    the common 2.5 us: its one-round shape (16 BM x 16 BN) as many slices deep
+    as it has LDS stages (at least two: the pipeline full) and at K = 2048,
+    the line through them taken back to K = 0."""
     v = sg.sgemm_f32_variant(vid)
-    M1, N1, k1 = 16 * v.bm, 16 * v.bn, 2 * v.bk
+    stages = max(2, round(v.lds_bytes / (4.0 * (v.bm + v.bn) * v.bk)))
+    M1, N1, k1 = 16 * v.bm, 16 * v.bn, stages * v.bk
     t1 = _forced(torch, sg, vid, M1, N1, k1, warm_ms)
     t2 = _forced(torch, sg, vid, M1, N1, 2048, warm_ms)
     fixed = max(t1 - (t2 - t1) / (2048.0 - k1) * k1 - floor, 0.0)
@@ -183,45 +182,6 @@ def calibrate_variant(torch, sg, vid, warm_ms, floor, fixed=TILE_FIXED_NS):
         out[name] = round(e)
         _record(vid, v, name, M, N, K, t, e)
     return out
-
-
-def resident_k(bm, bn):
-    """Largest power-of-two K at which the operand rows and columns that one
-    XCD's tiles read in a full round (32 tiles, 8 tile rows by 4 columns, the
-    default tile order) take at most 3 MiB of its 4 MiB L2."""
-    per_k = 4 * (8 * bm + 4 * bn)
-    k = 1
-    while 2 * k * per_k <= 3 * 1024 * 1024:
-        k *= 2
-    return k
-
-
-def calibrate_one_round_spill(torch, sg, vid, warm_ms, floor):
-    """A tile variant whose one-round rate depends on whether the operands one
-    XCD reads fit in its L2 (the 64 x 64 tiles: a round of them streams the
-    operands at K = 4096, and their short slices do not hide it):
-
-    - its fixed cost and one-round rate from its one-round shape (16 BM x 16
-      BN) one slice deep and at the largest K where those operands stay in
-      L2 (resident_k);
-    - its one-round spill factor from the same shape at K = 4096.
-    The rates over four rounds and on unaligned rows stay those of
-    calibrate_variant (the model applies this spill factor to one round only)."""
-    v = sg.sgemm_f32_variant(vid)
-    bm, bn, bk = v.bm, v.bn, v.bk
-    M1, N1 = 16 * bm, 16 * bn
-    kr = resident_k(bm, bn)
-    t1 = _forced(torch, sg, vid, M1, N1, bk, warm_ms)
-    tr = _forced(torch, sg, vid, M1, N1, kr, warm_ms)
-    fixed = max(t1 - (tr - t1) / (kr - bk) * bk - floor, 0.0)
-    e_one = eff_from_time(tr - floor, bm, bn, bk, M1, N1, kr, fixed)
-    _record(vid, v, "one (resident)", M1, N1, kr, tr, e_one)
-    t4k = _forced(torch, sg, vid, M1, N1, 4096, warm_ms)
-    spill = (t4k - floor - fixed) / (-(-4096 // bk) * slice_ns(bm, bn, bk, e_one))
-    print(json.dumps({"variant": vid, "shape": "one-round spill", "M": M1, "N": N1, "K": [bk, kr, 4096],
-                      "us": [round(t1 / 1e3, 2), round(tr / 1e3, 2), round(t4k / 1e3, 2)],
-                      "fixed_ns": round(fixed), "spill_permille": round(1000.0 * spill)}), flush=True)
-    return {"one": round(e_one), "fixed": round(fixed), "spill": round(1000.0 * spill)}
 
 
 def calibrate_ksplit(torch, sg, vid, warm_ms, floor):
@@ -339,10 +299,7 @@ def main(argv=None):
     ap.add_argument("--fit-fixed", default="",
                     help="comma-separated tile variants whose fixed cost is fitted instead "
                          "of taken as 2.5 us")
-    ap.add_argument("--one-round-spill", default="",
-                    help="comma-separated tile variants whose one-round rate is measured "
-                         "with the operands in L2, with a one-round spill factor (the 64 x 64 "
-                         "tiles)")
+
     args = ap.parse_args(argv)
     import torch
     import fp32_gemm_sgemm_amd as sg
@@ -357,15 +314,9 @@ def main(argv=None):
         vids = [i for i in range(sg.sgemm_f32_num_variants()) if _is_mfma(sg, i)]
     floor = launch_floor(torch, sg, args.ms) if vids else 0.0
     fit = {int(x) for x in args.fit_fixed.split(",") if x}
-    ors = {int(x) for x in args.one_round_spill.split(",") if x}
     table = {}
     for vid in vids:
-        if vid in ors:
-            table[vid] = calibrate_variant(torch, sg, vid, args.ms, floor)
-            r = calibrate_one_round_spill(torch, sg, vid, args.ms, floor)
-            table[vid]["one"] = r["one"]
-            table[vid]["ors"] = r
-        elif sg.sgemm_f32_variant(vid).spill_full_permille > 0:
+        if sg.sgemm_f32_variant(vid).spill_full_permille > 0:
             table[vid] = calibrate_ksplit(torch, sg, vid, args.ms, floor)
         elif vid in fit:
             fixed = fit_fixed(torch, sg, vid, args.ms, floor)
@@ -378,8 +329,6 @@ def main(argv=None):
         extra = f", {e['fixed']}, {e['spill']}, {e['spill_full']}, {co}" if "spill" in e else ""
         if "fit" in e:
             extra = f", {e['fit']}"
-        if "ors" in e:
-            extra = f", {e['ors']['fixed']}, {e['ors']['spill']}"
         print(f"variant {vid}: ({e['full']}, {e['one']}, {e['unaligned']}{extra})", flush=True)
     if not args.no_strips:
         st = calibrate_strips(torch, sg, args.ms)

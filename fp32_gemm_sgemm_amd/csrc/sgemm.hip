@@ -46,13 +46,13 @@ Variant mfma_variant(int eff_permille, int eff_one_permille, int eff_unaligned_p
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int OPS, bool DW = false,
           int PIPE = 0>
 Variant dl_variant(int eff_permille, int eff_one_permille, int eff_unaligned_permille,
-                   int fixed_ns = 0, int spill_permille = 0)
+                   int fixed_ns = 0)
 {
     typedef sgemm::DlTraits<BM, BN, BK, WM, WN, STAGES, false, false, DW> T;
     Variant v{SGEMM_KERNEL_MFMA, BM, BN, BK, WM, WN, -1, STAGES, DW ? 1 : 0,
               T::NT, (int)(T::LDS_FLOATS * sizeof(float)),
               {nullptr, nullptr, nullptr, nullptr}, eff_permille, eff_one_permille,
-              eff_unaligned_permille, fixed_ns, spill_permille, 0, 0};
+              eff_unaligned_permille, fixed_ns, 0, 0, 0};
     v.fn[0] = reinterpret_cast<const void *>(
         &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, false, false, DW, PIPE>);
     if constexpr ((OPS & 2) != 0)
@@ -116,12 +116,12 @@ constexpr int kCrossSliceAgpr = 6;
 // and 72 per lane for W = 4, 8, 16 in the NN layout, so 8, 3 and 1), whose
 // fixed costs overlap.  The others use the model's common 2.5 us, no spill
 // term and one fixed cost per round.
-// The 64x64 tiles carry their own fixed cost (--fit-fixed), and the 32-deep
-// ones a one-round spill factor as well: their one-round figure is measured
-// with the operands one XCD's tiles read held in its L2 (K = 1024), and a
-// round at K = 4096, where those operands stream from beyond L2, is slower by
-// that factor (x1000; --one-round-spill).  The 64-deep ones hide that
-// streaming (factor about 1) and are not modelled.
+// The 64x64 tiles carry their own fixed cost (--fit-fixed).  The two-stage
+// 32-deep ones are rated over one round at K = 4096, where the operands one
+// XCD's tiles read stream from beyond its L2: with fewer K they run faster only
+// when the same operands are still in L2 from the call before, so the
+// four-stage ones (20, 21), which keep their rate either way, are the one-round
+// choice.
 // The 4-byte direct-load variants serve only rows that are not 16-byte
 // aligned.  The vector-FMA comparison kernel carries no figures: the selector
 // never picks it.
@@ -137,8 +137,8 @@ const Variant kVariants[] = {
     mfma_variant<128, 128, 16, 2, 4, 0>(827, 825, 671),    // 8: 8 waves of 64x32
     mfma_variant<128, 128, 32, 2, 4, 1>(817, 790, 743),    // 9: 8 waves of 64x32, BK 32
     dl_variant<192, 192, 32, 2, 6, 2, kAllOps, true, kCrossSliceAgpr>(946, 910, 942),  // 10: 4-byte direct loads
-    dl_variant<64, 64, 32, 2, 2, 2, kAllOps, false, kCrossSliceAgpr>(895, 810, 509, 3329, 1225),  // 11: direct loads, 4 waves of 32x32
-    dl_variant<64, 64, 32, 2, 2, 2, kAllOps, true, kCrossSliceAgpr>(903, 693, 897, 3874, 1056),  // 12: 4-byte direct loads
+    dl_variant<64, 64, 32, 2, 2, 2, kAllOps, false, kCrossSliceAgpr>(895, 662, 509, 3329),  // 11: direct loads, 4 waves of 32x32
+    dl_variant<64, 64, 32, 2, 2, 2, kAllOps, true, kCrossSliceAgpr>(903, 651, 897, 3874),  // 12: 4-byte direct loads
     dl_variant<128, 128, 32, 4, 2, 2, kAllOps, true, kCrossSliceAgpr>(923, 888, 915),  // 13: 4-byte direct loads, 8 waves of 32x64
     sk_variant<4>(500, 576, 424, 3204, 1054, 990, 8),      // 14: 32x32, K split over 4 waves
     sk_variant<16>(681, 572, 581, 3242, 1045, 1179, 1),    // 15: 32x32, K split over 16 waves
@@ -146,6 +146,8 @@ const Variant kVariants[] = {
     dl_variant<64, 64, 64, 2, 2, 2, kAllOps, false, kCrossSliceAgpr>(893, 765, 336, 4108),  // 17: direct loads, 64-deep slices
     dl_variant<64, 64, 64, 2, 2, 2, kAllOps, true, kCrossSliceAgpr>(863, 706, 855, 4808),  // 18: 4-byte direct loads, 64-deep slices
     dl_variant<256, 256, 16, 4, 2, 2, kAllOps, true, kCrossSliceAgpr>(932, 955, 927),  // 19: 4-byte direct loads, 16-deep slices
+    dl_variant<64, 64, 32, 2, 2, 4, kAllOps, false, kCrossSliceAgpr>(868, 815, 374, 3970),  // 20: direct loads, 4 stages
+    dl_variant<64, 64, 32, 2, 2, 4, kAllOps, true, kCrossSliceAgpr>(786, 700, 784, 4382),   // 21: 4-byte direct loads, 4 stages
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
