@@ -423,6 +423,18 @@ inline int variant_eff(const Variant &v, bool aligned16, bool lds_ok, bool stric
     return aligned16 && lds_ok ? v.eff_permille : v.eff_unaligned_permille;
 }
 
+// A 16-byte direct-load tile at the edge of an index-contiguous operand (B
+// as stored, or A transposed) whose last 16-byte chunk is only partly inside
+// N (or M) fetches every slice through registers, and the round waits for
+// it: such a block is priced at the variant's unaligned rate (measured with
+// every slice fetched through registers).
+inline bool edge_chunks(const Variant &v, const Problem &q)
+{
+    if (v.stages == 0 || v.dword) return false;
+    return (!q.transb && q.N % 4 != 0 && q.N % v.bn != 0) ||
+           (q.transa && q.M % 4 != 0 && q.M % v.bm != 0);
+}
+
 // Strip widths worth trying along a dimension of size d with tile size b:
 // none, and the rows past the last full tile when there are at most
 // kStripMaxWidth of them (all of d when d itself is that small).
@@ -469,6 +481,7 @@ inline Choice select_plan(const Variant *vs, int n, const Problem &p, int cus, b
                         }
                         continue;
                     }
+                    const int e = edge_chunks(v, q) ? v.eff_unaligned_permille : eff;
                     int last = 0;
                     for (int want : kSplitCandidates) {
                         int splits, k_chunk;
@@ -479,7 +492,7 @@ inline Choice select_plan(const Variant *vs, int n, const Problem &p, int cus, b
                         const long long grid =
                             ceil_div_ll(q.M, v.bm) * ceil_div_ll(q.N, v.bn) * splits * (long long)q.batch;
                         if (grid > INT_MAX) break;
-                        const double t = estimate_ns(v, q, splits, k_chunk, cus, eff) + ts;
+                        const double t = estimate_ns(v, q, splits, k_chunk, cus, e) + ts;
                         if (best.id < 0 || t < best_t) {
                             best = {i, splits, sms[a], sns[b]};
                             best_t = t;

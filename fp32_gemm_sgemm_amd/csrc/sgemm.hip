@@ -43,27 +43,28 @@ Variant mfma_variant(int eff_permille, int eff_one_permille, int eff_unaligned_p
 
 // OPS: bit (transa + 2*transb) set for each operand layout to compile.  DW:
 // 4-byte direct loads (rows need only be 4-byte aligned).
+// MB: 32x32 (32) or 16x16 (16) MFMA blocks.
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int OPS, bool DW = false,
-          int PIPE = 0>
+          int PIPE = 0, int MB = 32>
 Variant dl_variant(int eff_permille, int eff_one_permille, int eff_unaligned_permille,
                    int fixed_ns = 0)
 {
-    typedef sgemm::DlTraits<BM, BN, BK, WM, WN, STAGES, false, false, DW> T;
+    typedef sgemm::DlTraits<BM, BN, BK, WM, WN, STAGES, false, false, DW, MB> T;
     Variant v{SGEMM_KERNEL_MFMA, BM, BN, BK, WM, WN, -1, STAGES, DW ? 1 : 0,
               T::NT, (int)(T::LDS_FLOATS * sizeof(float)),
               {nullptr, nullptr, nullptr, nullptr}, eff_permille, eff_one_permille,
               eff_unaligned_permille, fixed_ns, 0, 0, 0};
     v.fn[0] = reinterpret_cast<const void *>(
-        &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, false, false, DW, PIPE>);
+        &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, false, false, DW, PIPE, MB>);
     if constexpr ((OPS & 2) != 0)
         v.fn[1] = reinterpret_cast<const void *>(
-            &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, true, false, DW, PIPE>);
+            &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, true, false, DW, PIPE, MB>);
     if constexpr ((OPS & 4) != 0)
         v.fn[2] = reinterpret_cast<const void *>(
-            &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, false, true, DW, PIPE>);
+            &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, false, true, DW, PIPE, MB>);
     if constexpr ((OPS & 8) != 0)
         v.fn[3] = reinterpret_cast<const void *>(
-            &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, true, true, DW, PIPE>);
+            &sgemm::sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, true, true, DW, PIPE, MB>);
     return v;
 }
 
@@ -146,8 +147,8 @@ const Variant kVariants[] = {
     dl_variant<64, 64, 64, 2, 2, 2, kAllOps, false, kCrossSliceAgpr>(893, 765, 336, 4108),  // 17: direct loads, 64-deep slices
     dl_variant<64, 64, 64, 2, 2, 2, kAllOps, true, kCrossSliceAgpr>(863, 706, 855, 4808),  // 18: 4-byte direct loads, 64-deep slices
     dl_variant<256, 256, 16, 4, 2, 2, kAllOps, true, kCrossSliceAgpr>(932, 955, 927),  // 19: 4-byte direct loads, 16-deep slices
-    dl_variant<64, 64, 32, 2, 2, 4, kAllOps, false, kCrossSliceAgpr>(868, 815, 374, 3970),  // 20: direct loads, 4 stages
-    dl_variant<64, 64, 32, 2, 2, 4, kAllOps, true, kCrossSliceAgpr>(786, 700, 784, 4382),   // 21: 4-byte direct loads, 4 stages
+    dl_variant<64, 64, 32, 2, 2, 4, kAllOps, false, kCrossSliceAgpr, 16>(906, 868, 371, 3900),  // 20: direct loads, 4 stages, 16x16 blocks
+    dl_variant<64, 64, 32, 2, 2, 4, kAllOps, true, kCrossSliceAgpr, 16>(894, 770, 894, 4455),   // 21: 4-byte direct loads, 4 stages, 16x16 blocks
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 

@@ -6,8 +6,11 @@
 // write instructions, and STAGES slices can be in flight.
 //
 // The MFMA part (wave tiles of 32x32 blocks, k permutation, fragment
-// ping-pong) is the one of sgemm_mfma.hpp.  What differs is the LDS layout
-// and the fetch:
+// ping-pong) is the one of sgemm_mfma.hpp; MB = 16 builds the same tiles from
+// 16x16 blocks (v_mfma_f32_16x16x4_f32), four times as many independent
+// accumulator chains per wave, which pays when one wave per SIMD runs a small
+// wave tile.  What differs from sgemm_mfma.hpp is the LDS layout and the
+// fetch:
 //
 //  * A direct load writes a wave's 64 lanes x EL floats to contiguous LDS
 //    (lane l at offset 4*EL*l, checked on the device for EL = 4 and EL = 1),
@@ -23,7 +26,9 @@
 //    BK = 16: f(r) = ((r >> 1) ^ (r >> 2)) & 3;
 //    BK = 32: f(r) = (r ^ ((r >> 3) & 1)) & 7;
 //    BK = 64: f(r) = r & 15 (a row is the 64 banks' width, so 16 rows read
-//    16 distinct chunk positions).
+//    16 distinct chunk positions);
+//    16x16 blocks (32-deep slices): f(r) = ((r & 2) << 1) | ((r & 4) >> 1),
+//    see chunk_swizzle.
 //  * Loads go through buffer resources ending at the operands' last
 //    elements; rows past the end read as zero, and data wholly past K, M or N
 //    gets an offset beyond every resource (also zero).  With 16-byte loads,
@@ -49,15 +54,31 @@
 //  PIPE & 4 keeps the accumulators in AGPRs.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace sgemm {
 
-template <int BK> __device__ __forceinline__ int chunk_swizzle(int r)
+// MB = 16 (16x16 blocks, 32-deep slices): f(r) = ((r & 2) << 1) | ((r & 4) >> 1).
+// A 16-byte fragment read there takes 16 consecutive rows in each lane
+// quarter q, at chunk 4g + q.  With the 32x32 layout's f that read costs 4
+// bank-conflict cycles on gfx950 (SQ_LDS_BANK_CONFLICT); among the linear maps
+// of row bits 0-3 to a chunk, this one was measured conflict-free for both k
+// groups of a slice at every 2 KB offset (the offsets of blocks, waves,
+// operands and stages here).
+template <int BK, int MB = 32> __device__ __forceinline__ int chunk_swizzle(int r)
 {
-    if constexpr (BK == 16) return ((r >> 1) ^ (r >> 2)) & 3;
-    else if constexpr (BK == 32) return (r ^ ((r >> 3) & 1)) & 7;
-    else return r & 15;
+    if constexpr (MB == 16) {
+        static_assert(BK == 32, "16x16 blocks are laid out for 32-deep slices");
+        return ((r & 2) << 1) | ((r & 4) >> 1);
+    } else if constexpr (BK == 16) {
+        return ((r >> 1) ^ (r >> 2)) & 3;
+    } else if constexpr (BK == 32) {
+        return (r ^ ((r >> 3) & 1)) & 7;
+    } else {
+        return r & 15;
+    }
 }
 
 // Three adjacent floats with 4-byte alignment (the compiler picks the LDS
@@ -92,25 +113,26 @@ __device__ __forceinline__ float dl_elem(const V &v, int b)
 }
 
 // One operand's tile in LDS.  X is the operand's own index (rows of C for A,
-// columns of C for B); a tile covers E of them, a wave WT, in W blocks of 32.
-// Block b of a wave holds the indices x = wave_offset + W*l + b, l = 0..31
-// (interleaved), so a lane's W results of one C row or column are adjacent.
+// columns of C for B); a tile covers E of them, a wave WT, in W blocks of MB
+// (32 or 16).  Block b of a wave holds the indices x = wave_offset + W*l + b,
+// l = 0..MB-1 (interleaved), so a lane's W results of one C row or column are
+// adjacent.
 //
 //  KC ("k contiguous": A, or a transposed B): the operand's rows run along k.
 //     LDS holds E rows of BK floats; row L holds index P(L) = wave offset +
-//     W*(L%32) + (L%WT)/32, so the 32 rows a fragment read touches are
+//     W*(L%MB) + (L%WT)/MB, so the MB rows a fragment read touches are
 //     consecutive; chunk p of row L is stored at chunk p ^ f(L).  A fragment
 //     read is one 16-byte read per block: 4 successive k of one index.
 //  XC ("index contiguous": B, or a transposed A): the operand's rows run
 //     along X.  LDS holds BK rows of E floats; a fragment read is one W-wide
 //     read per k: the W blocks' values at one k.
-template <int E, int BK, int WT, int NW, bool KC, bool DW>
+template <int E, int BK, int WT, int NW, bool KC, bool DW, int MB = 32>
 struct DlOperand {
-    static constexpr int W = WT / 32;
+    static constexpr int W = WT / MB;
     static constexpr int ELEMS = DW ? 1 : 4;            // floats per lane per load
     static constexpr int LOADS = E * BK / ELEMS / (NW * 64);  // per thread per slice
     static constexpr int FLOATS = E * BK;
-    static_assert(WT % 32 == 0 && W >= 1, "wave tiles must be multiples of 32");
+    static_assert(WT % MB == 0 && W >= 1, "wave tiles must be multiples of the block");
     static_assert(KC || (W >= 1 && W <= 4), "index-contiguous fragments are 1 to 4 wide");
     static_assert(LOADS * NW * 64 * ELEMS == E * BK, "slices must split into whole wave loads");
 
@@ -152,24 +174,24 @@ struct DlOperand {
         c = q % rl;
         r = row;
         if constexpr (KC) {
-            c = 4 * ((c / 4) ^ chunk_swizzle<BK>(row)) + c % 4;
+            c = 4 * ((c / 4) ^ chunk_swizzle<BK, MB>(row)) + c % 4;
             const int in = row % WT;
-            r = row - in + W * (in % 32) + in / 32;
+            r = row - in + W * (in % MB) + in / MB;
         }
     }
 };
 
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, bool TA, bool TB,
-          bool DW = false>
+          bool DW = false, int MB = 32>
 struct DlTraits {
     static constexpr int NW = WAVES_M * WAVES_N;
     static constexpr int NT = NW * 64;
     static constexpr int WTM = BM / WAVES_M;
     static constexpr int WTN = BN / WAVES_N;
-    static constexpr int RM = WTM / 32;
-    static constexpr int NB = WTN / 32;
-    typedef DlOperand<BM, BK, WTM, NW, !TA, DW> OpA;
-    typedef DlOperand<BN, BK, WTN, NW, TB, DW> OpB;
+    static constexpr int RM = WTM / MB;
+    static constexpr int NB = WTN / MB;
+    typedef DlOperand<BM, BK, WTM, NW, !TA, DW, MB> OpA;
+    typedef DlOperand<BN, BK, WTN, NW, TB, DW, MB> OpB;
     static constexpr int A_FLOATS = BM * BK;
     static constexpr int STAGE_FLOATS = BM * BK + BK * BN;
     static constexpr int LDS_FLOATS = STAGES * STAGE_FLOATS;
@@ -181,17 +203,20 @@ struct DlTraits {
 
 
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, bool TA, bool TB, bool DW,
-          int PIPE = 0>
+          int PIPE = 0, int MB = 32>
 __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64)
 sgemm_mfma_dl_kernel(GemmArgs g)
 {
-    typedef DlTraits<BM, BN, BK, WAVES_M, WAVES_N, STAGES, TA, TB, DW> T;
+    typedef DlTraits<BM, BN, BK, WAVES_M, WAVES_N, STAGES, TA, TB, DW, MB> T;
     typedef typename T::OpA OpA;
     typedef typename T::OpB OpB;
     constexpr int NW = T::NW, WTM = T::WTM, WTN = T::WTN, RM = T::RM, NB = T::NB;
     constexpr int A_LOADS = OpA::LOADS, B_LOADS = OpB::LOADS;
     constexpr int STAGE_FLOATS = T::STAGE_FLOATS, A_FLOATS = T::A_FLOATS;
-    constexpr int G = BK / 8;
+    static_assert(MB == 32 || MB == 16, "32x32x2 or 16x16x4 blocks");
+    constexpr int G = BK / (MB == 32 ? 8 : 16);  // k groups per slice
+    constexpr int ACC = MB == 32 ? 16 : 4;        // accumulators per block per lane
+    typedef typename std::conditional<MB == 32, f32x16, f32x4>::type acc_t;
     constexpr int EL = DW ? 1 : 4;  // floats per lane per load
 
     __shared__ __attribute__((aligned(1024))) float smem[T::LDS_FLOATS];
@@ -212,13 +237,13 @@ sgemm_mfma_dl_kernel(GemmArgs g)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
-    f32x16 acc[RM][NB];
+    acc_t acc[RM][NB];
 #pragma unroll
     for (int i = 0; i < RM; ++i)
 #pragma unroll
         for (int j = 0; j < NB; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+            for (int r = 0; r < ACC; ++r) acc[i][j][r] = 0.0f;
 
     // ---- fetch assignment ------------------------------------------------------
     // Load j of this thread fills EL floats at LDS float (j*NW + wave)*64*EL +
@@ -349,15 +374,20 @@ sgemm_mfma_dl_kernel(GemmArgs g)
     };
 
     // ---- fragments -----------------------------------------------------------------
-    // MFMA step t (0..3) of k group g takes k = 8g + t from lanes 0-31 and
-    // k = 8g + 4 + t from lanes 32-63 (h = lane >> 5).
-    //  KC: block b's index for lane l is LDS row wave_offset + 32b + (l & 31),
-    //      whose k values 8g + 4h .. +3 are logical chunk 2g + h, stored at
-    //      (2g + h) ^ f(row) = 2g ^ (h ^ f(l & 31)) (2g is even, and f only
-    //      sees row bits 0-3).
-    //  XC: LDS row k, W floats at column wave_offset + W*(l & 31).
-    const int l31 = lane & 31, h = lane >> 5;
-    const int u = h ^ chunk_swizzle<BK>(l31);
+    // 32x32 blocks: MFMA step t (0..3) of k group g (8 deep) takes k = 8g + t
+    // from lanes 0-31 and k = 8g + 4 + t from lanes 32-63 (h = lane >> 5).
+    // 16x16 blocks: step t of k group g (16 deep) takes k = 16g + 4h + t from
+    // lane quarter h = lane >> 4.  Both operands use the same k for a lane
+    // group, so the permuted order sums the same products.
+    //  KC: block b's index for lane l is LDS row wave_offset + MB*b + (l mod
+    //      MB), whose k values of step 0..3 are logical chunk KQ*g + h (KQ
+    //      chunks per k group), stored at (KQ*g + h) ^ f(row) = KQ*g ^ (h ^
+    //      f(l mod MB)) (KQ*g has no bit of h, and f only sees row bits 0-3).
+    //  XC: LDS row k, W floats at column wave_offset + W*(l mod MB).
+    constexpr int LB = MB - 1;
+    constexpr int KQ = MB == 32 ? 2 : 4;  // 16-byte chunks per k group
+    const int l31 = lane & LB, h = MB == 32 ? lane >> 5 : lane >> 4;
+    const int u = h ^ chunk_swizzle<BK, MB>(l31);
     typedef typename DlXVec<TA, RM>::T xa_t;
     typedef typename DlXVec<!TB, NB>::T xb_t;
     struct Frag {
@@ -374,20 +404,20 @@ sgemm_mfma_dl_kernel(GemmArgs g)
         if constexpr (TA) {
 #pragma unroll
             for (int t = 0; t < 4; ++t)
-                f.xa[t] = *reinterpret_cast<const xa_t *>(as + (8 * gi + t) * BM);
+                f.xa[t] = *reinterpret_cast<const xa_t *>(as + (4 * KQ * gi + t) * BM);
         } else {
 #pragma unroll
             for (int i = 0; i < RM; ++i)
-                f.ka[i] = *reinterpret_cast<const f32x4 *>(as + i * 32 * BK + 4 * ((2 * gi) ^ u));
+                f.ka[i] = *reinterpret_cast<const f32x4 *>(as + i * MB * BK + 4 * ((KQ * gi) ^ u));
         }
         if constexpr (TB) {
 #pragma unroll
             for (int j = 0; j < NB; ++j)
-                f.kb[j] = *reinterpret_cast<const f32x4 *>(bs + j * 32 * BK + 4 * ((2 * gi) ^ u));
+                f.kb[j] = *reinterpret_cast<const f32x4 *>(bs + j * MB * BK + 4 * ((KQ * gi) ^ u));
         } else {
 #pragma unroll
             for (int t = 0; t < 4; ++t)
-                f.xb[t] = *reinterpret_cast<const xb_t *>(bs + (8 * gi + t) * BN);
+                f.xb[t] = *reinterpret_cast<const xb_t *>(bs + (4 * KQ * gi + t) * BN);
         }
     };
     auto mfma_frag = [&](const Frag &f) {
@@ -402,7 +432,10 @@ sgemm_mfma_dl_kernel(GemmArgs g)
                     else a = f.ka[i][t];
                     if constexpr (TB) b = f.kb[j][t];
                     else b = dl_elem<NB>(f.xb[t], j);
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc[i][j], 0, 0, 0);
+                    if constexpr (MB == 32)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc[i][j], 0, 0, 0);
+                    else
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[i][j], 0, 0, 0);
                 }
     };
 
@@ -546,16 +579,18 @@ sgemm_mfma_dl_kernel(GemmArgs g)
 
     // ---- epilogue ----------------------------------------------------------------------
     // Accumulator r of block (i, j) in lane l is D[8*(r/4) + 4*h + r%4][l & 31]
-    // of that block: C row wave_offset + RM*(8*(r/4) + 4*h + r%4) + i, column
-    // wave_offset + NB*(l & 31) + j, so a lane holds NB adjacent columns.
+    // of a 32x32 block, D[4*h + r][l & 15] of a 16x16 one (h as above): C row
+    // wave_offset + RM*(that row) + i, column wave_offset + NB*(l mod MB) + j,
+    // so a lane holds NB adjacent columns.
     float *__restrict__ C = g.C;
     const int ldc = g.ldc;
     const int col = n0 + wn * WTN + NB * l31;
 #pragma unroll
     for (int i = 0; i < RM; ++i) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = m0 + wm * WTM + RM * (8 * (r >> 2) + 4 * h + (r & 3)) + i;
+        for (int r = 0; r < ACC; ++r) {
+            const int row = m0 + wm * WTM +
+                            RM * (MB == 32 ? 8 * (r >> 2) + 4 * h + (r & 3) : 4 * h + r) + i;
             if (row >= M) continue;
             float v[NB];
 #pragma unroll
