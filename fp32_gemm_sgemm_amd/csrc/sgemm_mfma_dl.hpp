@@ -94,6 +94,18 @@ constexpr uint32_t kOobOffset = 0x80000000u;
 
 template <bool B> struct DlTag { static constexpr bool value = B; };
 
+// x if e < n, else +0: the sign of e - n as a bit mask, with no compare (a
+// compare per element leaves a 64-bit lane mask per element in scalar
+// registers, which the compiler hoists and spills).
+__device__ __forceinline__ float keep_below(float x, int e, int n)
+{
+    const uint32_t keep = (uint32_t)((e - n) >> 31);
+    uint32_t r;
+    // (the AND is opaque: the compiler would turn the mask back into a compare)
+    asm volatile("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(__builtin_bit_cast(uint32_t, x)), "v"(keep));
+    return __builtin_bit_cast(float, r);
+}
+
 template <int W> struct DlVec;
 template <> struct DlVec<1> { typedef float T; };
 template <> struct DlVec<2> { typedef f32x2 T; };
@@ -327,10 +339,11 @@ sgemm_mfma_dl_kernel(GemmArgs g)
 #pragma unroll
             for (int j = 0; j < A_LOADS; ++j) {
                 float v[EL];
+                const int n_in = a_lim - a_col[j];  // floats of this load inside the data
 #pragma unroll
                 for (int e = 0; e < EL; ++e) {
                     const float x = buffer_load_f32(ar, a_off[j] + 4u * e);
-                    v[e] = (a_col[j] + e < a_lim) ? x : 0.0f;
+                    v[e] = keep_below(x, e, n_in);
                 }
                 put(smem + s * STAGE_FLOATS + ((j * NW + wave) * 64 + lane) * EL, v);
                 __builtin_amdgcn_sched_barrier(0);
@@ -338,10 +351,11 @@ sgemm_mfma_dl_kernel(GemmArgs g)
 #pragma unroll
             for (int j = 0; j < B_LOADS; ++j) {
                 float v[EL];
+                const int n_in = b_lim - b_col[j];  // floats of this load inside the data
 #pragma unroll
                 for (int e = 0; e < EL; ++e) {
                     const float x = buffer_load_f32(br, b_off[j] + 4u * e);
-                    v[e] = (b_col[j] + e < b_lim) ? x : 0.0f;
+                    v[e] = keep_below(x, e, n_in);
                 }
                 put(smem + s * STAGE_FLOATS + A_FLOATS + ((j * NW + wave) * 64 + lane) * EL, v);
                 __builtin_amdgcn_sched_barrier(0);
