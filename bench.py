@@ -43,7 +43,9 @@ One JSON line is printed.  Besides the driver's fields it holds:
   meta          device, HIP runtime and driver, ROCm and hipcc versions, the
                 power mode, and the host's cores.
   vendor        context only: torch.matmul in float32 (the ROCm BLAS libraries,
-                TF32 disabled) timed the same way at 8192^3 and 3072^3.
+                TF32 disabled) timed the same way on the square shapes from
+                512^3 to 8192^3, and torch.bmm on the two batched attention
+                products.
   extras        the library's other paths, each timed the same way after a
                 time-based warm-up (--extra-warm-ms): the small 512^3
                 configuration and the one-tile 128 x 128 x 32768 product with
@@ -51,7 +53,7 @@ One JSON line is printed.  Besides the driver's fields it holds:
                 transposed-operand layouts at 8192^3 and 3072^3, strided
                 batches of attention-like products, the 1024 x 8192 x 8192
                 row band one GPU would run if 8192^3 were split over 8 GPUs,
-                shapes whose few edge rows or columns (or all of them, for
+                1024^3 (one 64 x 64 tile per CU), shapes whose few edge rows or columns (or all of them, for
                 products of 1 row or column) go to the strip kernel, and the
                 vector-FMA comparison kernel forced at 8192^3 and 3072^3
                 (with its fraction of valu_probe).
@@ -378,16 +380,18 @@ def extras(torch, sg, steps, warm_ms, cus, peak):
     torch.cuda.empty_cache()
 
     # one GPU's share of 8192^3 split by rows of C over 8 GPUs (a 1024-row band
-    # of A times all of B), the shape each GPU would run in a row-band sharding
-    M, N, K = 1024, 8192, 8192
-    A, B = operand((M, K)), operand((K, N))
-    C = torch.empty((M, N), device="cuda")
-    plan = sg.sgemm_f32_plan(M, N, K, K, N, N, cus)
-    h = stream.cuda_stream
-    ms = time_call(torch, lambda: chk(sg.sgemm_f32(M, N, K, A.data_ptr(), K, B.data_ptr(), N,
-                                                C.data_ptr(), N, h)), steps, warm_ms)
-    record("row-band shard 1024x8192x8192 (8192^3 over 8 GPUs)", 2.0 * M * N * K, ms, plan)
-    del A, B, C
+    # of A times all of B), the shape each GPU would run in a row-band sharding;
+    # and 1024^3, one 64x64 tile per CU
+    for name, M, N, K in [("row-band shard 1024x8192x8192 (8192^3 over 8 GPUs)", 1024, 8192, 8192),
+                          ("1024^3", 1024, 1024, 1024)]:
+        A, B = operand((M, K)), operand((K, N))
+        C = torch.empty((M, N), device="cuda")
+        plan = sg.sgemm_f32_plan(M, N, K, K, N, N, cus)
+        h = stream.cuda_stream
+        ms = time_call(torch, lambda: chk(sg.sgemm_f32(M, N, K, A.data_ptr(), K, B.data_ptr(), N,
+                                                    C.data_ptr(), N, h)), steps, warm_ms)
+        record(name, 2.0 * M * N * K, ms, plan)
+        del A, B, C
     torch.cuda.empty_cache()
 
     # edge strips: a few rows or columns past the last full tile, and products
@@ -414,18 +418,32 @@ def extras(torch, sg, steps, warm_ms, cus, peak):
 
 
 def vendor(torch, steps, warm_ms, peak):
-    """torch.matmul (rocBLAS / hipBLASLt) in float32 on the same shapes, for context."""
+    """torch.matmul (rocBLAS / hipBLASLt) in float32 on the same shapes, and
+    torch.bmm on the two batched attention products, for context."""
     out = []
     torch.backends.cuda.matmul.allow_tf32 = False
-    for n in (8192, 3072, 4096, 2048, 512):
+
+    def rec(shape, flops, ms):
+        tf = flops / (ms * 1e-3) / 1e12
+        out.append(dict(shape=shape, value=round(tf, 3), unit="TFLOP/s", ms=round(ms, 5),
+                        frac_of_fp32_matrix_peak=round(tf / peak, 4)))
+
+    for n in (8192, 3072, 4096, 2048, 1024, 512):
         A = torch.rand((n, n), device="cuda") * 2 - 1
         B = torch.rand((n, n), device="cuda") * 2 - 1
         C = torch.empty((n, n), device="cuda")
-        ms = time_call(torch, lambda: torch.matmul(A, B, out=C), steps, warm_ms)
-        tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
-        out.append(dict(shape=f"{n}^3", value=round(tf, 3), unit="TFLOP/s", ms=round(ms, 5),
-                        frac_of_fp32_matrix_peak=round(tf / peak, 4)))
+        rec(f"{n}^3", 2.0 * n ** 3, time_call(torch, lambda: torch.matmul(A, B, out=C), steps, warm_ms))
         del A, B, C
+    # float32 operands: B of the NT product is passed as a transposed view
+    for shape, batch, M, N, K, tb in [("64 x QK^T 1024x1024x128 NT (torch.bmm)", 64, 1024, 1024, 128, 1),
+                                      ("64 x PV 1024x128x1024 NN (torch.bmm)", 64, 1024, 128, 1024, 0)]:
+        A = torch.rand((batch, M, K), device="cuda") * 2 - 1
+        B = torch.rand((batch, N, K) if tb else (batch, K, N), device="cuda") * 2 - 1
+        Bv = B.transpose(1, 2) if tb else B
+        C = torch.empty((batch, M, N), device="cuda")
+        rec(shape, 2.0 * batch * M * N * K,
+            time_call(torch, lambda: torch.bmm(A, Bv, out=C), steps, warm_ms))
+        del A, B, Bv, C
     torch.cuda.empty_cache()
     return out
 
