@@ -17,6 +17,9 @@ LIB_PATH = os.path.join(HERE, "libsgemm.so")
 # The LDS race check build of the same sources (LDS words set to NaN before
 # each refill); only tests route calls to it, through library().
 POISON_LIB_PATH = os.path.join(HERE, "libsgemm_lds_poison.so")
+# The timeline build (clock readings inside the direct-load kernel, read
+# through the functions of include/sgemm_timeline.h); timeline.py drives it.
+TIMELINE_LIB_PATH = os.path.join(HERE, "libsgemm_timeline.so")
 
 SGEMM_KERNEL_MFMA = 0
 SGEMM_KERNEL_VALU = 1
@@ -99,6 +102,15 @@ def load(path=None):
         fn.restype = i
     lib.sgemm_f32_version.argtypes = []
     lib.sgemm_f32_version.restype = ctypes.c_char_p
+    if hasattr(lib, "sgemm_f32_timeline_read"):  # the timeline build only
+        ip = ctypes.POINTER(i)
+        lib.sgemm_f32_timeline_layout.argtypes = [ip, ip, ip, ip]
+        lib.sgemm_f32_timeline_read.argtypes = [p, sz, p, sz]
+        lib.sgemm_f32_timeline_clear.argtypes = []
+        lib.sgemm_f32_timeline_clock_khz.argtypes = [ip]
+        for name in ("sgemm_f32_timeline_layout", "sgemm_f32_timeline_read",
+                     "sgemm_f32_timeline_clear", "sgemm_f32_timeline_clock_khz"):
+            getattr(lib, name).restype = i
     _libs[path] = lib
     return lib
 

@@ -9,7 +9,10 @@ warns that it does not know that feature, which is harmless.
 Besides the product library it builds the measurement probes
 (libsgemm_probes.so) and the LDS race check build of the same sources
 (libsgemm_lds_poison.so, SGEMM_LDS_POISON=1: LDS words are set to NaN before
-each refill), which only the tests load.  The three compile in parallel.
+each refill), which only the tests load, and the timeline build
+(libsgemm_timeline.so, SGEMM_TIMELINE=1: clock readings per workgroup and per
+K slice, read through include/sgemm_timeline.h).  The four compile in
+parallel.
 """
 import argparse
 import os
@@ -23,6 +26,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsgemm.so")
 PROBES_LIB = os.path.join(HERE, "libsgemm_probes.so")
 POISON_LIB = os.path.join(HERE, "libsgemm_lds_poison.so")
+TIMELINE_LIB = os.path.join(HERE, "libsgemm_timeline.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -50,14 +54,17 @@ def _hipcc(out, sources, save_temps=None, verbose=False, extra=()):
 
 def build(save_temps: str = None, verbose: bool = False, extra=()) -> str:
     """Compile libsgemm.so (the product), libsgemm_probes.so (measurement
-    probes) and libsgemm_lds_poison.so (the LDS race check build); returns
-    the product library's path.  With save_temps, only the product library is
+    probes), libsgemm_lds_poison.so (the LDS race check build) and
+    libsgemm_timeline.so (the timeline build); returns the product library's
+    path.  With save_temps, only the product library is
     built (its intermediate files go there)."""
     jobs = [_hipcc(LIB, SOURCES, save_temps, verbose, extra)]
     if not save_temps:
         jobs.append(_hipcc(PROBES_LIB, PROBE_SOURCES, None, verbose, extra))
         jobs.append(_hipcc(POISON_LIB, SOURCES, None, verbose,
                            ("-DSGEMM_LDS_POISON=1", *extra)))
+        jobs.append(_hipcc(TIMELINE_LIB, SOURCES, None, verbose,
+                           ("-DSGEMM_TIMELINE=1", *extra)))
     failed = []
     for proc, out in jobs:
         if proc.wait() != 0:

@@ -163,6 +163,36 @@ __device__ __forceinline__ void lds_poison_done()
     asm volatile("" ::: "memory");
 }
 
+// Timeline build.  With SGEMM_TIMELINE=1 the direct-load kernel reads the
+// shader clock (s_memtime) at fixed points and keeps the readings in device
+// arrays that sgemm_f32_timeline_read copies out:
+//  phase: per workgroup of a call's first launch with id below
+//         kTlPhaseWgs, the clock at entry, after the first slice has landed
+//         (the loop starts), after the last slice, and once every thread's
+//         stores of C are done; then the device's constant-rate real-time
+//         counter (s_memrealtime) at entry and at that end;
+//  slice: per workgroup below kTlSliceWgs, per wave and per slice below
+//         kTlSlices, the clock before and after the wave waits for its own
+//         loads of the next slice (the workgroup barrier follows).
+// The per-slice readings go to LDS beside the stages and are copied out at
+// the end, so the loop issues no global stores; the clock readings are
+// scalar reads, whose count the loop waits out right after the second one.
+// Shader-clock readings of different compute units come from unrelated
+// counters: only differences within one workgroup mean anything.  The
+// real-time counter is one for the device, so its readings place the
+// workgroups against each other, and against the shader clock they give the
+// clock's rate.  The normal build
+// (SGEMM_TIMELINE=0) compiles none of it.
+#ifndef SGEMM_TIMELINE
+#define SGEMM_TIMELINE 0
+#endif
+#if SGEMM_TIMELINE
+constexpr int kTlPhaseWgs = 4096, kTlSliceWgs = 16, kTlWaves = 16, kTlSlices = 256;
+constexpr int kTlPhaseValues = 6;
+__device__ unsigned long long g_tl_phase[kTlPhaseWgs * kTlPhaseValues];
+__device__ uint32_t g_tl_slice[kTlSliceWgs * kTlWaves * kTlSlices * 2];
+#endif
+
 // A raw buffer resource over [base, base + bytes): loads at or past its end
 // return zero and never fault.  bytes <= 0 gives an empty resource; sizes
 // above 4 GiB - 1 are clamped (offsets used with a resource stay below that).

@@ -738,3 +738,60 @@ int sgemm_f32(int M, int N, int K, const float *A, int lda, const float *B, int 
 }
 
 }  // extern "C"
+
+#if SGEMM_TIMELINE
+// Timeline build only: the clock readings of the direct-load kernel (the
+// layout is documented in sgemm_timeline.h).
+extern "C" {
+
+int sgemm_f32_timeline_layout(int *phase_wgs, int *slice_wgs, int *waves, int *slices)
+{
+    if (!phase_wgs || !slice_wgs || !waves || !slices) return (int)hipErrorInvalidValue;
+    static_assert(sgemm::kTlPhaseValues == 6, "phase readings per workgroup");
+    *phase_wgs = sgemm::kTlPhaseWgs;
+    *slice_wgs = sgemm::kTlSliceWgs;
+    *waves = sgemm::kTlWaves;
+    *slices = sgemm::kTlSlices;
+    return (int)hipSuccess;
+}
+
+int sgemm_f32_timeline_read(unsigned long long *phase, size_t phase_bytes, unsigned int *slice,
+                            size_t slice_bytes)
+{
+    if (phase_bytes > sizeof(sgemm::g_tl_phase) || slice_bytes > sizeof(sgemm::g_tl_slice) ||
+        (phase_bytes && !phase) || (slice_bytes && !slice))
+        return (int)hipErrorInvalidValue;
+    hipError_t e = hipSuccess;
+    if (phase_bytes)
+        e = hipMemcpyFromSymbol(phase, HIP_SYMBOL(sgemm::g_tl_phase), phase_bytes, 0,
+                                hipMemcpyDeviceToHost);
+    if (e == hipSuccess && slice_bytes)
+        e = hipMemcpyFromSymbol(slice, HIP_SYMBOL(sgemm::g_tl_slice), slice_bytes, 0,
+                                hipMemcpyDeviceToHost);
+    return (int)e;
+}
+
+int sgemm_f32_timeline_clock_khz(int *khz)
+{
+    if (!khz) return (int)hipErrorInvalidValue;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(khz, hipDeviceAttributeWallClockRate, dev);
+    return (int)e;
+}
+
+int sgemm_f32_timeline_clear(void)
+{
+    constexpr size_t kBytes = sizeof(sgemm::g_tl_slice) > sizeof(sgemm::g_tl_phase)
+                                  ? sizeof(sgemm::g_tl_slice) : sizeof(sgemm::g_tl_phase);
+    static const unsigned char zeros[kBytes] = {};
+    hipError_t e = hipMemcpyToSymbol(HIP_SYMBOL(sgemm::g_tl_phase), zeros, sizeof(sgemm::g_tl_phase), 0,
+                                     hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+        e = hipMemcpyToSymbol(HIP_SYMBOL(sgemm::g_tl_slice), zeros, sizeof(sgemm::g_tl_slice), 0,
+                              hipMemcpyHostToDevice);
+    return (int)e;
+}
+
+}  // extern "C"
+#endif

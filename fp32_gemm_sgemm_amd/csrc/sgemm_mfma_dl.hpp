@@ -231,7 +231,17 @@ sgemm_mfma_dl_kernel(GemmArgs g)
     typedef typename std::conditional<MB == 32, f32x16, f32x4>::type acc_t;
     constexpr int EL = DW ? 1 : 4;  // floats per lane per load
 
+#if SGEMM_TIMELINE
+    // per-slice clock readings beside the stages (see g_tl_slice)
+    static_assert(NW <= kTlWaves, "waves recorded per workgroup");
+    __shared__ __attribute__((aligned(1024))) float smem[T::LDS_FLOATS + NW * kTlSlices * 2];
+    uint32_t *const tl_lds = reinterpret_cast<uint32_t *>(smem + T::LDS_FLOATS);
+    const unsigned long long tl_entry = __builtin_amdgcn_s_memtime();
+    const unsigned long long tl_entry_rt = __builtin_amdgcn_s_memrealtime();
+    unsigned long long tl_loop0 = 0;
+#else
     __shared__ __attribute__((aligned(1024))) float smem[T::LDS_FLOATS];
+#endif
 
     // PIPE bit 2: an (empty) AGPR clobber makes the register allocator keep
     // the accumulators in AGPRs.  It pays with the cross-slice loop; with the
@@ -493,6 +503,10 @@ sgemm_mfma_dl_kernel(GemmArgs g)
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
             read_frag(0, 0, f[0]);
+#if SGEMM_TIMELINE
+            tl_loop0 = __builtin_amdgcn_s_memtime();
+            __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));  // the reading (and the reads above)
+#endif
         }
         uint32_t af[A_LOADS], bf[B_LOADS];
         // One slice kt.  FULL: the slice fetched here (kt+STAGES-1) lies wholly
@@ -531,8 +545,21 @@ sgemm_mfma_dl_kernel(GemmArgs g)
                     // own loads of slice kt+1 landed (the later slices' may still
                     // be in flight) and own reads of slice kt done, barrier, then
                     // the next slice's first fragments
+#if SGEMM_TIMELINE
+                    const uint32_t tl_t0 = (uint32_t)__builtin_amdgcn_s_memtime();
+#endif
                     if (more) __builtin_amdgcn_s_waitcnt(WAIT_LATER_LGKM0);
                     else __builtin_amdgcn_s_waitcnt(WAIT_ALL);
+#if SGEMM_TIMELINE
+                    const uint32_t tl_t1 = (uint32_t)__builtin_amdgcn_s_memtime();
+                    // wait for the reading on every path, so that no later
+                    // fragment wait has to cover an outstanding scalar read
+                    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));
+                    if (lane == 0 && kt < kTlSlices) {
+                        tl_lds[(wave * kTlSlices + kt) * 2] = tl_t0;
+                        tl_lds[(wave * kTlSlices + kt) * 2 + 1] = tl_t1;
+                    }
+#endif
                     asm volatile("" ::: "memory");
                     __builtin_amdgcn_s_barrier();
                     asm volatile("" ::: "memory");
@@ -563,8 +590,14 @@ sgemm_mfma_dl_kernel(GemmArgs g)
             for (; kt < kend; ++kt) slice(kt, DlTag<true>());
         }
         for (; kt < nk; ++kt) slice(kt, DlTag<false>());
+#if SGEMM_TIMELINE
+        if (nk == 0) tl_loop0 = __builtin_amdgcn_s_memtime();
+#endif
     } else {
         // Plain pipeline.
+#if SGEMM_TIMELINE
+        tl_loop0 = __builtin_amdgcn_s_memtime();
+#endif
 #pragma unroll
         for (int s = 0; s < STAGES - 1; ++s)
             if (s < nk) fetch(s, s);
@@ -591,6 +624,9 @@ sgemm_mfma_dl_kernel(GemmArgs g)
         }
     }
 
+#if SGEMM_TIMELINE
+    const unsigned long long tl_loop1 = __builtin_amdgcn_s_memtime();
+#endif
     // ---- epilogue ----------------------------------------------------------------------
     // Accumulator r of block (i, j) in lane l is D[8*(r/4) + 4*h + r%4][l & 31]
     // of a 32x32 block, D[4*h + r][l & 15] of a 16x16 one (h as above): C row
@@ -612,6 +648,29 @@ sgemm_mfma_dl_kernel(GemmArgs g)
             store_row<NB>(C + (int64_t)row * ldc + col, col, N, v, g.alpha, g.beta);
         }
     }
+#if SGEMM_TIMELINE
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's stores are done
+    __syncthreads();
+    const unsigned long long tl_end = __builtin_amdgcn_s_memtime();
+    const unsigned long long tl_end_rt = __builtin_amdgcn_s_memrealtime();
+    if (g.wg_base == 0 && (int)blockIdx.x < kTlSliceWgs) {
+        // the slices this workgroup ran (the plain pipeline records none);
+        // the LDS slots past them were never written
+        const int rec = (PIPE & 2) != 0 ? min(nk, kTlSlices) : 0;
+        uint32_t *dst = g_tl_slice + (size_t)blockIdx.x * kTlWaves * kTlSlices * 2;
+        for (int i = tid; i < NW * kTlSlices * 2; i += T::NT)
+            dst[i] = (i >> 1) % kTlSlices < rec ? tl_lds[i] : 0u;
+    }
+    if (g.wg_base == 0 && tid == 0 && (int)blockIdx.x < kTlPhaseWgs) {
+        unsigned long long *ph = g_tl_phase + (size_t)blockIdx.x * kTlPhaseValues;
+        ph[0] = tl_entry;
+        ph[1] = tl_loop0;
+        ph[2] = tl_loop1;
+        ph[3] = tl_end;
+        ph[4] = tl_entry_rt;
+        ph[5] = tl_end_rt;
+    }
+#endif
 }
 
 }  // namespace sgemm

@@ -36,11 +36,11 @@ def test_header_declares_expected_entry_points():
     assert len(names) >= 7
 
 
-@pytest.mark.parametrize("path", [sg.LIB_PATH, sg.POISON_LIB_PATH],
-                         ids=["product", "lds_poison"])
+@pytest.mark.parametrize("path", [sg.LIB_PATH, sg.POISON_LIB_PATH, sg.TIMELINE_LIB_PATH],
+                         ids=["product", "lds_poison", "timeline"])
 def test_every_declared_symbol_is_exported(lib, path):
-    """The product library and its LDS race check build export every entry
-    point the header declares."""
+    """The product library, its LDS race check build and its timeline build
+    export every entry point the header declares."""
     out = subprocess.run(["nm", "-D", "--defined-only", path],
                          capture_output=True, text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
@@ -48,6 +48,36 @@ def test_every_declared_symbol_is_exported(lib, path):
     for name in declared_functions():
         assert name in exported, name
         assert hasattr(handle, name)
+
+
+def timeline_functions():
+    text = open(os.path.join(ROOT, "include", "sgemm_timeline.h")).read()
+    return sorted(set(re.findall(r"^\s*int\s*(sgemm_f32_timeline\w*)\s*\(", text, re.M)))
+
+
+def test_timeline_functions_only_in_the_timeline_build(lib):
+    """include/sgemm_timeline.h's functions are exported by the timeline build
+    and by no other; without a GPU, layout() reports the array sizes and
+    read() refuses oversized copies before any HIP call."""
+    names = timeline_functions()
+    assert names == ["sgemm_f32_timeline_clear", "sgemm_f32_timeline_clock_khz",
+                     "sgemm_f32_timeline_layout", "sgemm_f32_timeline_read"]
+
+    def exported(path):
+        out = subprocess.run(["nm", "-D", "--defined-only", path],
+                             capture_output=True, text=True, check=True).stdout
+        return {line.split()[-1] for line in out.splitlines() if line.strip()}
+    assert set(names) <= exported(sg.TIMELINE_LIB_PATH)
+    assert not set(names) & exported(sg.LIB_PATH)
+    assert not set(names) & exported(sg.POISON_LIB_PATH)
+    tl = sg.load(sg.TIMELINE_LIB_PATH)
+    vals = [ctypes.c_int() for _ in range(4)]
+    assert tl.sgemm_f32_timeline_layout(*[ctypes.byref(v) for v in vals]) == 0
+    assert [v.value for v in vals] == [4096, 16, 16, 256]
+    assert tl.sgemm_f32_timeline_layout(None, None, None, None) == HIP_ERROR_INVALID_VALUE
+    assert tl.sgemm_f32_timeline_read(None, 4096 * 6 * 8 + 8, None, 0) == HIP_ERROR_INVALID_VALUE
+    assert tl.sgemm_f32_timeline_clock_khz(None) == HIP_ERROR_INVALID_VALUE
+    assert tl.sgemm_f32_timeline_read(None, 8, None, 0) == HIP_ERROR_INVALID_VALUE
 
 
 def test_library_switch_routes_calls():

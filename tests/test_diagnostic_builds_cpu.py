@@ -1,7 +1,8 @@
-"""The LDS race check build is not vacuous: compiled for gfx950 with
-SGEMM_LDS_POISON=1, every kernel that reads LDS writes the quiet-NaN pattern
-into it, and the normal build writes it nowhere (its kernels are untouched).
-Host-only: hipcc emits the device assembly without a GPU."""
+"""The diagnostic builds are not vacuous and leave the normal build alone.
+Compiled for gfx950 with SGEMM_LDS_POISON=1, every kernel that reads LDS writes
+the quiet-NaN pattern into it; with SGEMM_TIMELINE=1, every direct-load kernel
+reads the shader clock and no other kernel does.  The normal build contains
+neither.  Host-only: hipcc emits the device assembly without a GPU."""
 import os
 import re
 import subprocess
@@ -11,6 +12,7 @@ import pytest
 from fp32_gemm_sgemm_amd import build
 
 NAN_BITS = "0x7fc00000"
+DL_KERNEL = "sgemm_mfma_dl_kernel"
 
 
 def start_device_asm(out, defines=()):
@@ -36,15 +38,17 @@ def builds(tmp_path_factory):
     if not os.path.exists(build.HIPCC):
         pytest.skip("hipcc not available")
     tmp = tmp_path_factory.mktemp("asm")
-    outs = [str(tmp / "normal.s"), str(tmp / "poison.s")]
-    jobs = [start_device_asm(outs[0]), start_device_asm(outs[1], ["-DSGEMM_LDS_POISON=1"])]
-    for j in jobs:
-        assert j.wait() == 0, "hipcc failed"
-    return tuple(kernels(open(o).read()) for o in outs)
+    names = {"normal": (), "poison": ("-DSGEMM_LDS_POISON=1",),
+             "timeline": ("-DSGEMM_TIMELINE=1",)}
+    jobs = {n: (str(tmp / f"{n}.s"), start_device_asm(str(tmp / f"{n}.s"), d))
+            for n, d in names.items()}
+    for n, (_, j) in jobs.items():
+        assert j.wait() == 0, f"hipcc failed for the {n} build"
+    return {n: kernels(open(path).read()) for n, (path, _) in jobs.items()}
 
 
 def test_every_lds_kernel_is_poisoned(builds):
-    normal, poisoned = builds
+    normal, poisoned = builds["normal"], builds["poison"]
     assert set(normal) == set(poisoned)
     lds_kernels = [k for k, body in poisoned.items() if re.search(r"\bds_read", body)]
     assert len(lds_kernels) >= 20
@@ -54,6 +58,27 @@ def test_every_lds_kernel_is_poisoned(builds):
 
 
 def test_normal_build_carries_no_poison(builds):
-    normal, _ = builds
-    for k, body in normal.items():
+    for k, body in builds["normal"].items():
         assert NAN_BITS not in body, k
+
+
+def test_timeline_build_reads_the_clock_in_every_direct_load_kernel(builds):
+    """Entry, loop start, two readings per slice, loop end and the end: at
+    least four clock readings in each direct-load kernel, none elsewhere."""
+    normal = builds["normal"]
+    # the timeline build adds its two device arrays to the labels
+    timeline = {k: b for k, b in builds["timeline"].items() if "g_tl_" not in k}
+    assert set(normal) == set(timeline)
+    dl = [k for k in timeline if DL_KERNEL in k]
+    assert len(dl) >= 40
+    for k, body in timeline.items():
+        n = len(re.findall(r"\bs_memtime\b", body))
+        if DL_KERNEL in k:
+            assert n >= 4, f"{k}: {n} clock readings"
+        else:
+            assert n == 0, k
+
+
+def test_normal_build_reads_no_clock(builds):
+    for k, body in builds["normal"].items():
+        assert not re.search(r"\bs_memtime\b", body), k
