@@ -154,16 +154,37 @@ def measure(M, N, K, variant=None, warm_ms=200.0, seed=0, batch=1, transa=0, tra
         binding._check(lib.sgemm_f32_timeline_clear(), "sgemm_f32_timeline_clear")
         call()
         torch.cuda.synchronize()
-    phase, sl = read(lib)
-    return cfg, phase, sl, clock_khz(lib)
+        phase, sl = read(lib)
+        timed_us = call_us(torch, call)
+    with binding.library(binding.LIB_PATH):  # the same plan through the normal build
+        normal_us = call_us(torch, call, warm_ms)
+    return cfg, phase, sl, clock_khz(lib), (normal_us, timed_us)
+
+
+def call_us(torch, call, warm_ms=0.0, n=50):
+    """Mean time of n back-to-back calls (HIP events), after about warm_ms of
+    calls."""
+    end = time.perf_counter() + warm_ms / 1e3
+    while time.perf_counter() < end:
+        call()
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
 
 
 def report(M, N, K, variant=None, batch=1, transa=0, transb=0):
-    cfg, phase, sl, khz = measure(M, N, K, variant, batch=batch, transa=transa, transb=transb)
+    cfg, phase, sl, khz, (normal_us, timed_us) = measure(M, N, K, variant, batch=batch,
+                                                         transa=transa, transb=transb)
     lay = ("T" if transa else "N") + ("T" if transb else "N")
     r = {"shape": [M, N, K], "batch": batch, "layout": lay, "variant": cfg.id,
          "tile": f"{cfg.bm}x{cfg.bn}x{cfg.bk}",
-         "waves": cfg.threads // 64, "grid": cfg.grid, "strips": [cfg.strip_m, cfg.strip_n]}
+         "waves": cfg.threads // 64, "grid": cfg.grid, "strips": [cfg.strip_m, cfg.strip_n],
+         "call_us_normal": round(normal_us, 2), "call_us_timeline": round(timed_us, 2)}
     r.update(summarize(cfg, K, phase, sl, khz))
     return r
 
@@ -204,12 +225,15 @@ def markdown(rows, command):
         g = lambda q: " / ".join(f"{v:g}" for v in q)
         out += ["", "From the device's real-time counter (microseconds after the call's first",
                 "workgroup started; the shader clock's rate is each workgroup's cycles over its",
-                "real time):", "",
-                "| product | shader clock GHz (10th / 50th / 90th) | call span us | workgroup starts (median / 90th / last) | workgroup ends (first / median / last) |",
-                "|---|---|---|---|---|"]
+                "real time), and the mean time of 50 back-to-back calls of the same plan through",
+                "the normal build and through the timeline build (the readings' own cost):", "",
+                "| product | shader clock GHz (10th / 50th / 90th) | call span us | workgroup starts (median / 90th / last) | workgroup ends (first / median / last) | call us, normal / timeline build |",
+                "|---|---|---|---|---|---|"]
         for r in rt:
+            cu = (f"{r['call_us_normal']:g} / {r['call_us_timeline']:g}"
+                  if "call_us_normal" in r else "")
             out.append(f"| {name(r)} | {g(r['clock_ghz'])} | {r['call_span_us']:g} | "
-                       f"{g(r['start_us'])} | {g(r['end_us'])} |")
+                       f"{g(r['start_us'])} | {g(r['end_us'])} | {cu} |")
     return "\n".join(out) + "\n"
 
 

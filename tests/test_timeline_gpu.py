@@ -48,7 +48,8 @@ def test_timeline_build_computes_the_same_results(ta, tb):
                                        (300, 200, 64, 11)])
 def test_readings_are_consistent(M, N, K, vid):
     note(f"timeline readings {M}x{N}x{K} variant {vid}")
-    cfg, phase, sl, khz = timeline.measure(M, N, K, vid, warm_ms=5.0, seed=vid)
+    cfg, phase, sl, khz, (normal_us, timed_us) = timeline.measure(M, N, K, vid, warm_ms=5.0, seed=vid)
+    assert normal_us > 0 and timed_us > 0
     nwg = cfg.grid
     ph = phase[:nwg].astype(np.int64)
     assert (ph[:, 0] > 0).all(), "a workgroup left no readings"
