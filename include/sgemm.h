@@ -30,7 +30,8 @@ extern "C" {
 #endif
 
 /* Kernel families. */
-#define SGEMM_KERNEL_MFMA 0 /* matrix cores: v_mfma_f32_32x32x2_f32 */
+#define SGEMM_KERNEL_MFMA 0 /* matrix cores: v_mfma_f32_32x32x2_f32 (v_mfma_f32_16x16x4_f32
+                               for the four-stage 64 x 64 tiles) */
 #define SGEMM_KERNEL_VALU 1 /* vector FMA, kept only as a measured comparison */
 
 /* Operand layouts (transa, transb). */
