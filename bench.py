@@ -7,11 +7,14 @@ the FP32 matrix peak.
 A step is one C = A x B call through the library's C ABI at the headline
 workload, M = N = K = 8192, row-major, A and B i.i.d. U[-1, 1] drawn with seed
 4 (synthetic data; inputs are resident in HBM before timing starts).  W
-untimed warm-up steps are followed by exactly K timed steps, bracketed by
-device synchronisation, with HIP events recorded on the launch stream around
-each step.  TFLOP/s = 2*M*N*K / t ("4.1 CUDA GEMM operator performance
-optimization", section 1.3).  By default the operands stay cached between
-steps (warm); --cold writes 512 MiB between steps, outside the step's events.  A second workload, 3072^3 with N(0, 1) inputs
+untimed warm-up steps are followed by exactly K timed steps back to back,
+bracketed by device synchronisation, with one pair of HIP events recorded on
+the launch stream around them; a second pass of K steps, each between its
+own events, gives the per-step distribution (median, min, p90) and the
+roofline's mean launch time.  TFLOP/s = 2*M*N*K / t ("4.1 CUDA GEMM operator
+performance optimization", section 1.3).  By default the operands stay cached
+between steps (warm); --cold writes 512 MiB between steps, outside the step's
+events, and takes the value from the per-step events.  A second workload, 3072^3 with N(0, 1) inputs
 (seed 2), is timed the same way and reported under "secondary"; its launches
 are only ~0.45 ms, so it is warmed for at least --secondary-warm-ms of GPU
 time (the chip takes about 0.1 s of sustained load to reach its full clock;
@@ -138,6 +141,24 @@ def time_workload(torch, sg, w, steps, warmup, cfg=None, cold=False):
     for _ in range(warmup):
         sg.sgemm(A, B, out=C, stream=stream, cfg=cfg)
     torch.cuda.synchronize()
+    # the timed region: `steps` calls back to back between two synchronisations,
+    # one event pair around all of them (events between the calls would put a
+    # barrier packet between the kernels); with --cold each step is bracketed
+    # by its own events instead, so that the cache flush stays outside them
+    region_ms, wall_s = None, None
+    if flush is None:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(steps):
+            sg.sgemm(A, B, out=C, stream=stream, cfg=cfg)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall_s = time.perf_counter() - t0
+        region_ms = e0.elapsed_time(e1)
+    # the per-step distribution: a second pass of `steps` calls, each between
+    # its own pair of events
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     torch.cuda.synchronize()
@@ -149,10 +170,11 @@ def time_workload(torch, sg, w, steps, warmup, cfg=None, cold=False):
         sg.sgemm(A, B, out=C, stream=stream, cfg=cfg)
         ends[i].record(stream)
     torch.cuda.synchronize()
-    wall_s = time.perf_counter() - t0
+    if wall_s is None:
+        wall_s = time.perf_counter() - t0
+        region_ms = starts[0].elapsed_time(ends[-1])
     del flush
     per_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
-    region_ms = starts[0].elapsed_time(ends[-1])
     return {
         "A": A_np, "B": B_np, "C": C,
         "region_ms": region_ms, "wall_s": wall_s,
