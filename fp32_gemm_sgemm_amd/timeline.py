@@ -191,7 +191,7 @@ def report(M, N, K, variant=None, batch=1, transa=0, transb=0):
 
 def markdown(rows, command):
     out = ["# Inside the direct-load kernel: prologue, loop and stores (timeline build)", "",
-           "Command (from the repository root on the GPU box; committed files only):", "",
+           "Command (from the repository root, on the MI355X; committed files only):", "",
            "```", command, "```", "",
            "One call per product after 200 ms of identical warm-up calls (operands warm in the",
            "caches, the clock ramped up),",
