@@ -80,12 +80,14 @@ def summarize(cfg, K, phase, sl, khz=0):
     kk = cfg.k_chunk if cfg.splits > 1 else K
     nk = -(-kk // cfg.bk)
     ideal = cfg.bm * cfg.bn * nk * cfg.bk * 2 / FLOP_PER_CYCLE_PER_CU
+    if not len(ph):  # a plan on another kernel: no readings
+        return {"workgroups": 0, "slices": nk}
     pro, loop, epi = ph[:, 1] - ph[:, 0], ph[:, 2] - ph[:, 1], ph[:, 3] - ph[:, 2]
     out = {
         "workgroups": int(len(ph)), "slices": nk,
         "prologue": _q(pro), "loop": _q(loop), "stores": _q(epi), "total": _q(ph[:, 3] - ph[:, 0]),
         "loop_ideal": int(round(ideal)),
-        "loop_efficiency": round(ideal / float(np.median(loop)), 4) if len(ph) else None,
+        "loop_efficiency": round(ideal / float(np.median(loop)), 4),
     }
     if khz > 0 and len(ph) and (ph[:, 5] > ph[:, 4]).all():
         us = 1e3 / khz  # microseconds per real-time tick
@@ -213,6 +215,10 @@ def markdown(rows, command):
             m = f"{r['batch']} x {m}"
         return m if r["layout"] == "NN" else f"{m} {r['layout']}"
     for r in rows:
+        if not r["workgroups"]:
+            out.append(f"| {name(r)} | v{r['variant']} {r['tile']} (no readings: not the direct-load "
+                       "kernel) | 0 | | | | | | | | |")
+            continue
         per = f"{f(r['slice_period'])} ({r['slice_ideal']:,})" if "slice_period" in r else ""
         out.append(
             f"| {name(r)} | v{r['variant']} {r['tile']}, "

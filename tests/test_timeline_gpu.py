@@ -91,3 +91,20 @@ def test_other_kernels_record_nothing():
         check_general(C, A, B, 0, 0)
         phase, sl = timeline.read(lib)
         assert not phase.any() and not sl.any(), vid
+
+
+def test_command_line_summary(tmp_path):
+    """python -m fp32_gemm_sgemm_amd.timeline writes a summary with both tables
+    for a forced plan, a batched and transposed default plan, and a plan on
+    the K-split 32 x 32 tiles (a row without readings)."""
+    out = tmp_path / "summary.md"
+    note("timeline command line")
+    assert timeline.main(["--out", str(out), "--shape", "256", "256", "96", "20",
+                          "--shape", "640", "384", "512", "-1", "4", "0", "1",
+                          "--shape", "300", "200", "64", "16"]) == 0
+    md = out.read_text()
+    assert "| 256x256x96 | v20 64x64x32, 4 waves" in md
+    assert "| 4 x 640x384x512 NT | v20 64x64x32" in md
+    assert "| 300x200x64 | v16 32x32x8 (no readings" in md
+    assert "call us, normal / timeline build" in md
+    assert "--shape 256 256 96 20 --shape 640 384 512 -1 4 0 1 --shape 300 200 64 16" in md
