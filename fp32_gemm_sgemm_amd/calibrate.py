@@ -191,12 +191,14 @@ def calibrate_ksplit(torch, sg, vid, warm_ms, floor):
       BN) one slice deep and at K = 2048, where the operands one XCD reads
       stay in its L2;
     - its rate over four rounds (32 BM x 32 BN, K = 1024) with that fixed cost;
-    - its spill factors from the one-round and four-round shapes at K = 4096,
-      where those operands do not fit;
+    - its spill factors from the one-round and four-round shapes at K = 4096
+      (32 x 32 tiles) or 8192 (16 x 16 tiles), where those operands do not
+      fit: the operand rows and columns one XCD's tiles read are as many
+      bytes for either tile;
     - its rate on unaligned rows where these tiles serve: a few tiles with
-      long K (4 BM - 5 x 4 BN - 5, K = 16387, 16 tiles, spilled), the spill
-      factor taken out, stored scaled by full / one as the model scales it
-      back for one round."""
+      long K (4 BM - 5 x 4 BN - 5, 16 tiles, K = 16387 or 32771, spilled as
+      above), the spill factor taken out, stored scaled by full / one as the
+      model scales it back for one round."""
     v = sg.sgemm_f32_variant(vid)
     bm, bn, bk = v.bm, v.bn, v.bk
     co = v.coresident
@@ -213,22 +215,23 @@ def calibrate_ksplit(torch, sg, vid, warm_ms, floor):
     e_full = eff_from_time(t - floor, bm, bn, bk, M, N, K, fixed, co)
     out["full"] = round(e_full)
     _record(vid, v, "full", M, N, K, t, e_full)
-    slices = -(-4096 // bk)
-    t4k = _forced(torch, sg, vid, M1, N1, 4096, warm_ms)
+    k_spill = 4096 * 32 // bm
+    slices = -(-k_spill // bk)
+    t4k = _forced(torch, sg, vid, M1, N1, k_spill, warm_ms)
     spill = (t4k - floor - fixed) / (slices * slice_ns(bm, bn, bk, e_one))
     out["spill"] = round(1000.0 * spill)
     M4, N4 = 32 * bm, 32 * bn
     tiles4 = (M4 // bm) * (N4 // bn)
     rounds = -(-tiles4 // CUS)
     waves = -(-tiles4 // (CUS * co)) if co > 1 else rounds
-    t4k_full = _forced(torch, sg, vid, M4, N4, 4096, warm_ms)
+    t4k_full = _forced(torch, sg, vid, M4, N4, k_spill, warm_ms)
     out["spill_full"] = round(1000.0 * ((t4k_full - floor - waves * fixed) / rounds) /
                               (slices * slice_ns(bm, bn, bk, e_full)))
-    print(json.dumps({"variant": vid, "shape": "spill", "M": [M1, M4], "N": [N1, N4], "K": 4096,
+    print(json.dumps({"variant": vid, "shape": "spill", "M": [M1, M4], "N": [N1, N4], "K": k_spill,
                       "us": [round(t4k / 1e3, 2), round(t4k_full / 1e3, 2)],
                       "fixed_ns": out["fixed"], "spill_permille": out["spill"],
                       "spill_full_permille": out["spill_full"]}), flush=True)
-    M, N, K = 4 * bm - 5, 4 * bn - 5, 16387
+    M, N, K = 4 * bm - 5, 4 * bn - 5, 16384 * 32 // bm + 3
     t = _forced(torch, sg, vid, M, N, K, warm_ms)
     e = eff_from_time(t - floor, bm, bn, bk, M, N, K, fixed, co) * spill
     out["unaligned"] = round(e * e_full / e_one)

@@ -68,8 +68,8 @@ constexpr int kMaxDim = INT_MAX - 1024;
 // thread inside one slice stay below 2^32, for up to 256 rows of a
 // k-contiguous operand (A, or a transposed B) and 32 rows of an
 // index-contiguous one (B, or a transposed A).  Beyond them the selector
-// keeps to the variants that address in 64 bits (ld64: the 32 x 32 tiles that
-// split K over their waves) and to the strip kernel.
+// keeps to the variants that address in 64 bits (ld64: the 32 x 32 and 16 x 16
+// tiles that split K over their waves) and to the strip kernel.
 constexpr int kMaxLdK = (1 << 22) - 64;
 constexpr int kMaxLdX = (1 << 25) - 512;
 // Direct global -> LDS loads keep those offsets below 2^31 (the offset given
@@ -449,9 +449,22 @@ inline int strip_candidates(int d, int b, int (&out)[2])
     return 1;
 }
 
+// Whether block q can split K across workgroups within `workspace_bytes`.
+inline bool can_split(const Problem &q, long long workspace_bytes)
+{
+    int splits, k_chunk;
+    split_k(q.K, 2, splits, k_chunk);
+    return splits > 1 && split_workspace_bytes(q, splits) <= workspace_bytes;
+}
+
 // The fastest (variant, split count, strips) by the cost model among the
 // variants compiled for the operand layout whose workspace fits in
 // `workspace_bytes`.  Returns id -1 if no variant serves the layout.
+// Tiles smaller than 32 x 32 (the 16 x 16 K-split ones) compete only where K
+// cannot be split across workgroups: they read twice the operand bytes per
+// flop of the 32 x 32 tiles, their rate depends on how many compute units
+// stream at once (which the model does not capture), and with a workspace a
+// split over larger tiles reaches the same parallelism at half the bytes.
 inline Choice select_plan(const Variant *vs, int n, const Problem &p, int cus, bool aligned16,
                           bool lds_ok, long long workspace_bytes)
 {
@@ -471,6 +484,7 @@ inline Choice select_plan(const Variant *vs, int n, const Problem &p, int cus, b
             for (int a = 0; a < nsm; ++a) {
                 for (int b = 0; b < nsn; ++b) {
                     const Problem q = main_block(p, sms[a], sns[b]);
+                    if (v.bm < 32 && q.M > 0 && q.N > 0 && can_split(q, workspace_bytes)) continue;
                     double ts = strip_ns(p, sms[a], sns[b], cus);
                     if (q.M == 0 || q.N == 0) {
                         ts -= kLaunchFloorNs;

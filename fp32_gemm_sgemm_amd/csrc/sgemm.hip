@@ -68,19 +68,20 @@ Variant dl_variant(int eff_permille, int eff_one_permille, int eff_unaligned_per
     return v;
 }
 
-// 32x32 tiles with K split across the W waves of the workgroup (every layout).
-// waves_m = W describes the waves (they share the tile and split K).
-template <int W>
+// MB x MB tiles (32x32 or 16x16 MFMA blocks) with K split across the W waves
+// of the workgroup (every layout).  waves_m = W describes the waves (they
+// share the tile and split K); bk is the k of one group of four MFMA steps.
+template <int W, int MB = 32>
 Variant sk_variant(int eff_permille, int eff_one_permille, int eff_unaligned_permille, int fixed_ns,
                    int spill_permille, int spill_full_permille, int coresident)
 {
-    typedef sgemm::SkTraits<W> T;
-    return Variant{SGEMM_KERNEL_MFMA, T::BM, T::BN, 8, W, 1, -1, 0, 0,
+    typedef sgemm::SkTraits<W, MB> T;
+    return Variant{SGEMM_KERNEL_MFMA, T::BM, T::BN, T::GK, W, 1, -1, 0, 0,
                    T::NT, (int)(T::LDS_FLOATS * sizeof(float)),
-                   {reinterpret_cast<const void *>(&sgemm::sgemm_mfma_sk_kernel<W, false, false>),
-                    reinterpret_cast<const void *>(&sgemm::sgemm_mfma_sk_kernel<W, true, false>),
-                    reinterpret_cast<const void *>(&sgemm::sgemm_mfma_sk_kernel<W, false, true>),
-                    reinterpret_cast<const void *>(&sgemm::sgemm_mfma_sk_kernel<W, true, true>)},
+                   {reinterpret_cast<const void *>(&sgemm::sgemm_mfma_sk_kernel<W, false, false, MB>),
+                    reinterpret_cast<const void *>(&sgemm::sgemm_mfma_sk_kernel<W, true, false, MB>),
+                    reinterpret_cast<const void *>(&sgemm::sgemm_mfma_sk_kernel<W, false, true, MB>),
+                    reinterpret_cast<const void *>(&sgemm::sgemm_mfma_sk_kernel<W, true, true, MB>)},
                    eff_permille, eff_one_permille, eff_unaligned_permille, fixed_ns,
                    spill_permille, spill_full_permille, coresident, 1};
 }
@@ -109,13 +110,15 @@ constexpr int kCrossSliceAgpr = 6;
 // `python -m fp32_gemm_sgemm_amd.calibrate` measures them; the figures below
 // come from such runs on MI355X (each family of related tiles from one run:
 // the 64x64 tiles together, the 4-byte-load tiles of 128x128 and up together),
-// with the launch floor every launch pays taken off each time.  The K-split 32x32 tiles carry four more numbers:
+// with the launch floor every launch pays taken off each time.  The K-split tiles carry four more numbers:
 // their fixed cost per tile in ns; the factors (x1000) by which a slice slows
 // once the operand rows and columns one XCD's tiles read exceed its L2, over
 // one round and over several (their rates are measured where those fit); and
 // how many of their workgroups share a CU (from their register use: 62, 72
-// and 72 per lane for W = 4, 8, 16 in the NN layout, so 8, 3 and 1), whose
-// fixed costs overlap.  The others use the model's common 2.5 us, no spill
+// and 72 per lane for the 32x32 tiles with W = 4, 8, 16 in the NN layout, so
+// 8, 3 and 1; 48 for the 16x16 ones, so 4 and 2 for W = 8 and 16 at 8 waves
+// per SIMD), whose fixed costs overlap.  The selector offers the 16x16 tiles
+// only where K cannot be split across workgroups.  The others use the model's common 2.5 us, no spill
 // term and one fixed cost per round.
 // The 64x64 tiles carry their own fixed cost (--fit-fixed).  The two-stage
 // 32-deep ones are rated over one round at K = 4096, where the operands one
@@ -149,6 +152,8 @@ const Variant kVariants[] = {
     dl_variant<256, 256, 16, 4, 2, 2, kAllOps, true, kCrossSliceAgpr>(932, 955, 927),  // 19: 4-byte direct loads, 16-deep slices
     dl_variant<64, 64, 32, 2, 2, 4, kAllOps, false, kCrossSliceAgpr, 16>(906, 868, 371, 3900),  // 20: direct loads, 4 stages, 16x16 blocks
     dl_variant<64, 64, 32, 2, 2, 4, kAllOps, true, kCrossSliceAgpr, 16>(894, 770, 894, 4455),   // 21: 4-byte direct loads, 4 stages, 16x16 blocks
+    sk_variant<16, 16>(293, 365, 256, 3048, 1195, 866, 2),    // 22: 16x16, K split over 16 waves
+    sk_variant<8, 16>(309, 455, 251, 3056, 1410, 909, 4),     // 23: 16x16, K split over 8 waves
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 

@@ -8,15 +8,19 @@
 // here K is split across the W waves of one workgroup instead, so the partial
 // results meet in LDS:
 //
-//  * a workgroup owns one 32x32 tile of C (one v_mfma_f32_32x32x2_f32 block),
-//    four times as many tiles as 64x64 ones;
-//  * wave w accumulates the tile over its own K range (a multiple of 8), its
-//    fragments loaded straight from global memory into registers: for the MFMA
-//    step t of an 8-deep group, lanes 0-31 give k = t and lanes 32-63 k = 4+t,
-//    so a lane's four A values (and B values) of a group are 4 successive k of
-//    one row or column: one 16-byte load for an operand stored k-contiguous
-//    (A, or a transposed B), four 4-byte loads that 32 lanes make into one
-//    128-byte row segment for an operand stored index-contiguous (B, or a
+//  * a workgroup owns one MB x MB tile of C: one v_mfma_f32_32x32x2_f32 block
+//    (MB = 32, four times as many tiles as 64x64 ones) or one
+//    v_mfma_f32_16x16x4_f32 block (MB = 16, four times as many again, for
+//    outputs too small to give every compute unit a 32x32 tile);
+//  * wave w accumulates the tile over its own K range (a multiple of the group
+//    depth GK = 8 or 16), its fragments loaded straight from global memory into
+//    registers: for the MFMA step t of a group, lane l gives k = 4h + t of the
+//    group, h = l / MB (the half or quarter of the wave whose values the MFMA
+//    contracts), so a lane's four A values (and B values) of a group are 4
+//    successive k of one row or column: one 16-byte load for an operand stored
+//    k-contiguous
+//    (A, or a transposed B), four 4-byte loads that the MB lanes of a block
+//    make into one row segment for an operand stored index-contiguous (B, or a
 //    transposed A);
 //  * the W partial tiles are added through LDS in wave order, so a result is
 //    the same on every run, and written with alpha/beta like the other
@@ -28,29 +32,35 @@
 // N-1 (in bounds, never stored); k past the wave's range reads as zero.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace sgemm {
 
-template <int W> struct SkTraits {
-    static constexpr int BM = 32, BN = 32;
+template <int W, int MB = 32> struct SkTraits {
+    static_assert(MB == 32 || MB == 16, "32x32x2 or 16x16x4 blocks");
+    static constexpr int BM = MB, BN = MB;
+    static constexpr int REGS = MB == 32 ? 16 : 4;  // accumulators per lane
+    static constexpr int GK = MB == 32 ? 8 : 16;    // k of one group (4 MFMA steps)
     static constexpr int NT = W * 64;
-    static constexpr int LDS_FLOATS = W * 16 * 64;
-    static constexpr int DEPTH = 4;  // 8-deep k groups in flight per wave
+    static constexpr int LDS_FLOATS = W * REGS * 64;
+    static constexpr int DEPTH = 4;  // k groups in flight per wave
 };
 
-template <int W, bool TA, bool TB>
+template <int W, bool TA, bool TB, int MB = 32>
 __global__ void __launch_bounds__(W * 64) sgemm_mfma_sk_kernel(GemmArgs g)
 {
-    typedef SkTraits<W> T;
-    constexpr int D = T::DEPTH;
+    typedef SkTraits<W, MB> T;
+    constexpr int D = T::DEPTH, REGS = T::REGS, GK = T::GK;
+    typedef typename std::conditional<MB == 32, f32x16, f32x4>::type acc_t;
     __shared__ __attribute__((aligned(16))) float red[T::LDS_FLOATS];
 
     if constexpr (kLdsPoison) {
         // LDS race check build: the partial-tile area starts as NaN everywhere
         const int w0 = threadIdx.x >> 6, l0 = threadIdx.x & 63;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) lds_poison(&red[(w0 * 16 + r) * 64 + l0], 1);
+        for (int r = 0; r < REGS; ++r) lds_poison(&red[(w0 * REGS + r) * 64 + l0], 1);
         lds_poison_done();
         __syncthreads();
     }
@@ -60,19 +70,19 @@ __global__ void __launch_bounds__(W * 64) sgemm_mfma_sk_kernel(GemmArgs g)
     const float *__restrict__ A = g.A;
     const float *__restrict__ B = g.B;
     const int M = g.M, N = g.N, K = g.K, lda = g.lda, ldb = g.ldb;
-    const int m0 = wk.tm * 32, n0 = wk.tn * 32;
+    const int m0 = wk.tm * MB, n0 = wk.tn * MB;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l31 = lane & 31, h = lane >> 5;
+    const int l31 = lane & (MB - 1), h = MB == 32 ? lane >> 5 : lane >> 4;
 
-    // this wave's K range [kb, ke): nfull whole 8-deep groups, then rem < 8
-    // more k (only in the last wave, when K is not a multiple of 8)
-    const int kc = (((K + W - 1) / W) + 7) & ~7;
+    // this wave's K range [kb, ke): nfull whole groups, then rem < GK more k
+    // (only in the last wave, when K is not a multiple of GK)
+    const int kc = (((K + W - 1) / W) + GK - 1) & ~(GK - 1);
     const int kb = wave * kc;
     const int ke = min(K, kb + kc);
     const int len = ke > kb ? ke - kb : 0;
-    const int nfull = len >> 3;
-    const int rem = len & 7;
+    const int nfull = len / GK;
+    const int rem = len % GK;
 
     const int ia = min(m0 + l31, M - 1);  // row of op(A) this lane feeds
     const int jb = min(n0 + l31, N - 1);  // column of op(B) this lane feeds
@@ -85,12 +95,12 @@ __global__ void __launch_bounds__(W * 64) sgemm_mfma_sk_kernel(GemmArgs g)
     struct Frag {
         f32x4 a, b;
     };
-    // whole group q of this wave: k = kb + 8q + 4h + t, t = 0..3.  The loop
+    // whole group q of this wave: k = kb + GK q + 4h + t, t = 0..3.  The loop
     // below has no branch and no lane-dependent condition, so the compiler
     // waits for each group's loads alone, with the later groups still in
     // flight.
     auto load = [&](int q, Frag &f) {
-        const int k = kb + 8 * q + 4 * h;
+        const int k = kb + GK * q + 4 * h;
         if constexpr (!TA) f.a = *reinterpret_cast<const f32x4u *>(pa + k);
         else {
 #pragma unroll
@@ -102,13 +112,17 @@ __global__ void __launch_bounds__(W * 64) sgemm_mfma_sk_kernel(GemmArgs g)
             for (int t = 0; t < 4; ++t) f.b[t] = pb[(int64_t)(k + t) * sb];
         }
     };
-    f32x16 acc;
+    acc_t acc;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    for (int r = 0; r < REGS; ++r) acc[r] = 0.0f;
     auto mma = [&](const Frag &f) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[t], f.b[t], acc, 0, 0, 0);
+        for (int t = 0; t < 4; ++t) {
+            if constexpr (MB == 32)
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[t], f.b[t], acc, 0, 0, 0);
+            else
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(f.a[t], f.b[t], acc, 0, 0, 0);
+        }
     };
 
     if (nfull > 0) {
@@ -133,7 +147,7 @@ __global__ void __launch_bounds__(W * 64) sgemm_mfma_sk_kernel(GemmArgs g)
     }
     if (rem > 0) {
         // the ragged group: k past ke reads a clamped address and becomes 0
-        const int k = kb + 8 * nfull + 4 * h;
+        const int k = kb + GK * nfull + 4 * h;
         Frag f;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -148,18 +162,19 @@ __global__ void __launch_bounds__(W * 64) sgemm_mfma_sk_kernel(GemmArgs g)
     // partial tiles -> LDS as [wave][register][lane]; then each thread adds
     // the W partials of its outputs in wave order
 #pragma unroll
-    for (int r = 0; r < 16; ++r) red[(wave * 16 + r) * 64 + lane] = acc[r];
+    for (int r = 0; r < REGS; ++r) red[(wave * REGS + r) * 64 + lane] = acc[r];
     __syncthreads();
     float *__restrict__ C = g.C;
     const int ldc = g.ldc;
-    for (int o = tid; o < 16 * 64; o += W * 64) {
+    for (int o = tid; o < REGS * 64; o += W * 64) {
         const int r = o >> 6, ln = o & 63;
         float s = red[r * 64 + ln];
 #pragma unroll
-        for (int w = 1; w < W; ++w) s += red[(w * 16 + r) * 64 + ln];
-        // register r of lane ln holds D[8*(r/4) + 4*(ln/32) + r%4][ln%32]
-        const int row = m0 + 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
-        const int col = n0 + (ln & 31);
+        for (int w = 1; w < W; ++w) s += red[(w * REGS + r) * 64 + ln];
+        // register r of lane ln holds D[8*(r/4) + 4*(ln/32) + r%4][ln%32] of a
+        // 32x32 block, D[4*(ln/16) + r][ln%16] of a 16x16 one
+        const int row = m0 + (MB == 32 ? 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3) : 4 * (ln >> 4) + r);
+        const int col = n0 + (ln & (MB - 1));
         if (row < M && col < N) {
             float *p = C + (int64_t)row * ldc + col;
             *p = g.beta != 0.0f ? g.alpha * s + g.beta * *p : g.alpha * s;

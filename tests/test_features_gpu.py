@@ -56,21 +56,23 @@ def test_transposed_layouts_every_variant(ta, tb):
 
 def _ksplit_variants():
     return [v for v in range(sg.sgemm_f32_num_variants())
-            if (sg.sgemm_f32_variant(v).bm, sg.sgemm_f32_variant(v).bk) == (32, 8)]
+            if (sg.sgemm_f32_variant(v).bm, sg.sgemm_f32_variant(v).bk) in ((32, 8), (16, 16))]
 
 
 @pytest.mark.parametrize("ta,tb", LAYOUTS)
 def test_ksplit_tiles_k_ranges(ta, tb):
-    """The tiles that split K over their W waves: each wave takes a range of
-    whole 8-deep groups and keeps four groups of loads in flight (prefetch
-    clamped to its last whole group); the last wave may end in a ragged
-    group.  K values cover a single k, one ragged group, exactly one group per
-    wave, one k more or less, waves left with no range (K below 8 (W - 1)),
-    whole prefetch blocks plus a remainder, and ragged M and N."""
+    """The tiles that split K over their W waves (32 x 32 tiles in 8-deep
+    groups, 16 x 16 ones in 16-deep groups): each wave takes a range of whole
+    G-deep groups and keeps four groups of loads in flight (prefetch clamped
+    to its last whole group); the last wave may end in a ragged group.  K
+    values cover a single k, one ragged group, exactly one group per wave, one
+    k more or less, waves left with no range (K below G (W - 1)), whole
+    prefetch blocks plus a remainder, and ragged M and N."""
     for vid in _ksplit_variants():
         W = sg.sgemm_f32_variant(vid).waves_m
-        ks = sorted({1, 3, 7, 8, 9, 8 * W - 1, 8 * W, 8 * W + 1, 8 * (W - 1) - 3,
-                     8 * W * 4 * 2 + 5, 8 * W * 4 * 3 + 8 * 3, 8 * W * 5 + 17} - {0})
+        G = sg.sgemm_f32_variant(vid).bk
+        ks = sorted({1, 3, G - 1, G, G + 1, G * W - 1, G * W, G * W + 1, G * (W - 1) - 3,
+                     G * W * 4 * 2 + 5, G * W * 4 * 3 + G * 3, G * W * 5 + 17} - {0})
         for K in ks:
             if K <= 0:
                 continue
@@ -86,8 +88,9 @@ def test_random_problems_through_the_selector():
     skinny with long K and wide with short K, half with sizes that are
     multiples of 4; random layout, alpha/beta, workspace or none, padded
     strides and 4-byte shifted starts.  The plans this reaches include the
-    K-split 32 x 32 tiles (with and without an outer split), the 64 x 64
-    tiles with 32- and 64-deep slices and edge strips."""
+    K-split 32 x 32 tiles (with and without an outer split), the K-split
+    16 x 16 tiles, the 64 x 64 tiles with 32- and 64-deep slices and edge
+    strips."""
     rng = np.random.default_rng(20261202)
     for case in range(100):
         kind = rng.integers(0, 4)
@@ -149,7 +152,7 @@ def test_alpha_beta(alpha, beta):
     A, B = inputs.make_operands(M, N, K, seed=100)
     C0 = inputs.make_operands(M, N, 1, seed=101)[0][:, :1] * np.linspace(-1, 1, N, dtype=np.float32)
     C0 = np.ascontiguousarray(C0.astype(np.float32))
-    for vid in (None, 1, 2, 3, 4, 5, 6, 14, 15, 16, 17, 18):
+    for vid in (None, 1, 2, 3, 4, 5, 6, 14, 15, 16, 17, 18, 22, 23):
         note(f"alpha={alpha} beta={beta} variant {vid}")
         cfg = None if vid is None else forced(vid)
         C = run_general(A, B, 0, 0, alpha, beta, C0, cfg=cfg)
@@ -172,7 +175,7 @@ def test_beta_zero_ignores_nan_and_k_zero_scales():
     assert np.array_equal(C, (np.float32(-0.5) * C0).astype(np.float32))
 
 
-SPLIT_VARIANTS = [1, 2, 3, 4, 5, 6, 14, 15, 16, 17, 18]
+SPLIT_VARIANTS = [1, 2, 3, 4, 5, 6, 14, 15, 16, 17, 18, 22, 23]
 
 
 @pytest.mark.parametrize("K", [1000, 1001, 130])

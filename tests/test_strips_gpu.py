@@ -51,17 +51,23 @@ def test_forced_strips_every_layout(ta, tb):
                                    (1000, 1, 4100), (700, 3, 9301), (2, 2, 4100), (1, 1, 1),
                                    (4, 33, 4608)])
 def test_strip_only_products(ta, tb, M, N, K):
-    """Products with at most 4 rows or columns go to the strip kernel alone
-    (no tiles), through the default selector; K within one staged chunk of
-    the small operand, exactly one, and past two."""
+    """Products with at most 4 rows or columns on the strip kernel alone (a
+    forced strip-only plan), and through the default selector, which runs
+    them on the strips or, without a workspace, on the 16 x 16 tiles that
+    split K over their waves; K within one staged chunk of the small operand,
+    exactly one, and past two."""
     A, B = inputs.make_operands(M, N, K, seed=310 + M + N)
     As, Bs = stored(A, ta), stored(B, tb)
     note(f"strip-only ta={ta} tb={tb} {M}x{N}x{K}")
-    C = run_general(As, Bs, ta, tb)
+    C = run_general(As, Bs, ta, tb, cfg=with_strips(4, M, 0) if M <= 4 else with_strips(4, 0, N))
+    check_general(C, As, Bs, ta, tb)
+    note(f"default plan ta={ta} tb={tb} {M}x{N}x{K}")
+    C = run_general(As, Bs, ta, tb, workspace=False)
     check_general(C, As, Bs, ta, tb)
     if K >= 4096:
         q = sg.sgemm_f32_plan(M, N, K, M if ta else K, K if tb else N, N, 256, ta, tb)
-        assert q.grid == 0 and (q.strip_m == M or q.strip_n == N)
+        strips = q.grid == 0 and (q.strip_m == M or q.strip_n == N)
+        assert strips or (q.bm == 16 and q.splits == 1), q.as_dict()
 
 
 @pytest.mark.parametrize("alpha,beta", [(1.5, -0.75), (-2.0, 0.0), (0.25, 2.0)])
@@ -181,9 +187,9 @@ def test_strip_only_batches_past_one_launch():
     assert rep["n_bad"] == 0, rep
 
 
-@pytest.mark.parametrize("vid", [14, 15, 16])
+@pytest.mark.parametrize("vid", [14, 15, 16, 22, 23])
 def test_ksplit_tiles_with_outer_splits_batches_and_strips(vid):
-    """The 32x32 tiles that split K over their waves, combined with a split
+    """The 32x32 and 16x16 tiles that split K over their waves, combined with a split
     across workgroups (workspace), batches with a broadcast operand, strips
     and alpha/beta, in every layout."""
     batch, M, N, K = 3, 67, 98, 1500
