@@ -22,11 +22,11 @@ and the cost model of select.hpp,
 is inverted for eff (x1000), the three numbers each variant carries in the
 table of sgemm.hip (printed at the end as table lines).  With --fit-fixed the
 listed variants get their own fixed cost in place of the 2.5 us (fit_fixed),
-a fourth number in their table line.  The variants that split K over their
-waves (32 x 32 tiles, whose L2 spill the model prices) also get their own
-fixed cost and
-spill factors (one round, several rounds), and are measured at K where the
-operands one XCD reads fit in its L2 (calibrate_ksplit); several of their
+a fourth number in their table line.  The variants that split K inside the
+workgroup (32 x 32, 16 x 16 and 8 x 8 tiles, whose L2 spill the model prices)
+also get their own fixed cost and spill factors (one round, several rounds),
+and are measured at K where the operands one XCD reads fit in its L2
+(calibrate_ksplit); several of their
 workgroups share a CU, and the model charges their fixed cost once per wave
 of co-resident workgroups.  The strip kernel is timed alone on 4-row products
 in both storage orders of its streamed operand: two sizes that fill the chip
@@ -191,14 +191,14 @@ def calibrate_ksplit(torch, sg, vid, warm_ms, floor):
       BN) one slice deep and at K = 2048, where the operands one XCD reads
       stay in its L2;
     - its rate over four rounds (32 BM x 32 BN, K = 1024) with that fixed cost;
-    - its spill factors from the one-round and four-round shapes at K = 4096
-      (32 x 32 tiles) or 8192 (16 x 16 tiles), where those operands do not
-      fit: the operand rows and columns one XCD's tiles read are as many
-      bytes for either tile;
+    - its spill factors from the one-round and four-round shapes at
+      K = 4096 * 32 / BM (4096, 8192 and 16384 for 32 x 32, 16 x 16 and
+      8 x 8 tiles), where those operands do not fit: the operand rows and
+      columns one XCD's tiles read are then as many bytes for every tile;
     - its rate on unaligned rows where these tiles serve: a few tiles with
-      long K (4 BM - 5 x 4 BN - 5, 16 tiles, K = 16387 or 32771, spilled as
-      above), the spill factor taken out, stored scaled by full / one as the
-      model scales it back for one round."""
+      long K (4 BM - 5 x 4 BN - 5, 16 tiles, K = 16384 * 32 / BM + 3, spilled
+      as above), the spill factor taken out, stored scaled by full / one as
+      the model scales it back for one round."""
     v = sg.sgemm_f32_variant(vid)
     bm, bn, bk = v.bm, v.bn, v.bk
     co = v.coresident
@@ -314,7 +314,7 @@ def main(argv=None):
     elif args.variants:
         vids = [int(x) for x in args.variants.split(",")]
     else:
-        vids = [i for i in range(sg.sgemm_f32_num_variants()) if _is_mfma(sg, i)]
+        vids = [i for i in range(sg.sgemm_f32_num_variants()) if _is_rated(sg, i)]
     floor = launch_floor(torch, sg, args.ms) if vids else 0.0
     fit = {int(x) for x in args.fit_fixed.split(",") if x}
     table = {}
@@ -341,10 +341,12 @@ def main(argv=None):
     return 0
 
 
-def _is_mfma(sg, vid):
-    """Matrix-core variants (the ones the table rates; the vector-FMA
-    comparison kernel is measured only when named with --variants)."""
-    return sg.sgemm_f32_variant(vid).kernel == sg.binding.SGEMM_KERNEL_MFMA
+def _is_rated(sg, vid):
+    """The variants the table rates: the matrix-core ones and the vector-FMA
+    tiles that split K (the vector-FMA comparison kernel is measured only
+    when named with --variants)."""
+    v = sg.sgemm_f32_variant(vid)
+    return v.kernel == sg.binding.SGEMM_KERNEL_MFMA or v.spill_full_permille > 0
 
 
 if __name__ == "__main__":

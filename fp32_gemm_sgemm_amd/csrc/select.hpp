@@ -32,7 +32,8 @@ struct Variant {
     int lds_bytes;
     const void *fn[4];  // kernel per operand layout, index transa + 2*transb (null: none)
     int eff_permille;   // measured steady-state fraction of the FP32 matrix peak
-                        // (x1000) over rounds of full tiles; 0 = never chosen by the selector
+                        // (x1000; the FP32 vector-FMA peak is the same figure) over
+                        // rounds of full tiles; 0 = never chosen by the selector
     int eff_one_permille;        // the same when the grid has at most one workgroup
                                  // per CU (no co-resident workgroups to hide latency)
     int eff_unaligned_permille;  // the same as eff_permille when rows are not
@@ -68,8 +69,8 @@ constexpr int kMaxDim = INT_MAX - 1024;
 // thread inside one slice stay below 2^32, for up to 256 rows of a
 // k-contiguous operand (A, or a transposed B) and 32 rows of an
 // index-contiguous one (B, or a transposed A).  Beyond them the selector
-// keeps to the variants that address in 64 bits (ld64: the 32 x 32 and 16 x 16
-// tiles that split K over their waves) and to the strip kernel.
+// keeps to the variants that address in 64 bits (ld64: the 32 x 32, 16 x 16
+// and 8 x 8 tiles that split K inside the workgroup) and to the strip kernel.
 constexpr int kMaxLdK = (1 << 22) - 64;
 constexpr int kMaxLdX = (1 << 25) - 512;
 // Direct global -> LDS loads keep those offsets below 2^31 (the offset given
@@ -449,6 +450,16 @@ inline int strip_candidates(int d, int b, int (&out)[2])
     return 1;
 }
 
+// The 8 x 8 vector-FMA tiles compete only from this K on, and not for
+// products of at most kStripMaxWidth rows or columns.  Below that K a call is
+// mostly fixed costs (theirs include a butterfly reduction across the wave),
+// which their one fixed-cost figure prices poorly once several share a CU:
+// measured on MI355X against the 16 x 16 tiles they would replace, 0.99-1.12
+// of the time (geometric mean by K) for K = 256-2048, 0.70-0.87 for K = 4096-
+// 65536.  Products of a few rows or columns waste most of an 8-row tile, and
+// against the strip kernel they took up to 1.5 times as long.
+constexpr int kVskMinK = 4096;
+
 // Whether block q can split K across workgroups within `workspace_bytes`.
 inline bool can_split(const Problem &q, long long workspace_bytes)
 {
@@ -460,11 +471,12 @@ inline bool can_split(const Problem &q, long long workspace_bytes)
 // The fastest (variant, split count, strips) by the cost model among the
 // variants compiled for the operand layout whose workspace fits in
 // `workspace_bytes`.  Returns id -1 if no variant serves the layout.
-// Tiles smaller than 32 x 32 (the 16 x 16 K-split ones) compete only where K
-// cannot be split across workgroups: they read twice the operand bytes per
-// flop of the 32 x 32 tiles, their rate depends on how many compute units
-// stream at once (which the model does not capture), and with a workspace a
-// split over larger tiles reaches the same parallelism at half the bytes.
+// Tiles smaller than 32 x 32 (the 16 x 16 and 8 x 8 K-split ones) compete
+// only where K cannot be split across workgroups: they read two and four
+// times the operand bytes per flop of the 32 x 32 tiles, their rate depends
+// on how many compute units stream at once (which the model does not
+// capture), and with a workspace a split over larger tiles reaches the same
+// parallelism with fewer bytes.
 inline Choice select_plan(const Variant *vs, int n, const Problem &p, int cus, bool aligned16,
                           bool lds_ok, long long workspace_bytes)
 {
@@ -474,7 +486,7 @@ inline Choice select_plan(const Variant *vs, int n, const Problem &p, int cus, b
     for (int pass = 0; pass < 2 && best.id < 0; ++pass) {
         for (int i = 0; i < n; ++i) {
             const Variant &v = vs[i];
-            if (v.kernel != SGEMM_KERNEL_MFMA || v.eff_permille <= 0 || v.eff_one_permille <= 0 ||
+            if (v.eff_permille <= 0 || v.eff_one_permille <= 0 ||
                 v.eff_unaligned_permille <= 0 || !v.fn[op] || !variant_fits(v, p))
                 continue;
             const int eff = variant_eff(v, aligned16, lds_ok, pass == 0);
@@ -485,6 +497,9 @@ inline Choice select_plan(const Variant *vs, int n, const Problem &p, int cus, b
                 for (int b = 0; b < nsn; ++b) {
                     const Problem q = main_block(p, sms[a], sns[b]);
                     if (v.bm < 32 && q.M > 0 && q.N > 0 && can_split(q, workspace_bytes)) continue;
+                    if (v.kernel == SGEMM_KERNEL_VALU &&
+                        (q.K < kVskMinK || p.M <= kStripMaxWidth || p.N <= kStripMaxWidth))
+                        continue;
                     double ts = strip_ns(p, sms[a], sns[b], cus);
                     if (q.M == 0 || q.N == 0) {
                         ts -= kLaunchFloorNs;

@@ -17,6 +17,7 @@
 #include "sgemm_mfma.hpp"
 #include "sgemm_mfma_dl.hpp"
 #include "sgemm_mfma_sk.hpp"
+#include "sgemm_valu_sk.hpp"
 #include "sgemm_reduce.hpp"
 #include "sgemm_strip.hpp"
 #include "sgemm_valu.hpp"
@@ -86,6 +87,23 @@ Variant sk_variant(int eff_permille, int eff_one_permille, int eff_unaligned_per
                    spill_permille, spill_full_permille, coresident, 1};
 }
 
+// 8x8 tiles with K split over the lane pairs and W waves of the workgroup,
+// on vector FMAs (every layout); bk is the k of one group (one per lane pair).
+template <int W>
+Variant vsk_variant(int eff_permille, int eff_one_permille, int eff_unaligned_permille, int fixed_ns,
+                    int spill_permille, int spill_full_permille, int coresident)
+{
+    typedef sgemm::VskTraits<W> T;
+    return Variant{SGEMM_KERNEL_VALU, T::BM, T::BN, T::GK, W, 1, -1, 0, 0,
+                   T::NT, (int)(T::LDS_FLOATS * sizeof(float)),
+                   {reinterpret_cast<const void *>(&sgemm::sgemm_valu_sk_kernel<W, false, false>),
+                    reinterpret_cast<const void *>(&sgemm::sgemm_valu_sk_kernel<W, true, false>),
+                    reinterpret_cast<const void *>(&sgemm::sgemm_valu_sk_kernel<W, false, true>),
+                    reinterpret_cast<const void *>(&sgemm::sgemm_valu_sk_kernel<W, true, true>)},
+                   eff_permille, eff_one_permille, eff_unaligned_permille, fixed_ns,
+                   spill_permille, spill_full_permille, coresident, 1};
+}
+
 Variant valu_variant()
 {
     typedef sgemm::ValuTraits T;
@@ -117,8 +135,10 @@ constexpr int kCrossSliceAgpr = 6;
 // how many of their workgroups share a CU (from their register use: 62, 72
 // and 72 per lane for the 32x32 tiles with W = 4, 8, 16 in the NN layout, so
 // 8, 3 and 1; 48 for the 16x16 ones, so 4 and 2 for W = 8 and 16 at 8 waves
-// per SIMD), whose fixed costs overlap.  The selector offers the 16x16 tiles
-// only where K cannot be split across workgroups.  The others use the model's common 2.5 us, no spill
+// per SIMD; 108 for the 8x8 vector-FMA tiles, so 4), whose fixed costs
+// overlap.  The selector offers the 16x16 and 8x8 tiles only where K cannot
+// be split across workgroups (the 8x8 ones also need K >= 4096 and more than
+// 4 rows and columns).  The others use the model's common 2.5 us, no spill
 // term and one fixed cost per round.
 // The 64x64 tiles carry their own fixed cost (--fit-fixed).  The two-stage
 // 32-deep ones are rated over one round at K = 4096, where the operands one
@@ -154,6 +174,7 @@ const Variant kVariants[] = {
     dl_variant<64, 64, 32, 2, 2, 4, kAllOps, true, kCrossSliceAgpr, 16>(894, 770, 894, 4455),   // 21: 4-byte direct loads, 4 stages, 16x16 blocks
     sk_variant<16, 16>(293, 365, 256, 3048, 1195, 866, 2),    // 22: 16x16, K split over 16 waves
     sk_variant<8, 16>(309, 455, 251, 3056, 1410, 909, 4),     // 23: 16x16, K split over 8 waves
+    vsk_variant<4>(108, 121, 76, 3032, 1022, 859, 4),         // 24: 8x8 vector FMA, K split over lane pairs and 4 waves
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 

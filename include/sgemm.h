@@ -32,7 +32,9 @@ extern "C" {
 /* Kernel families. */
 #define SGEMM_KERNEL_MFMA 0 /* matrix cores: v_mfma_f32_32x32x2_f32 (v_mfma_f32_16x16x4_f32
                                for the four-stage 64 x 64 tiles and the 16 x 16 tiles) */
-#define SGEMM_KERNEL_VALU 1 /* vector FMA, kept only as a measured comparison */
+#define SGEMM_KERNEL_VALU 1 /* vector FMA: the 8 x 8 tiles that split K over lane
+                               pairs and waves, and the 128 x 128 register-blocked
+                               tile kept only as a measured comparison */
 
 /* Operand layouts (transa, transb). */
 #define SGEMM_OP_N 0 /* the operand as stored, row-major */
@@ -43,10 +45,11 @@ typedef struct sgemm_cfg {
     int id;        /* variant index, 0 .. sgemm_f32_num_variants()-1 */
     int kernel;    /* SGEMM_KERNEL_MFMA or SGEMM_KERNEL_VALU */
     int bm, bn, bk;       /* workgroup tile: BM x BN outputs, BK-deep K slices */
-    int waves_m, waves_n; /* wavefront grid inside a workgroup (the 32 x 32 and
-                             16 x 16 variants that split K over their waves
-                             report waves_m = that count, waves_n = 1, and bk =
-                             the k of one group of four MFMA steps) */
+    int waves_m, waves_n; /* wavefront grid inside a workgroup (the 32 x 32,
+                             16 x 16 and 8 x 8 variants that split K inside the
+                             workgroup report waves_m = their wave count,
+                             waves_n = 1, and bk = the k of one group: four
+                             MFMA steps, or one k per lane pair) */
     int group_m;   /* raster: tile rows per group, walked column by column
                       (0 = plain row-major order over tiles) */
     int xcd_remap; /* 1: give each XCD a contiguous run of logical tiles */
@@ -96,8 +99,8 @@ typedef struct sgemm_cfg {
  * M, N, K, lda, ldb, ldc <= INT_MAX - 1024.  The LDS-tiled kernels use
  * 32-bit byte offsets inside one K slice and serve lda <= 2^22 - 64 and
  * ldb <= 2^25 - 512; larger leading dimensions run on the kernels that
- * address in 64 bits (the 32 x 32 and 16 x 16 tiles that split K over their
- * waves, and the edge-strip kernel), more slowly.
+ * address in 64 bits (the 32 x 32, 16 x 16 and 8 x 8 tiles that split K
+ * inside the workgroup, and the edge-strip kernel), more slowly.
  *
  * Semantics of degenerate sizes: M == 0 or N == 0 does nothing; K == 0 sets
  * the M x N block of C to zero (an empty sum).

@@ -117,17 +117,16 @@ def test_few_strip_workgroups_take_a_split_when_a_workspace_fits(lib, M, N, K, t
     """A product of at most 4 rows whose strips would run on a handful of
     workgroups (each covers all of K) is split across workgroups instead when
     a workspace allows it.  Without one, the plan needs none: the strips, or
-    16 x 16 tiles that split K over their waves (NN: twice the strip's
-    workgroups, 20-38% faster on MI355X at these sizes)."""
+    16 x 16 or 8 x 8 tiles that split K inside the workgroup (NN: more
+    workgroups than the strip; 16 x 16 ones were 20-38% faster on MI355X at
+    these sizes)."""
     ldb = K if tb else N
     q = sg.sgemm_f32_plan(M, N, K, K, ldb, N, 256, 0, tb, 1, 1 << 30)
     assert q.grid > 0 and q.splits > 1 and q.grid >= 64, q.as_dict()
     q = sg.sgemm_f32_plan(M, N, K, K, ldb, N, 256, 0, tb, 1, 0)
     assert q.splits == 1 and q.workspace_bytes == 0, q.as_dict()
-    if tb:
-        assert q.grid == 0 and q.strip_m == M, q.as_dict()
-    else:
-        assert q.bm == 16 and q.strip_m == 0, q.as_dict()
+    strips = q.grid == 0 and q.strip_m == M
+    assert strips or (q.bm in (8, 16) and q.strip_m == 0), q.as_dict()
 
 
 def test_no_undefined_own_symbols(lib):
@@ -149,18 +148,18 @@ def test_version_and_variants(lib):
         kinds.add(v.kernel)
         assert v.threads == 64 * v.waves_m * v.waves_n or v.kernel == sg.binding.SGEMM_KERNEL_VALU
         assert 0 < v.lds_bytes <= 160 * 1024
-        assert v.bm % 16 == 0 and v.bn % 16 == 0 and v.bk % 8 == 0
-        # tiles under 32 x 32 are the 16 x 16 ones that split K over their waves
-        assert v.bm % 32 == 0 or (v.bm, v.bn, v.bk) == (16, 16, 16)
+        assert v.bm % 8 == 0 and v.bn % 8 == 0 and v.bk % 8 == 0
+        # tiles under 32 x 32 are the 16 x 16 and 8 x 8 ones that split K
+        assert v.bm % 32 == 0 or (v.bm, v.bn, v.bk) in ((16, 16, 16), (8, 8, 32))
     assert kinds == {sg.binding.SGEMM_KERNEL_MFMA, sg.binding.SGEMM_KERNEL_VALU}
     # cost-model figures: every variant reports a fixed cost (2.5 us or its
-    # own); only the tiles that split K over their waves (32 x 32 x 8 and
-    # 16 x 16 x 16) price an L2 spill and overlap the fixed costs of
-    # co-resident workgroups
+    # own); only the tiles that split K inside the workgroup (32 x 32 x 8,
+    # 16 x 16 x 16, 8 x 8 x 32) price an L2 spill and overlap the fixed costs
+    # of co-resident workgroups
     for i in range(n):
         v = sg.sgemm_f32_variant(i)
         assert 0 < v.fixed_ns < 20000 and v.coresident >= 1
-        if (v.bm, v.bn, v.bk) in ((32, 32, 8), (16, 16, 16)):
+        if (v.bm, v.bn, v.bk) in ((32, 32, 8), (16, 16, 16), (8, 8, 32)):
             assert v.spill_permille > 0 and v.spill_full_permille > 0
             # LDS bounds the workgroups that can share a CU
             assert v.coresident * v.lds_bytes <= 160 * 1024
@@ -242,7 +241,7 @@ def test_large_leading_dimensions_go_to_64_bit_kernels(lib):
     refused."""
     lib_ = sg.load()
     ld64 = {i for i in range(sg.sgemm_f32_num_variants())
-            if (sg.sgemm_f32_variant(i).bm, sg.sgemm_f32_variant(i).bk) in ((32, 8), (16, 16))}
+            if (sg.sgemm_f32_variant(i).bm, sg.sgemm_f32_variant(i).bk) in ((32, 8), (16, 16), (8, 32))}
     big = (1 << 31) - 1 - 1024
     cases = [(0, 0, 64, 64, 64, 1 << 23, 64), (0, 0, 64, 64, (1 << 22) + 64, (1 << 22) + 64, 64),
              (0, 0, 1, 1, (1 << 22) + 64, (1 << 22) + 64, 1), (0, 0, 300, 200, 8, 8, 1 << 25),
@@ -354,7 +353,8 @@ def test_plan_geometry(lib, M, N, K):
     for cus in (256, 80):
         for ws in (0, 1 << 40):
             p = sg.sgemm_f32_plan(M, N, K, max(K, 1), N, N, cus, workspace_bytes=ws)
-            assert p.kernel == sg.binding.SGEMM_KERNEL_MFMA
+            # matrix-core tiles, or the 8 x 8 vector-FMA tiles that split K
+            assert p.kernel == sg.binding.SGEMM_KERNEL_MFMA or (p.bm, p.bn) == (8, 8)
             Mm, Nn = _check_tiles(p, M, N)
             assert p.threads == 64 * p.waves_m * p.waves_n
             assert p.group_m > 0 and p.xcd_remap == 1
@@ -408,9 +408,9 @@ def test_selector_strips(lib):
     """A few rows or columns past the last full tile go to the strip kernel
     when a tile row of them would cost a round; products with at most 4 rows
     or columns run on the strip kernel alone, or (without a workspace) on the
-    16 x 16 tiles that split K over their waves, which give such a product
-    more workgroups than its strips (measured 0.6-1.1x the strip plans' time
-    on MI355X)."""
+    16 x 16 or 8 x 8 tiles that split K inside the workgroup, which give such
+    a product more workgroups than its strips (16 x 16: measured 0.6-1.1x the
+    strip plans' time on MI355X)."""
     p = sg.sgemm_f32_plan(8196, 8192, 8192, 8192, 8192, 8192, 256)
     assert (p.strip_m, p.strip_n, p.bm, p.grid) == (4, 0, 256, 1024)
     p = sg.sgemm_f32_plan(2049, 2050, 2048, 2048, 2052, 2050, 256)
@@ -421,7 +421,7 @@ def test_selector_strips(lib):
                 p = sg.sgemm_f32_plan(M, N, 4096, M if ta else 4096, 4096 if tb else N, N, 256,
                                       ta, tb)
                 strips = p.grid == 0 and (p.strip_m == M or p.strip_n == N)
-                assert strips or (p.bm == 16 and p.splits == 1), (M, N, p.as_dict())
+                assert strips or (p.bm in (8, 16) and p.splits == 1), (M, N, p.as_dict())
 
 
 def test_cfg_geometry_of_forced_strips(lib):

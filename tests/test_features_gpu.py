@@ -56,13 +56,14 @@ def test_transposed_layouts_every_variant(ta, tb):
 
 def _ksplit_variants():
     return [v for v in range(sg.sgemm_f32_num_variants())
-            if (sg.sgemm_f32_variant(v).bm, sg.sgemm_f32_variant(v).bk) in ((32, 8), (16, 16))]
+            if (sg.sgemm_f32_variant(v).bm, sg.sgemm_f32_variant(v).bk) in ((32, 8), (16, 16), (8, 32))]
 
 
 @pytest.mark.parametrize("ta,tb", LAYOUTS)
 def test_ksplit_tiles_k_ranges(ta, tb):
     """The tiles that split K over their W waves (32 x 32 tiles in 8-deep
-    groups, 16 x 16 ones in 16-deep groups): each wave takes a range of whole
+    groups, 16 x 16 ones in 16-deep groups, the 8 x 8 vector-FMA ones in
+    32-deep groups, one k per lane pair): each wave takes a range of whole
     G-deep groups and keeps four groups of loads in flight (prefetch clamped
     to its last whole group); the last wave may end in a ragged group.  K
     values cover a single k, one ragged group, exactly one group per wave, one
@@ -89,7 +90,7 @@ def test_random_problems_through_the_selector():
     multiples of 4; random layout, alpha/beta, workspace or none, padded
     strides and 4-byte shifted starts.  The plans this reaches include the
     K-split 32 x 32 tiles (with and without an outer split), the K-split
-    16 x 16 tiles, the 64 x 64 tiles with 32- and 64-deep slices and edge
+    16 x 16 and 8 x 8 tiles, the 64 x 64 tiles with 32- and 64-deep slices and edge
     strips."""
     rng = np.random.default_rng(20261202)
     for case in range(100):
@@ -152,7 +153,7 @@ def test_alpha_beta(alpha, beta):
     A, B = inputs.make_operands(M, N, K, seed=100)
     C0 = inputs.make_operands(M, N, 1, seed=101)[0][:, :1] * np.linspace(-1, 1, N, dtype=np.float32)
     C0 = np.ascontiguousarray(C0.astype(np.float32))
-    for vid in (None, 1, 2, 3, 4, 5, 6, 14, 15, 16, 17, 18, 22, 23):
+    for vid in (None, 1, 2, 3, 4, 5, 6, 14, 15, 16, 17, 18, 22, 23, 24):
         note(f"alpha={alpha} beta={beta} variant {vid}")
         cfg = None if vid is None else forced(vid)
         C = run_general(A, B, 0, 0, alpha, beta, C0, cfg=cfg)
@@ -175,7 +176,7 @@ def test_beta_zero_ignores_nan_and_k_zero_scales():
     assert np.array_equal(C, (np.float32(-0.5) * C0).astype(np.float32))
 
 
-SPLIT_VARIANTS = [1, 2, 3, 4, 5, 6, 14, 15, 16, 17, 18, 22, 23]
+SPLIT_VARIANTS = [1, 2, 3, 4, 5, 6, 14, 15, 16, 17, 18, 22, 23, 24]
 
 
 @pytest.mark.parametrize("K", [1000, 1001, 130])

@@ -281,8 +281,8 @@ def test_direct_load_kernels_on_every_fetch_path(M, N, K, shift):
 
     for vid in range(sg.sgemm_f32_num_variants()):
         v = sg.sgemm_f32_variant(vid)
-        if v.kernel != sg.SGEMM_KERNEL_MFMA:
-            continue
+        if v.kernel != sg.SGEMM_KERNEL_MFMA and (v.bm, v.bn) != (8, 8):
+            continue  # the vector-FMA comparison kernel
         note(f"fetch paths variant {vid} M={M} N={N} K={K} shift={shift}")
         Ad, Bd = place(A), place(B)
         out = torch.full((M, N), float("nan"), device="cuda")
