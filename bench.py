@@ -47,12 +47,14 @@ One JSON line is printed.  Besides the driver's fields it holds:
                 power mode, and the host's cores.
   vendor        context only: torch.matmul in float32 (the ROCm BLAS libraries,
                 TF32 disabled) timed the same way on the square shapes from
-                512^3 to 8192^3, and torch.bmm on the two batched attention
-                products.
+                512^3 to 8192^3 and on 128 x 128 x 32768 in every layout, and
+                torch.bmm on the two batched attention products.
   extras        the library's other paths, each timed the same way after a
                 time-based warm-up (--extra-warm-ms): the small 512^3
                 configuration and the one-tile 128 x 128 x 32768 product with
-                and without a workspace (K split across workgroups), the
+                and without a workspace (K split across workgroups), the same
+                product in every layout on each form of tile that splits K
+                inside the workgroup (forced: 32 x 32, 16 x 16, 8 x 8), the
                 transposed-operand layouts at 8192^3 and 3072^3, strided
                 batches of attention-like products, the 1024 x 8192 x 8192
                 row band one GPU would run if 8192^3 were split over 8 GPUs,
@@ -347,6 +349,33 @@ def extras(torch, sg, steps, warm_ms, cus, peak):
                speedup=round(ms_no / ms_ws, 3))
         del A, B, C, ws
 
+    # the tiles that split K inside the workgroup (32 x 32 and 16 x 16 MFMA
+    # tiles over 8 waves, 8 x 8 vector-FMA tiles over lane pairs and 4 waves),
+    # each forced, on the one-tile long-K product in every layout
+    forms = {(32, 32, 8, 8), (16, 16, 16, 8), (8, 8, 32, 4)}
+    ksplit = [i for i in range(sg.sgemm_f32_num_variants())
+              if (sg.sgemm_f32_variant(i).bm, sg.sgemm_f32_variant(i).bn, sg.sgemm_f32_variant(i).bk,
+                  sg.sgemm_f32_variant(i).waves_m) in forms]
+    M = N = 128
+    K = 32768
+    for ta, tb in ((0, 0), (1, 0), (0, 1), (1, 1)):
+        A = operand((K, M) if ta else (M, K))
+        B = operand((N, K) if tb else (K, N))
+        C = torch.empty((M, N), device="cuda")
+        lda, ldb = A.shape[1], B.shape[1]
+        lay = ("T" if ta else "N") + ("T" if tb else "N")
+        h = stream.cuda_stream
+        for vid in ksplit:
+            cfg = sg.SgemmCfg()
+            cfg.id, cfg.group_m, cfg.xcd_remap, cfg.splits = vid, 8, 1, 1
+            plan = sg.sgemm_f32_cfg_geometry(cfg, ta, tb, M, N, K, lda, ldb, N)
+            ms = time_call(torch, lambda: chk(sg.sgemm_f32_ex(ta, tb, M, N, K, 1.0, A.data_ptr(), lda, 0,
+                                                          B.data_ptr(), ldb, 0, 0.0, C.data_ptr(), N, 0,
+                                                          1, 0, 0, h, cfg)), steps, warm_ms)
+            record(f"128x128x32768 {lay} forced K-split tile v{vid}", 2.0 * M * N * K, ms, plan)
+        del A, B, C
+    torch.cuda.empty_cache()
+
     # transposed operands (loaded as stored)
     for n in (8192, 3072):
         for ta, tb in ((1, 0), (0, 1), (1, 1)):
@@ -466,6 +495,19 @@ def vendor(torch, steps, warm_ms, peak):
         rec(shape, 2.0 * batch * M * N * K,
             time_call(torch, lambda: torch.bmm(A, Bv, out=C), steps, warm_ms))
         del A, B, Bv, C
+    # one 128 x 128 output with K = 32768 in every layout (a transposed
+    # operand passed as a transposed view of its stored form)
+    M = N = 128
+    K = 32768
+    for ta, tb in ((0, 0), (1, 0), (0, 1), (1, 1)):
+        A = torch.rand((K, M) if ta else (M, K), device="cuda") * 2 - 1
+        B = torch.rand((N, K) if tb else (K, N), device="cuda") * 2 - 1
+        Av, Bv = (A.t() if ta else A), (B.t() if tb else B)
+        C = torch.empty((M, N), device="cuda")
+        lay = ("T" if ta else "N") + ("T" if tb else "N")
+        rec(f"128x128x32768 {lay}", 2.0 * M * N * K,
+            time_call(torch, lambda: torch.matmul(Av, Bv, out=C), steps, warm_ms))
+        del A, B, Av, Bv, C
     torch.cuda.empty_cache()
     return out
 

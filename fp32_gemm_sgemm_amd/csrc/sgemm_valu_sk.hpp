@@ -23,7 +23,11 @@
 //  * the 32 accumulators of a lane are summed over the 32 lane pairs by a
 //    transposing butterfly (each step halves the values a lane keeps), then
 //    over the W waves through LDS in wave order, so a result is the same on
-//    every run, and written with alpha/beta like the other kernels' epilogue.
+//    every run, and written with alpha/beta like the other kernels' epilogue;
+//  * where both operands are k-contiguous (A as stored, B transposed) a lane
+//    instead takes 4 successive k and loads them from all 8 rows of each
+//    operand with 16-byte loads, so a wave reads 1 KiB (8 whole lines) of a
+//    row per load: half a line per k for the tile (vsk_kk).
 //
 // No operand goes through LDS and the K loop has no barrier and no branch
 // (one copy of it per load form, chosen once per workgroup): the loads of the
@@ -45,28 +49,17 @@ template <int W> struct VskTraits {
     static constexpr int DEPTH = 4;  // groups of loads in flight per wave
 };
 
+// One of the sums of the tile's 64 outputs over this wave's K range, for
+// the lane-pair form: lane l returns output (4 (l % 2) + (l / 2) / 8,
+// (l / 2) % 8).  g is located (batch entry and K split applied).
 template <int W, bool TA, bool TB>
-__global__ void __launch_bounds__(W * 64) sgemm_valu_sk_kernel(GemmArgs g)
+__device__ __forceinline__ float vsk_pairs(const GemmArgs &g, int m0, int n0, int wave, int lane)
 {
     typedef VskTraits<W> T;
     constexpr int GK = T::GK, D = T::DEPTH;
-    __shared__ float red[T::LDS_FLOATS];
-
-    if constexpr (kLdsPoison) {
-        // LDS race check build: the partial-tile area starts as NaN everywhere
-        lds_poison(&red[threadIdx.x], 1);
-        lds_poison_done();
-        __syncthreads();
-    }
-
-    const Work wk = map_work(g);
-    locate<TA, TB>(g, wk);
     const float *__restrict__ A = g.A;
     const float *__restrict__ B = g.B;
     const int M = g.M, N = g.N, K = g.K, lda = g.lda, ldb = g.ldb;
-    const int m0 = wk.tm * T::BM, n0 = wk.tn * T::BN;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int pair = lane >> 1, h = lane & 1;
 
     // this wave's K range [kb, ke): nfull whole groups, then rem < GK more k
@@ -209,15 +202,152 @@ __global__ void __launch_bounds__(W * 64) sgemm_valu_sk_kernel(GemmArgs g)
             v[x] = hi ? up : lo;
         }
     }
-    red[wave * 64 + lane] = v[0];
+    return v[0];
+}
+
+// The same for the form where both operands are k-contiguous (A as stored,
+// B transposed): lane l takes k = 4l..4l+3 of each 256-deep step of its
+// wave's range, loads those four k of all eight rows of op(A) and of op(B)^T
+// with one 16-byte load per row (a wave reads 1 KiB of each row: 8 whole
+// lines), and adds all 64 products of the tile into 64 accumulators.  Lane
+// l returns output (l / 8, l % 8).
+template <int W>
+__device__ __forceinline__ float vsk_kk(const GemmArgs &g, int m0, int n0, int wave, int lane)
+{
+    constexpr int GS = 256, D = 2;  // k of one step; steps of loads in flight
+    const int M = g.M, N = g.N, K = g.K;
+    const int kc = (((K + W - 1) / W) + GS - 1) & ~(GS - 1);
+    const int kb = wave * kc;
+    const int ke = min(K, kb + kc);
+    const int len = ke > kb ? ke - kb : 0;
+    const int nfull = len / GS;
+    const int rem = len % GS;
+
+    // row i of op(A) and of op(B)^T (clamped): the same for every lane
+    const float *pa[8];
+    const float *pb[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        pa[i] = g.A + (int64_t)min(m0 + i, M - 1) * g.lda;
+        pb[i] = g.B + (int64_t)min(n0 + i, N - 1) * g.ldb;
+    }
+    struct Frag {
+        f32x4 a[8], b[8];
+    };
+    auto load = [&](int st, Frag &f) {
+        const int k = kb + GS * st + 4 * lane;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            f.a[i] = *reinterpret_cast<const f32x4u *>(pa[i] + k);
+            f.b[i] = *reinterpret_cast<const f32x4u *>(pb[i] + k);
+        }
+    };
+    float acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
+    auto fma = [&](const Frag &f) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_fmaf(f.a[i][t], f.b[j][t], acc[i][j]);
+    };
+    if (nfull > 0) {
+        // prefetch indices past the last whole step reload it (in bounds,
+        // never multiplied in)
+        const int last = nfull - 1;
+        Frag f[D];
+#pragma unroll
+        for (int d = 0; d < D; ++d) load(min(d, last), f[d]);
+        int s0 = 0;
+        for (; s0 + D <= nfull; s0 += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                fma(f[d]);
+                load(min(s0 + D + d, last), f[d]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int d = 0; d < D - 1; ++d)
+            if (s0 + d < nfull) fma(f[d]);
+    }
+    if (rem > 0) {
+        // the ragged step: k past ke reads a clamped address and becomes 0
+        const int k = kb + GS * nfull + 4 * lane;
+        Frag f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int kk = min(k + t, ke - 1);
+            const bool in = k + t < ke;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float x = pa[i][kk], y = pb[i][kk];
+                f.a[i][t] = in ? x : 0.0f;
+                f.b[i][t] = in ? y : 0.0f;
+            }
+        }
+        fma(f);
+    }
+
+    // sum over the wave's 64 lanes: the step with offset s (32, 16, ..., 1)
+    // pairs lanes that differ in lane bit s; both add their copies of values
+    // x and x + s and each keeps the one whose bit s matches that lane bit,
+    // so lane l ends with value l = 8i + j
+    float v[64];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[8 * i + j] = acc[i][j];
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) {
+        const bool hi = (lane & s) != 0;
+#pragma unroll
+        for (int x = 0; x < s; ++x) {
+            const float lo = v[x] + __shfl_xor(v[x], s);
+            const float up = v[x + s] + __shfl_xor(v[x + s], s);
+            v[x] = hi ? up : lo;
+        }
+    }
+    return v[0];
+}
+
+template <int W, bool TA, bool TB>
+__global__ void __launch_bounds__(W * 64) sgemm_valu_sk_kernel(GemmArgs g)
+{
+    typedef VskTraits<W> T;
+    constexpr bool KK = !TA && TB;  // both operands k-contiguous
+    __shared__ float red[T::LDS_FLOATS];
+
+    if constexpr (kLdsPoison) {
+        // LDS race check build: the partial-tile area starts as NaN everywhere
+        lds_poison(&red[threadIdx.x], 1);
+        lds_poison_done();
+        __syncthreads();
+    }
+
+    const Work wk = map_work(g);
+    locate<TA, TB>(g, wk);
+    const int m0 = wk.tm * T::BM, n0 = wk.tn * T::BN;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    float part;
+    if constexpr (KK) part = vsk_kk<W>(g, m0, n0, wave, lane);
+    else part = vsk_pairs<W, TA, TB>(g, m0, n0, wave, lane);
+
+    // the waves' partial tiles, added in wave order
+    red[wave * 64 + lane] = part;
     __syncthreads();
     if (tid < 64) {
         float s = red[tid];
 #pragma unroll
         for (int w = 1; w < W; ++w) s += red[w * 64 + tid];
-        const int x = tid >> 1, hh = tid & 1;
-        const int row = m0 + 4 * hh + (x >> 3), col = n0 + (x & 7);
-        if (row < M && col < N) {
+        const int row = m0 + (KK ? tid >> 3 : 4 * (tid & 1) + (tid >> 4));
+        const int col = n0 + (KK ? tid & 7 : (tid >> 1) & 7);
+        if (row < g.M && col < g.N) {
             float *p = g.C + (int64_t)row * g.ldc + col;
             *p = g.beta != 0.0f ? g.alpha * s + g.beta * *p : g.alpha * s;
         }

@@ -84,6 +84,25 @@ def test_ksplit_tiles_k_ranges(ta, tb):
             check_general(run_general(As, Bs, ta, tb, cfg=forced(vid)), As, Bs, ta, tb)
 
 
+def test_vector_fma_ksplit_tile_both_k_contiguous():
+    """The 8 x 8 vector-FMA K-split tile in the NT layout (both operands
+    k-contiguous), whose lanes each take 4 successive k of 256-deep steps:
+    K below one step, exactly one and one more, steps that leave waves
+    without a range, an odd number of whole steps per wave (the loop and its
+    tail) with and without a ragged step, and outputs of fewer than 8 rows
+    or columns."""
+    vid = next(v for v in range(sg.sgemm_f32_num_variants())
+               if (sg.sgemm_f32_variant(v).bm, sg.sgemm_f32_variant(v).bk) == (8, 32))
+    W = sg.sgemm_f32_variant(vid).waves_m
+    for M, N in [(70, 45), (5, 3), (8, 8)]:
+        for K in (1, 255, 256, 257, 256 * (W - 1) + 3, 3 * 256 * W, 3 * 256 * W + 77,
+                  5 * 256 * W + 1):
+            note(f"vector-FMA k-split NT variant {vid} {M}x{N}x{K}")
+            A, B = inputs.make_operands(M, N, K, seed=720 + K + M)
+            Bs = stored(B, 1)
+            check_general(run_general(A, Bs, 0, 1, cfg=forced(vid)), A, Bs, 0, 1)
+
+
 def test_random_problems_through_the_selector():
     """100 seeded random problems through the default plan: small, medium,
     skinny with long K and wide with short K, half with sizes that are
