@@ -58,7 +58,9 @@ One JSON line is printed.  Besides the driver's fields it holds:
                 transposed-operand layouts at 8192^3 and 3072^3, strided
                 batches of attention-like products, the 1024 x 8192 x 8192
                 row band one GPU would run if 8192^3 were split over 8 GPUs,
-                1024^3 (one 64 x 64 tile per CU), shapes whose few edge rows or columns (or all of them, for
+                1024^3 (one 64 x 64 tile per CU), three shapes the selector
+                gives 32 x 64 tiles (beside the tile it would use without
+                them, forced), shapes whose few edge rows or columns (or all of them, for
                 products of 1 row or column) go to the strip kernel, and the
                 vector-FMA comparison kernel forced at 8192^3 and 3072^3
                 (with its fraction of valu_probe).
@@ -442,6 +444,28 @@ def extras(torch, sg, steps, warm_ms, cus, peak):
         ms = time_call(torch, lambda: chk(sg.sgemm_f32(M, N, K, A.data_ptr(), K, B.data_ptr(), N,
                                                     C.data_ptr(), N, h)), steps, warm_ms)
         record(name, 2.0 * M * N * K, ms, plan)
+        del A, B, C
+    torch.cuda.empty_cache()
+
+    # outputs between one and three rounds of 64x64 tiles (or fewer 32x32
+    # tiles than CUs), which the selector gives 32x64 tiles, three per CU:
+    # the default plan, and forced beside it the tile it would use without them
+    for M, N, K, before in [(1536, 1024, 4096, 20), (1024, 384, 1024, 16), (3072, 384, 4096, 16)]:
+        A, B = operand((M, K)), operand((K, N))
+        C = torch.empty((M, N), device="cuda")
+        h = stream.cuda_stream
+        plan = sg.sgemm_f32_plan(M, N, K, K, N, N, cus)
+        ms = time_call(torch, lambda: chk(sg.sgemm_f32(M, N, K, A.data_ptr(), K, B.data_ptr(), N,
+                                                    C.data_ptr(), N, h)), steps, warm_ms)
+        cfg = sg.SgemmCfg()
+        cfg.id, cfg.group_m, cfg.xcd_remap, cfg.splits = before, 8, 1, 1
+        plan_b = sg.sgemm_f32_cfg_geometry(cfg, 0, 0, M, N, K, K, N, N)
+        ms_b = time_call(torch, lambda: chk(sg.sgemm_f32_ex(0, 0, M, N, K, 1.0, A.data_ptr(), K, 0,
+                                                         B.data_ptr(), N, 0, 0.0, C.data_ptr(), N, 0,
+                                                         1, 0, 0, h, cfg)), steps, warm_ms)
+        record(f"{M}x{N}x{K}", 2.0 * M * N * K, ms, plan)
+        record(f"{M}x{N}x{K} forced v{before}", 2.0 * M * N * K, ms_b, plan_b,
+               default_speedup=round(ms_b / ms, 3))
         del A, B, C
     torch.cuda.empty_cache()
 
