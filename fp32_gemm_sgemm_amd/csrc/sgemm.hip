@@ -175,7 +175,7 @@ const Variant kVariants[] = {
     sk_variant<16, 16>(293, 365, 256, 3048, 1195, 866, 2),    // 22: 16x16, K split over 16 waves
     sk_variant<8, 16>(309, 455, 251, 3056, 1410, 909, 4),     // 23: 16x16, K split over 8 waves
     vsk_variant<4>(108, 121, 76, 3032, 1022, 859, 4),         // 24: 8x8 vector FMA, K split over lane pairs and 4 waves
-    dl_variant<32, 64, 32, 2, 2, 4, kAllOps, false, kCrossSliceAgpr, 16>(734, 752, 157, 3273),  // 25: direct loads, 4 stages, 4 waves of 16x32 on 16x16 blocks
+    dl_variant<32, 64, 32, 2, 2, 4, kAllOps, false, kCrossSliceAgpr, 16>(880, 752, 157, 3273),  // 25: direct loads, 4 stages, 4 waves of 16x32 on 16x16 blocks
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
