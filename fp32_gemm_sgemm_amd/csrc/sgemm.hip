@@ -146,6 +146,11 @@ constexpr int kCrossSliceAgpr = 6;
 // when the same operands are still in L2 from the call before, so the
 // four-stage ones (20, 21), which keep their rate either way, are the one-round
 // choice.
+// The 32x64 tile (25) puts three workgroups on a CU, so its four-round shape
+// (1,024 tiles) runs as unequal waves of 768 and 256 and reads 734; inverted on
+// 1536 x 1024 x 4096 (768 tiles, three per CU) the model gives 903.  Its table
+// figure, 880, lies between: every plan it changes on a 432-shape grid was
+// timed faster than the plan it replaced.
 // The 4-byte direct-load variants serve only rows that are not 16-byte
 // aligned.  The vector-FMA comparison kernel carries no figures: the selector
 // never picks it.
